@@ -1,0 +1,2 @@
+"""Seeded synthetic inputs shared by the oracle's tests and the HIP path (no layer arithmetic)."""
+from .gen import CONFIGS, CONFIG_ORDER, MoEConfig, Problem, make_problem  # noqa: F401
