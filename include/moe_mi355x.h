@@ -1,0 +1,194 @@
+/*
+ * moe_mi355x.h -- C ABI of the routed Mixture-of-Experts FFN layer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer (Qwen3.8-Flash-Next study, section "MoE: 512 experts behind a
+ * width-640 intermediate", eq. expert(x) and eq. MoE(x)):
+ *
+ *   expert_e(x) = W_down[e] ( SiLU(W_gate[e] x) * (W_up[e] x) )
+ *   out_t       = sum_{j<k} w[t,j] expert_{ids[t,j]}(x_t)
+ *                 + sigmoid(w_sg . x_t) * shared(x_t)
+ *
+ * computed in the stage order of that section's pipeline figure:
+ *   Router [T,E] -> top-k + normalise -> dispatch R = k*T assignments ->
+ *   grouped expert GEMMs -> weighted combine + gated shared expert.
+ * One entry point per stage, plus the whole layer in one call.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Pointers are device pointers (hipMalloc'd or equivalent) owned by the
+ *    caller; the library never allocates, frees or synchronises.  Tensors are
+ *    row-major and contiguous, except routed expert matrices, which may sit
+ *    at any element stride from one expert to the next (moe_weights).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *    enqueued on it asynchronously; no host<->device copy happens inside a call.
+ *  - `ws`/`ws_bytes` is caller-owned scratch device memory of at least
+ *    moe_workspace_bytes(p) bytes, 256-byte aligned.  Its contents on entry
+ *    do not matter; it must not be used by anything else until the stream has
+ *    run the call.  Concurrent calls need distinct workspaces.
+ *  - Validation happens on the host before any launch: a non-OK status means
+ *    nothing was enqueued.  MOE_ERR_HIP reports a failed launch
+ *    (hipGetLastError); faults during execution surface at the caller's next
+ *    synchronisation.  NaN/Inf inputs give unspecified outputs.
+ *  - T == 0 is a valid no-op returning MOE_OK; nothing is written.
+ *  - Routing ties: experts are ordered by descending fp32 logit, equal logits
+ *    by ascending expert id.  Results are deterministic run to run.
+ *  - Expert ids, the dispatch permutation and all integer outputs are exact;
+ *    floating outputs carry fp32 accumulation and bf16 rounding of the
+ *    intermediates h (the SwiGLU hidden) and y (per-assignment outputs).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  MOE_ERR_SHAPE = 2,       /* a size is out of range (T<0, k<1, k>E, E>1024, ...) */
+  MOE_ERR_DTYPE = 3,       /* unsupported activation / weight dtype pair        */
+  MOE_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned, or ws not 256   */
+  MOE_ERR_WORKSPACE = 5,   /* ws_bytes < moe_workspace_bytes(p)                 */
+  MOE_ERR_UNSUPPORTED = 6, /* valid shape the kernels do not cover (see below)  */
+  MOE_ERR_HIP = 7          /* a kernel launch failed                            */
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,             /* IEEE binary32                                     */
+  MOE_BF16 = 1,            /* bfloat16                                          */
+  MOE_FP8_E4M3FN = 2       /* OCP E4M3FN codes (uint8) with fp32 block scales   */
+} moe_dtype;
+
+/* Problem description.  Supported combinations:
+ *   act_dtype F32  with w_dtype F32   (all tensors fp32)
+ *   act_dtype BF16 with w_dtype BF16
+ *   act_dtype BF16 with w_dtype FP8_E4M3FN (routed experts only; router,
+ *       shared expert and shared gate stay bf16 -- "Qwen3.8, weights in hand",
+ *       section "What FP8 actually quantizes"); scale_block must be 128 and
+ *       H, I multiples of 128.
+ * Limits: 1 <= E <= 1024, 1 <= k <= min(E, 64), H and I multiples of 8 (bf16)
+ * or of 4 (f32), I_shared 0 or a multiple of 8; T*k < 2^31.                  */
+typedef struct {
+  int64_t T;          /* tokens                                               */
+  int64_t H;          /* hidden width                                          */
+  int64_t E;          /* routed experts                                        */
+  int64_t k;          /* experts chosen per token                              */
+  int64_t I;          /* routed expert intermediate width                      */
+  int64_t I_shared;   /* shared expert intermediate width; 0 = no shared expert */
+  int32_t act_dtype;  /* moe_dtype of x, router, shared expert, y, out         */
+  int32_t w_dtype;    /* moe_dtype of routed expert matrices                   */
+  int32_t scale_block;/* fp8 scale block edge (128), else ignored              */
+  uint32_t flags;     /* MOE_FLAG_* (0 = default)                              */
+} moe_problem;
+
+/* Force every routed expert onto the tiled MFMA GEMM path / the weight
+ * streaming path (default: per expert, by its token count).  For A/B tests. */
+#define MOE_FLAG_FORCE_GEMM   (1u << 0)
+#define MOE_FLAG_FORCE_STREAM (1u << 1)
+
+/* Weights.  Layouts follow PyTorch Linear (out x in), which matches the GGUF
+ * shapes on the Qwen3.8-2.4T-A95B hub discussion's zero-fraction table
+ * (ffn_gate_exps 8192x2048x512 innermost-first = [E][I][H] row-major):
+ *   w_router  [E, H]     act dtype
+ *   w_gate    [E][I, H]  w_dtype, expert e at w_gate + e*stride_gate elements
+ *   w_up      [E][I, H]  w_dtype, expert e at w_up   + e*stride_up
+ *   w_down    [E][H, I]  w_dtype, expert e at w_down + e*stride_down
+ *             stride 0 means dense (I*H).  A fused [E, 2I, H] gate_up tensor
+ *             is passed as w_gate = base, w_up = base + I*H, strides 2*I*H.
+ *   s_gate/s_up [E, I/128, H/128] fp32, s_down [E, H/128, I/128] fp32:
+ *             fp8 block scales (value = code * scale); NULL unless fp8.
+ *   sh_gate, sh_up [I_shared, H], sh_down [H, I_shared], sh_gate_w [1, H]:
+ *             shared expert and its gate projection, act dtype; NULL iff
+ *             I_shared == 0.                                                 */
+typedef struct {
+  const void* w_router;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  int64_t stride_gate;
+  int64_t stride_up;
+  int64_t stride_down;
+  const float* s_gate;
+  const float* s_up;
+  const float* s_down;
+  const void* sh_gate;
+  const void* sh_up;
+  const void* sh_down;
+  const void* sh_gate_w;
+} moe_weights;
+
+/* ABI version (MOE_ABI_VERSION) and a static string for a status code. */
+int moe_abi_version(void);
+const char* moe_status_str(moe_status s);
+
+/* Host-only check of a problem description (no device access).  Returns the
+ * status every entry point would return for these sizes and dtypes. */
+moe_status moe_validate(const moe_problem* p);
+
+/* Bytes of workspace every entry point below needs for problem p (the
+ * maximum over entry points; 0 if p is invalid).  Host only. */
+size_t moe_workspace_bytes(const moe_problem* p);
+
+/* Router, softmax, top-k and renormalisation ("Router [T, 512]" and
+ * "Top 10 + normalize" in the pipeline figure; "Selected router
+ * probabilities are normalized").
+ *   x [T,H] act, w_router [E,H] act, sh_gate_w [1,H] act or NULL.
+ * Outputs: topk_ids [T,k] int32, descending logit (ties -> lower id);
+ *          topk_w   [T,k] fp32, exp(l_j - l_max) / sum over the k chosen;
+ *          shared_logit [T] fp32 = w_sg . x_t (written iff sh_gate_w and
+ *          shared_logit are both non-NULL).
+ * Logits are fp32: bf16 x bf16 products accumulated in fp32 (no rounding of
+ * the logits to bf16).                                                      */
+moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
+                     const void* sh_gate_w, int32_t* topk_ids, float* topk_w,
+                     float* shared_logit, void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch ("Dispatch R tokens"): dropless, stable counting sort of the R = T*k
+ * flat assignments a = t*k + j by expert id.
+ *   topk_ids [T,k] int32 in [0,E).
+ * Outputs: expert_offsets [E+1] int32 (exclusive prefix sum of per-expert
+ *          counts, offsets[E] = R); sorted_assign [R] int32 (assignments in
+ *          (expert, a) order); assign_pos [R] int32 (its inverse).           */
+moe_status moe_dispatch(const moe_problem* p, const int32_t* topk_ids,
+                        int32_t* expert_offsets, int32_t* sorted_assign,
+                        int32_t* assign_pos, void* ws, size_t ws_bytes, void* stream);
+
+/* Grouped expert FFN ("Grouped expert GEMMs"): for every dispatched row
+ * r in [offsets[e], offsets[e+1]) with token t = sorted_assign[r] / k,
+ *   y[r] = expert_e(x_t)              (y [R,H] act, permuted order)
+ * and, if the problem has a shared expert and y_shared != NULL,
+ *   y_shared[t] = shared(x_t)         (y_shared [T,H] act).
+ * Experts with few rows stream their weights once through a small-M MFMA
+ * kernel; the rest run on an LDS-tiled MFMA grouped GEMM.                   */
+moe_status moe_expert_ffn(const moe_problem* p, const moe_weights* w, const void* x,
+                          const int32_t* expert_offsets, const int32_t* sorted_assign,
+                          void* y, void* y_shared, void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine + gated shared expert ("Weighted combine + gated shared
+ * expert"; eq. MoE(x)):
+ *   out[t] = sum_{j<k} topk_w[t,j] * y[assign_pos[t*k+j]]
+ *            + sigmoid(shared_logit[t]) * y_shared[t]
+ * in fp32, j ascending, then rounded to act dtype.  y_shared and
+ * shared_logit are both NULL (no shared term) or both non-NULL.            */
+moe_status moe_combine(const moe_problem* p, const void* y, const int32_t* assign_pos,
+                       const float* topk_w, const void* y_shared,
+                       const float* shared_logit, void* out, void* stream);
+
+/* The whole layer: route -> dispatch -> expert FFN -> combine, with all
+ * intermediates in ws.  out [T,H] act.  topk_ids / topk_w may be NULL; if
+ * given they receive the routing ([T,k] int32 / fp32).                      */
+moe_status moe_layer_forward(const moe_problem* p, const moe_weights* w, const void* x,
+                             void* out, int32_t* topk_ids, float* topk_w,
+                             void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,99 @@
+"""Routed Mixture-of-Experts FFN layer for AMD Instinct MI355X (gfx950).
+
+Python face of the C ABI in include/moe_mi355x.h: the functions below have
+the C entry points' names and arguments, take torch tensors (device memory)
+and pass their pointers plus the current HIP stream to the library.  No
+computation happens here.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from ._lib import (LIB, MOE_BF16, MOE_F32, MOE_FLAG_FORCE_GEMM, MOE_FLAG_FORCE_STREAM,  # noqa: F401
+                   MOE_FP8_E4M3FN, MOE_OK, EXPORTS, moe_problem, moe_weights)
+
+_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3FN}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {LIB.moe_status_str(status).decode()} (status {status})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MoE library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _check(st: int, where: str):
+    if st != MOE_OK:
+        raise MoEError(st, where)
+
+
+def problem(T, H, E, k, I, I_shared=0, act="bf16", wdt="bf16", scale_block=128, flags=0) -> moe_problem:
+    return moe_problem(T, H, E, k, I, I_shared, _DT[act], _DT[wdt], scale_block, flags)
+
+
+def weights(w_router, w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None, sh_gate=None, sh_up=None,
+            sh_down=None, sh_gate_w=None, stride_gate=0, stride_up=0, stride_down=0) -> moe_weights:
+    return moe_weights(_ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), stride_gate, stride_up,
+                       stride_down, _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(sh_gate), _ptr(sh_up),
+                       _ptr(sh_down), _ptr(sh_gate_w))
+
+
+def moe_abi_version() -> int:
+    return LIB.moe_abi_version()
+
+
+def moe_validate(p: moe_problem) -> int:
+    return LIB.moe_validate(ctypes.byref(p))
+
+
+def moe_workspace_bytes(p: moe_problem) -> int:
+    return LIB.moe_workspace_bytes(ctypes.byref(p))
+
+
+def workspace(p: moe_problem, device="cuda") -> torch.Tensor:
+    """A device buffer of moe_workspace_bytes(p) bytes (torch allocations are 256-byte aligned)."""
+    n = moe_workspace_bytes(p)
+    if n == 0:
+        _check(moe_validate(p), "moe_workspace_bytes")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def moe_route(p, x, w_router, sh_gate_w, topk_ids, topk_w, shared_logit, ws, stream=None):
+    _check(LIB.moe_route(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(sh_gate_w), _ptr(topk_ids), _ptr(topk_w),
+                         _ptr(shared_logit), _ptr(ws), ws.numel(), _stream(stream)), "moe_route")
+
+
+def moe_dispatch(p, topk_ids, expert_offsets, sorted_assign, assign_pos, ws, stream=None):
+    _check(LIB.moe_dispatch(ctypes.byref(p), _ptr(topk_ids), _ptr(expert_offsets), _ptr(sorted_assign),
+                            _ptr(assign_pos), _ptr(ws), ws.numel(), _stream(stream)), "moe_dispatch")
+
+
+def moe_expert_ffn(p, w: moe_weights, x, expert_offsets, sorted_assign, y, y_shared, ws, stream=None):
+    _check(LIB.moe_expert_ffn(ctypes.byref(p), ctypes.byref(w), _ptr(x), _ptr(expert_offsets), _ptr(sorted_assign),
+                              _ptr(y), _ptr(y_shared), _ptr(ws), ws.numel(), _stream(stream)), "moe_expert_ffn")
+
+
+def moe_combine(p, y, assign_pos, topk_w, y_shared, shared_logit, out, stream=None):
+    _check(LIB.moe_combine(ctypes.byref(p), _ptr(y), _ptr(assign_pos), _ptr(topk_w), _ptr(y_shared),
+                           _ptr(shared_logit), _ptr(out), _stream(stream)), "moe_combine")
+
+
+def moe_layer_forward(p, w: moe_weights, x, out, topk_ids, topk_w, ws, stream=None):
+    _check(LIB.moe_layer_forward(ctypes.byref(p), ctypes.byref(w), _ptr(x), _ptr(out), _ptr(topk_ids),
+                                 _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream)), "moe_layer_forward")

@@ -1,0 +1,303 @@
+// C ABI of the routed MoE layer: host-side validation, workspace carving and
+// stream-ordered launches.  Declarations and the contract of every entry
+// point are in include/moe_mi355x.h.
+#include "moe_mi355x.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "kernels.hpp"
+
+namespace {
+
+using moe::FfnArgs;
+
+constexpr size_t kAlign = 256;
+inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t act_bytes(const moe_problem* p) { return p->act_dtype == MOE_F32 ? 4 : 2; }
+size_t w_bytes(const moe_problem* p) {
+  return p->w_dtype == MOE_F32 ? 4 : (p->w_dtype == MOE_BF16 ? 2 : 1);
+}
+
+// ---------------------------------------------------------------------------
+// workspace layout
+// ---------------------------------------------------------------------------
+struct StageSizes {
+  size_t route, dispatch, ffn, stage;  // scratch of each stage; stage = max
+};
+
+StageSizes stage_sizes(const moe_problem* p) {
+  StageSizes s{};
+  const size_t T = (size_t)p->T, E = (size_t)p->E, k = (size_t)p->k;
+  const size_t R = T * k;
+  s.route = up(T * (E + 1) * 4);
+  s.dispatch = up(moe::dispatch_ws_ints(p->T, p->E) * 4);
+  s.ffn = up(moe::ffn_plan_ints(p->T, p->E, p->k, p->I_shared > 0) * 4) + up(R * (size_t)p->I * act_bytes(p)) +
+          up(T * (size_t)p->I_shared * act_bytes(p));
+  s.stage = s.route;
+  if (s.dispatch > s.stage) s.stage = s.dispatch;
+  if (s.ffn > s.stage) s.stage = s.ffn;
+  return s;
+}
+
+struct LayerWs {
+  int32_t* ids;
+  float* w;
+  float* sl;
+  int32_t* offsets;
+  int32_t* sorted;
+  int32_t* pos;
+  void* y;
+  void* y_sh;
+  void* stage;
+  size_t total;
+};
+
+LayerWs layer_layout(const moe_problem* p, void* base) {
+  const size_t T = (size_t)p->T, E = (size_t)p->E, k = (size_t)p->k, H = (size_t)p->H;
+  const size_t R = T * k;
+  char* b = static_cast<char*>(base);
+  size_t o = 0;
+  LayerWs L{};
+  auto take = [&](size_t bytes) {
+    char* r = b ? b + o : nullptr;
+    o += up(bytes);
+    return r;
+  };
+  L.ids = reinterpret_cast<int32_t*>(take(R * 4));
+  L.w = reinterpret_cast<float*>(take(R * 4));
+  L.sl = reinterpret_cast<float*>(take(T * 4));
+  L.offsets = reinterpret_cast<int32_t*>(take((E + 1) * 4));
+  L.sorted = reinterpret_cast<int32_t*>(take(R * 4));
+  L.pos = reinterpret_cast<int32_t*>(take(R * 4));
+  L.y = take(R * H * act_bytes(p));
+  L.y_sh = take(p->I_shared > 0 ? T * H * act_bytes(p) : 0);
+  L.stage = take(stage_sizes(p).stage);
+  L.total = o;
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// validation
+// ---------------------------------------------------------------------------
+moe_status check_problem(const moe_problem* p) {
+  if (!p) return MOE_ERR_NULL;
+  if (p->T < 0 || p->H < 1 || p->E < 1 || p->E > 1024 || p->k < 1 || p->k > p->E || p->k > 64 || p->I < 1 ||
+      p->I_shared < 0)
+    return MOE_ERR_SHAPE;
+  if (p->T > (int64_t)INT32_MAX / p->k || p->H > (1 << 24) || p->I > (1 << 24) || p->I_shared > (1 << 24))
+    return MOE_ERR_SHAPE;
+  const bool f32 = p->act_dtype == MOE_F32 && p->w_dtype == MOE_F32;
+  const bool bf = p->act_dtype == MOE_BF16 && p->w_dtype == MOE_BF16;
+  const bool fp8 = p->act_dtype == MOE_BF16 && p->w_dtype == MOE_FP8_E4M3FN;
+  if (!f32 && !bf && !fp8) return MOE_ERR_DTYPE;
+  const int64_t q = f32 ? 4 : 8;  // 16-byte vectors along every K-contiguous row
+  if (p->H % q || p->I % q || p->I_shared % q) return MOE_ERR_UNSUPPORTED;
+  if (fp8 && (p->scale_block != 128 || p->H % 128 || p->I % 128)) return MOE_ERR_UNSUPPORTED;
+  if (p->flags & ~(uint32_t)(MOE_FLAG_FORCE_GEMM | MOE_FLAG_FORCE_STREAM)) return MOE_ERR_UNSUPPORTED;
+  if ((p->flags & MOE_FLAG_FORCE_GEMM) && (p->flags & MOE_FLAG_FORCE_STREAM)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_ws(const moe_problem* p, const void* ws, size_t ws_bytes) {
+  if (!ws) return MOE_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOE_ERR_ALIGN;
+  if (ws_bytes < moe_workspace_bytes(p)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+moe_status check_weights(const moe_problem* p, const moe_weights* w, bool need_router, bool need_experts) {
+  if (!w) return MOE_ERR_NULL;
+  if (need_router && !w->w_router) return MOE_ERR_NULL;
+  if (need_router && !al16(w->w_router)) return MOE_ERR_ALIGN;
+  if (need_experts) {
+    if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_NULL;
+    if (!al16(w->w_gate) || !al16(w->w_up) || !al16(w->w_down)) return MOE_ERR_ALIGN;
+    if (w->stride_gate < 0 || w->stride_up < 0 || w->stride_down < 0) return MOE_ERR_SHAPE;
+    const int64_t wb = (int64_t)w_bytes(p);
+    if ((w->stride_gate * wb) % 16 || (w->stride_up * wb) % 16 || (w->stride_down * wb) % 16) return MOE_ERR_ALIGN;
+    if (p->w_dtype == MOE_FP8_E4M3FN) {
+      if (!w->s_gate || !w->s_up || !w->s_down) return MOE_ERR_NULL;
+      if (!al16(w->s_gate) || !al16(w->s_up) || !al16(w->s_down)) return MOE_ERR_ALIGN;
+    }
+    if (p->I_shared > 0) {
+      if (!w->sh_gate || !w->sh_up || !w->sh_down) return MOE_ERR_NULL;
+      if (!al16(w->sh_gate) || !al16(w->sh_up) || !al16(w->sh_down)) return MOE_ERR_ALIGN;
+    }
+  }
+  if (need_router && p->I_shared > 0) {
+    if (!w->sh_gate_w) return MOE_ERR_NULL;
+    if (!al16(w->sh_gate_w)) return MOE_ERR_ALIGN;
+  }
+  return MOE_OK;
+}
+
+inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// ---------------------------------------------------------------------------
+// stage bodies (arguments already validated)
+// ---------------------------------------------------------------------------
+moe_status do_route(const moe_problem* p, const void* x, const void* w_router, const void* sh_gate_w,
+                    int32_t* ids, float* w, float* sl, void* stage, hipStream_t s) {
+  const int T = (int)p->T, H = (int)p->H, E = (int)p->E, k = (int)p->k;
+  const void* wsg = (sh_gate_w && sl) ? sh_gate_w : nullptr;
+  float* logits = static_cast<float*>(stage);
+  hipError_t e;
+  if (p->act_dtype == MOE_F32)
+    e = moe::launch_router_logits_f32(static_cast<const float*>(x), static_cast<const float*>(w_router),
+                                      static_cast<const float*>(wsg), logits, T, H, E, s);
+  else
+    e = moe::launch_router_logits_bf16(x, w_router, wsg, logits, T, H, E, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_topk(logits, E + (wsg ? 1 : 0), T, E, k, wsg ? 1 : 0, ids, w, sl, s));
+}
+
+moe_status do_ffn(const moe_problem* p, const moe_weights* w, const void* x, const int32_t* offsets,
+                  const int32_t* sorted, void* y, void* y_sh, void* stage, hipStream_t s) {
+  FfnArgs a{};
+  a.T = (int)p->T;
+  a.H = (int)p->H;
+  a.E = (int)p->E;
+  a.k = (int)p->k;
+  a.I = (int)p->I;
+  a.Is = (p->I_shared > 0 && y_sh) ? (int)p->I_shared : 0;
+  a.fp8 = p->w_dtype == MOE_FP8_E4M3FN;
+  a.x = x;
+  a.offsets = offsets;
+  a.sorted = sorted;
+  a.wg = w->w_gate;
+  a.wu = w->w_up;
+  a.wd = w->w_down;
+  a.sg = w->stride_gate ? w->stride_gate : p->I * p->H;
+  a.su = w->stride_up ? w->stride_up : p->I * p->H;
+  a.sd = w->stride_down ? w->stride_down : p->H * p->I;
+  a.scg = w->s_gate;
+  a.scu = w->s_up;
+  a.scd = w->s_down;
+  a.shg = w->sh_gate;
+  a.shu = w->sh_up;
+  a.shd = w->sh_down;
+  a.y = y;
+  a.y_sh = a.Is ? y_sh : nullptr;
+  // stage scratch: plan ints | h | h_sh
+  char* b = static_cast<char*>(stage);
+  const size_t plan_bytes = up(moe::ffn_plan_ints(p->T, p->E, p->k, a.Is > 0) * 4);
+  int32_t* plan = reinterpret_cast<int32_t*>(b);
+  a.h = b + plan_bytes;
+  a.h_sh = b + plan_bytes + up((size_t)p->T * p->k * p->I * act_bytes(p));
+  if (p->act_dtype == MOE_F32) return hip_status(moe::launch_ffn_f32(a, s));
+  hipError_t e = moe::launch_ffn_plan(offsets, a.T, a.E, a.k, a.Is > 0 ? 1 : 0, p->flags, plan, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  moe::ffn_bind_plan(a, plan);
+  if ((e = moe::launch_ffn_gemm(a, 1, s)) != hipSuccess) return MOE_ERR_HIP;
+  if ((e = moe::launch_ffn_stream(a, 1, s)) != hipSuccess) return MOE_ERR_HIP;
+  if ((e = moe::launch_ffn_gemm(a, 2, s)) != hipSuccess) return MOE_ERR_HIP;
+  if ((e = moe::launch_ffn_stream(a, 2, s)) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range";
+    case MOE_ERR_DTYPE: return "unsupported dtype combination";
+    case MOE_ERR_ALIGN: return "misaligned pointer or stride";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_UNSUPPORTED: return "shape or flags not supported by the kernels";
+    case MOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+moe_status moe_validate(const moe_problem* p) { return check_problem(p); }
+
+size_t moe_workspace_bytes(const moe_problem* p) {
+  if (check_problem(p) != MOE_OK) return 0;
+  return layer_layout(p, nullptr).total;
+}
+
+moe_status moe_route(const moe_problem* p, const void* x, const void* w_router, const void* sh_gate_w,
+                     int32_t* topk_ids, float* topk_w, float* shared_logit, void* ws, size_t ws_bytes,
+                     void* stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_NULL;
+  if (!al16(x) || !al16(w_router) || (sh_gate_w && !al16(sh_gate_w))) return MOE_ERR_ALIGN;
+  if ((st = check_ws(p, ws, ws_bytes)) != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;
+  return do_route(p, x, w_router, sh_gate_w, topk_ids, topk_w, shared_logit, ws, (hipStream_t)stream);
+}
+
+moe_status moe_dispatch(const moe_problem* p, const int32_t* topk_ids, int32_t* expert_offsets,
+                        int32_t* sorted_assign, int32_t* assign_pos, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!topk_ids || !expert_offsets || !sorted_assign || !assign_pos) return MOE_ERR_NULL;
+  if ((st = check_ws(p, ws, ws_bytes)) != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;
+  return hip_status(moe::launch_dispatch(topk_ids, (int)p->T, (int)p->E, (int)p->k, expert_offsets, sorted_assign,
+                                         assign_pos, static_cast<int32_t*>(ws), (hipStream_t)stream));
+}
+
+moe_status moe_expert_ffn(const moe_problem* p, const moe_weights* w, const void* x, const int32_t* expert_offsets,
+                          const int32_t* sorted_assign, void* y, void* y_shared, void* ws, size_t ws_bytes,
+                          void* stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(p, w, false, true)) != MOE_OK) return st;
+  if (!x || !expert_offsets || !sorted_assign || !y) return MOE_ERR_NULL;
+  if (!al16(x) || !al16(y) || (y_shared && !al16(y_shared))) return MOE_ERR_ALIGN;
+  if ((st = check_ws(p, ws, ws_bytes)) != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;
+  return do_ffn(p, w, x, expert_offsets, sorted_assign, y, y_shared, ws, (hipStream_t)stream);
+}
+
+moe_status moe_combine(const moe_problem* p, const void* y, const int32_t* assign_pos, const float* topk_w,
+                       const void* y_shared, const float* shared_logit, void* out, void* stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!y || !assign_pos || !topk_w || !out) return MOE_ERR_NULL;
+  if ((y_shared == nullptr) != (shared_logit == nullptr)) return MOE_ERR_NULL;
+  if (!al16(y) || !al16(out) || (y_shared && !al16(y_shared))) return MOE_ERR_ALIGN;
+  if (p->T == 0) return MOE_OK;
+  return hip_status(moe::launch_combine(y, assign_pos, topk_w, y_shared, shared_logit, out, (int)p->T, (int)p->H,
+                                        (int)p->k, p->act_dtype == MOE_F32 ? 1 : 0, (hipStream_t)stream));
+}
+
+moe_status moe_layer_forward(const moe_problem* p, const moe_weights* w, const void* x, void* out,
+                             int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(p, w, true, true)) != MOE_OK) return st;
+  if (!x || !out) return MOE_ERR_NULL;
+  if (!al16(x) || !al16(out)) return MOE_ERR_ALIGN;
+  if ((st = check_ws(p, ws, ws_bytes)) != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  LayerWs L = layer_layout(p, ws);
+  int32_t* ids = topk_ids ? topk_ids : L.ids;
+  float* tw = topk_w ? topk_w : L.w;
+  const bool sh = p->I_shared > 0;
+  if ((st = do_route(p, x, w->w_router, sh ? w->sh_gate_w : nullptr, ids, tw, sh ? L.sl : nullptr, L.stage, s)) !=
+      MOE_OK)
+    return st;
+  if ((st = hip_status(moe::launch_dispatch(ids, (int)p->T, (int)p->E, (int)p->k, L.offsets, L.sorted, L.pos,
+                                            static_cast<int32_t*>(L.stage), s))) != MOE_OK)
+    return st;
+  if ((st = do_ffn(p, w, x, L.offsets, L.sorted, L.y, sh ? L.y_sh : nullptr, L.stage, s)) != MOE_OK) return st;
+  return hip_status(moe::launch_combine(L.y, L.pos, tw, sh ? L.y_sh : nullptr, sh ? L.sl : nullptr, out, (int)p->T,
+                                        (int)p->H, (int)p->k, p->act_dtype == MOE_F32 ? 1 : 0, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Weighted combine + gated shared expert (Qwen3.8-Flash-Next study, MoE
+// section: the last stage of the pipeline figure and eq. MoE(x)):
+//   out[t] = sum_{j<k} w[t,j] * y[pos[t*k+j]] + sigmoid(s_t) * y_shared[t]
+// One workgroup per token, 16-byte loads of y rows (8 bf16 or 4 fp32 per
+// thread), fp32 accumulation with j ascending, one rounding to the output
+// dtype.  HBM-bound: reads k+1 rows of H and writes one.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+template <bool F32>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y, const int32_t* __restrict__ pos,
+                                                      const float* __restrict__ w, const void* __restrict__ y_sh,
+                                                      const float* __restrict__ sl, void* __restrict__ out, int H,
+                                                      int k) {
+  constexpr int VEC = F32 ? 4 : 8;
+  const int t = blockIdx.x;
+  const float gamma = y_sh ? sigmoid(sl[t]) : 0.f;
+  const int nchunk = H / VEC;
+  for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
+    float acc[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int64_t a = (int64_t)t * k + j;
+      const float wj = w[a];
+      const int64_t p = pos[a];
+      const u32x4 v = ld16(reinterpret_cast<const char*>(y) + (p * H + (int64_t)c * VEC) * (F32 ? 4 : 2));
+      if (F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(wj, __builtin_bit_cast(float, v[i]), acc[i]);
+      } else {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, bf2f(b[i]), acc[i]);
+      }
+    }
+    if (y_sh) {
+      const u32x4 v = ld16(reinterpret_cast<const char*>(y_sh) + ((int64_t)t * H + (int64_t)c * VEC) * (F32 ? 4 : 2));
+      if (F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(gamma, __builtin_bit_cast(float, v[i]), acc[i]);
+      } else {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(gamma, bf2f(b[i]), acc[i]);
+      }
+    }
+    char* dst = reinterpret_cast<char*>(out) + ((int64_t)t * H + (int64_t)c * VEC) * (F32 ? 4 : 2);
+    if (F32) {
+      st16(dst, u32x4{__builtin_bit_cast(uint32_t, acc[0]), __builtin_bit_cast(uint32_t, acc[1]),
+                      __builtin_bit_cast(uint32_t, acc[2]), __builtin_bit_cast(uint32_t, acc[3])});
+    } else {
+      bf16x8 o;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = f2bf(acc[i]);
+      st16(dst, __builtin_bit_cast(u32x4, o));
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* y, const int32_t* pos, const float* w, const void* y_sh,
+                          const float* shared_logit, void* out, int T, int H, int k, int f32, hipStream_t s) {
+  if (f32) combine_kernel<true><<<T, 256, 0, s>>>(y, pos, w, y_sh, shared_logit, out, H, k);
+  else combine_kernel<false><<<T, 256, 0, s>>>(y, pos, w, y_sh, shared_logit, out, H, k);
+  return hipGetLastError();
+}
+
+}  // namespace moe

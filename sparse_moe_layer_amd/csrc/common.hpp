@@ -1,0 +1,54 @@
+// Device-side helpers shared by the MoE kernels (gfx950 / CDNA4 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf2f(bf16 v) { return (float)v; }
+__device__ __forceinline__ bf16 f2bf(float v) { return (bf16)v; }  // round to nearest even
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+// 16-byte global load / store helpers (addresses must be 16-byte aligned).
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Eight OCP e4m3fn codes (two dwords) times one fp32 scale -> eight bf16.
+// gfx950's v_cvt_pk_f32_fp8 decodes the OCP E4M3FN format.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 codes, float scale) {
+  u32x4 out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(codes[h], false);
+    f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(codes[h], true);
+    bf16x2 pa = {f2bf(a.x * scale), f2bf(a.y * scale)};
+    bf16x2 pb = {f2bf(b.x * scale), f2bf(b.y * scale)};
+    out[2 * h] = __builtin_bit_cast(uint32_t, pa);
+    out[2 * h + 1] = __builtin_bit_cast(uint32_t, pb);
+  }
+  return out;
+}
+
+// Wave-wide reductions (64 lanes).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+}  // namespace moe

@@ -1,0 +1,459 @@
+// Grouped expert GEMM on CDNA4 MFMA (v_mfma_f32_32x32x16_bf16), LDS-tiled.
+//
+// One kernel template covers the three dense contractions of the layer
+// (Qwen3.8-Flash-Next study, "MoE: 512 experts behind a width-640
+// intermediate": Router [T, E] and the grouped expert GEMMs of eq. expert(x)):
+//   ROUTER : logits[t, n] = x_t . W_r[n]  (n < E) and x_t . w_sg (n == E), fp32 out
+//   GATEUP : h[r, j] = SiLU(x_t . W_gate[e][j]) * (x_t . W_up[e][j]),  t = sorted[r]/k
+//   DOWN   : y[r, n] = h[r] . W_down[e][n]
+// Every operand is K-contiguous (x rows, weight rows, h rows), so both MFMA
+// fragments are 16-byte LDS reads along K.
+//
+// Tiling: 128 x 128 output tile per 256-thread workgroup (4 waves in 2 x 2,
+// 64 x 64 per wave = 2 x 2 MFMA 32x32 blocks), K step 64, two LDS buffers
+// (64 KB).  The gate/up tile interleaves 32 gate rows and 32 up rows per wave
+// so SiLU(g)*u is formed in registers.  Work is a device-built list of
+// (group, first row) m-tiles; the grid is persistent and walks
+// m-tile x n-tile indices, so no host sync is needed to size it.
+// fp8 routed weights are decoded (OCP e4m3fn x fp32 block scale -> bf16) on
+// their way into LDS.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int BM = kGemmBM;
+constexpr int BN = 128;
+constexpr int BK = 64;
+constexpr int NT = 256;
+
+enum { M_ROUTER = 0, M_GATEUP = 1, M_DOWN = 2 };
+
+struct RouterArgs {
+  const bf16* x;
+  const bf16* wr;
+  const bf16* wsg;  // may be null
+  float* logits;    // [T, N]
+  int T, H, E, N;
+};
+
+// Element offset of the 16-byte chunk `c` of tile row `r` (XOR swizzle).
+__device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ (r & 7)) << 3); }
+
+template <int MODE, bool FP8>
+__global__ __launch_bounds__(NT, 2) void gemm_kernel(FfnArgs f, RouterArgs ra, int n_tiles_n,
+                                                     int list_begin_idx, int list_end_idx) {
+  __shared__ __attribute__((aligned(16))) bf16 sA[2 * BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16 sB[2 * BN * BK];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  int mt_begin, mt_end;
+  if (MODE == M_ROUTER) {
+    mt_begin = 0;
+    mt_end = (ra.T + BM - 1) / BM;
+  } else {
+    // plan ints: [0] gemm tiles total, [2] routed gemm tiles (shared ones follow)
+    mt_begin = list_begin_idx < 0 ? 0 : f.plan[list_begin_idx];
+    mt_end = f.plan[list_end_idx];
+  }
+  const int total = (mt_end - mt_begin) * n_tiles_n;
+
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int mt = mt_begin + tile / n_tiles_n;
+    const int nt = tile % n_tiles_n;
+
+    // ---------------- resolve the group of this m-tile ----------------
+    int g = 0, base = 0, r0, nrows, K, Ncols;
+    if (MODE == M_ROUTER) {
+      r0 = mt * BM;
+      nrows = ra.T - r0;
+      K = ra.H;
+      Ncols = ra.N;
+    } else {
+      g = f.mt_group[mt];
+      r0 = f.mt_row0[mt];
+      const bool shared = g >= f.E;
+      if (!shared) {
+        base = f.offsets[g];
+        nrows = f.offsets[g + 1] - base - r0;
+      } else {
+        nrows = f.T - r0;
+      }
+      if (MODE == M_GATEUP) {
+        K = f.H;
+        Ncols = shared ? f.Is : f.I;
+      } else {
+        K = shared ? f.Is : f.I;
+        Ncols = f.H;
+      }
+    }
+    nrows = nrows < BM ? nrows : BM;
+    const bool shared = (MODE != M_ROUTER) && g >= f.E;
+    const bool fp8_tile = FP8 && !shared;
+    // n-tile coverage: GATEUP covers 64 hidden columns per tile, others 128.
+    const int ncov = (MODE == M_GATEUP) ? 64 : BN;
+    if (nt * ncov >= Ncols) continue;  // uniform across the block
+
+    // ---------------- per-thread operand row pointers ----------------
+    const bf16* a_ptr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int r = (tid >> 3) + 32 * i;
+      r = r < nrows ? r : nrows - 1;  // clamp: rows past the group are computed, never stored
+      const int gr = base + r0 + r;
+      if (MODE == M_ROUTER) {
+        a_ptr[i] = ra.x + (int64_t)gr * ra.H;
+      } else if (MODE == M_GATEUP) {
+        int tok = shared ? gr : f.sorted[gr] / f.k;
+        tok = tok < f.T ? tok : f.T - 1;
+        a_ptr[i] = reinterpret_cast<const bf16*>(f.x) + (int64_t)tok * f.H;
+      } else {
+        a_ptr[i] = shared ? reinterpret_cast<const bf16*>(f.h_sh) + (int64_t)gr * f.Is
+                          : reinterpret_cast<const bf16*>(f.h) + (int64_t)gr * f.I;
+      }
+    }
+    // B rows: bf16 layout uses rows (tid>>3)+32i, chunk tid&7 (4 chunks);
+    // fp8 layout uses rows (tid>>2)+64i, 16-code chunk tid&3 (2 chunks).
+    const void* b_ptr[4];
+    const float* s_ptr[4];
+    const int nb = fp8_tile ? 2 : 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i >= nb) { b_ptr[i] = nullptr; s_ptr[i] = nullptr; continue; }
+      const int n = fp8_tile ? (tid >> 2) + 64 * i : (tid >> 3) + 32 * i;
+      int col;  // matrix row of the weight (output column)
+      bool up = false;
+      if (MODE == M_GATEUP) {
+        const int within = n & 63;
+        up = within >= 32;
+        col = nt * 64 + (n >> 6) * 32 + (within & 31);
+      } else {
+        col = nt * BN + n;
+      }
+      col = col < Ncols ? col : Ncols - 1;
+      if (MODE == M_ROUTER) {
+        b_ptr[i] = col < ra.E ? ra.wr + (int64_t)col * ra.H : ra.wsg;
+        s_ptr[i] = nullptr;
+      } else if (MODE == M_GATEUP) {
+        if (shared) {
+          b_ptr[i] = reinterpret_cast<const bf16*>(up ? f.shu : f.shg) + (int64_t)col * f.H;
+          s_ptr[i] = nullptr;
+        } else if (fp8_tile) {
+          b_ptr[i] = reinterpret_cast<const uint8_t*>(up ? f.wu : f.wg) + (int64_t)g * (up ? f.su : f.sg) +
+                     (int64_t)col * f.H;
+          const int kb = f.H / 128;
+          s_ptr[i] = (up ? f.scu : f.scg) + (int64_t)g * (f.I / 128) * kb + (col / 128) * kb;
+        } else {
+          b_ptr[i] = reinterpret_cast<const bf16*>(up ? f.wu : f.wg) + (int64_t)g * (up ? f.su : f.sg) +
+                     (int64_t)col * f.H;
+          s_ptr[i] = nullptr;
+        }
+      } else {
+        if (shared) {
+          b_ptr[i] = reinterpret_cast<const bf16*>(f.shd) + (int64_t)col * f.Is;
+          s_ptr[i] = nullptr;
+        } else if (fp8_tile) {
+          b_ptr[i] = reinterpret_cast<const uint8_t*>(f.wd) + (int64_t)g * f.sd + (int64_t)col * f.I;
+          const int kb = f.I / 128;
+          s_ptr[i] = f.scd + (int64_t)g * (f.H / 128) * kb + (col / 128) * kb;
+        } else {
+          b_ptr[i] = reinterpret_cast<const bf16*>(f.wd) + (int64_t)g * f.sd + (int64_t)col * f.I;
+          s_ptr[i] = nullptr;
+        }
+      }
+    }
+
+    // ---------------- main loop ----------------
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    u32x4 ra_reg[4], rb_reg[4];
+    float rs_reg[2];
+    const int kc = tid & 7;
+    const int nk = (K + BK - 1) / BK;
+
+    auto gload = [&](int kt) {
+      const int k0 = kt * BK;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kk = k0 + kc * 8;
+        ra_reg[i] = kk < K ? ld16(a_ptr[i] + kk) : u32x4{0, 0, 0, 0};
+      }
+      if (fp8_tile) {
+        const int kk = k0 + (tid & 3) * 16;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          rb_reg[i] = ld16(reinterpret_cast<const uint8_t*>(b_ptr[i]) + kk);
+          rs_reg[i] = s_ptr[i][k0 / 128];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = k0 + kc * 8;
+          rb_reg[i] = kk < K ? ld16(reinterpret_cast<const bf16*>(b_ptr[i]) + kk) : u32x4{0, 0, 0, 0};
+        }
+      }
+    };
+    auto lstore = [&](int buf) {
+      bf16* a = sA + buf * BM * BK;
+      bf16* b = sB + buf * BN * BK;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = (tid >> 3) + 32 * i;
+        *reinterpret_cast<u32x4*>(a + lds_off(r, kc)) = ra_reg[i];
+      }
+      if (fp8_tile) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = (tid >> 2) + 64 * i;
+          const int c = (tid & 3) * 2;
+          u32x2 lo = {rb_reg[i][0], rb_reg[i][1]};
+          u32x2 hi = {rb_reg[i][2], rb_reg[i][3]};
+          *reinterpret_cast<u32x4*>(b + lds_off(r, c)) = fp8x8_to_bf16x8(lo, rs_reg[i]);
+          *reinterpret_cast<u32x4*>(b + lds_off(r, c + 1)) = fp8x8_to_bf16x8(hi, rs_reg[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = (tid >> 3) + 32 * i;
+          *reinterpret_cast<u32x4*>(b + lds_off(r, kc)) = rb_reg[i];
+        }
+      }
+    };
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nk) gload(kt + 1);
+      const bf16* a = sA + buf * BM * BK;
+      const bf16* b = sB + buf * BN * BK;
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const int c = ks * 2 + (lane >> 5);
+        bf16x8 af[2], bfr[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = wm * 64 + i * 32 + (lane & 31);
+          af[i] = *reinterpret_cast<const bf16x8*>(a + lds_off(r, c));
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int r = wn * 64 + j * 32 + (lane & 31);
+          bfr[j] = *reinterpret_cast<const bf16x8*>(b + lds_off(r, c));
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+      if (kt + 1 < nk) lstore(buf ^ 1);
+      __syncthreads();
+    }
+
+    // ---------------- epilogue ----------------
+    // C fragment: lane holds column (lane & 31), rows 8*(v/4) + 4*(lane/32) + v%4.
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rl = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (rl >= nrows) continue;
+        const int64_t gr = base + r0 + rl;
+        if (MODE == M_GATEUP) {
+          const int col = nt * 64 + wn * 32 + (lane & 31);
+          if (col < Ncols) {
+            const float hv = silu(acc[i][0][v]) * acc[i][1][v];
+            bf16* dst = shared ? reinterpret_cast<bf16*>(f.h_sh) + gr * f.Is
+                               : reinterpret_cast<bf16*>(f.h) + gr * f.I;
+            dst[col] = f2bf(hv);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int col = nt * BN + wn * 64 + j * 32 + (lane & 31);
+            if (col >= Ncols) continue;
+            if (MODE == M_ROUTER) {
+              ra.logits[gr * ra.N + col] = acc[i][j][v];
+            } else {
+              bf16* dst = shared ? reinterpret_cast<bf16*>(f.y_sh) : reinterpret_cast<bf16*>(f.y);
+              dst[gr * f.H + col] = f2bf(acc[i][j][v]);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Work planning: per group (routed expert or the shared one) decide the path
+// and emit (group, first row) entries for GEMM m-tiles and streaming m-blocks.
+// Layout of plan ints:
+//   [0] gemm m-tiles total        [1] stream m-blocks total
+//   [2] gemm m-tiles of routed groups (shared group's tiles follow)
+//   [3] stream m-blocks of routed groups
+//   [4..]  mt_group[max_mt], mt_row0[max_mt], sb_group[max_sb], sb_row0[max_sb]
+// ---------------------------------------------------------------------------
+__device__ int block_excl_scan(int v, int* tmp, int* total) {
+  // blockDim.x == 1024 (16 waves)
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int s = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(s, o, 64);
+    if (lane >= o) s += t;
+  }
+  if (lane == 63) tmp[w] = s;
+  __syncthreads();
+  if (w == 0) {
+    int t = lane < 16 ? tmp[lane] : 0;
+    int u = t;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      int q = __shfl_up(u, o, 64);
+      if (lane >= o) u += q;
+    }
+    if (lane < 16) tmp[16 + lane] = u - t;
+    if (lane == 15) *total = u;
+  }
+  __syncthreads();
+  const int r = s - v + tmp[16 + w];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* offsets, int T, int E, int has_shared,
+                                                    uint32_t flags, int32_t* plan, int max_mt, int max_sb) {
+  __shared__ int tmp[32];
+  __shared__ int tot;
+  int32_t* mt_group = plan + 4;
+  int32_t* mt_row0 = mt_group + max_mt;
+  int32_t* sb_group = mt_row0 + max_mt;
+  int32_t* sb_row0 = sb_group + max_sb;
+  const int G = E + (has_shared ? 1 : 0);
+  int carry_mt = 0, carry_sb = 0;
+  for (int g0 = 0; g0 < G; g0 += 1024) {
+    const int g = g0 + threadIdx.x;
+    int n = 0;
+    if (g < E) n = offsets[g + 1] - offsets[g];
+    else if (g < G) n = T;
+    bool gemm = false;
+    if (n > 0) {
+      if (flags & 1u) gemm = true;            // force GEMM
+      else if (flags & 2u) gemm = false;      // force streaming
+      else gemm = n > kStreamMaxRows;
+    }
+    const int cm = gemm ? (n + kGemmBM - 1) / kGemmBM : 0;
+    const int cs = (n > 0 && !gemm) ? (n + kStreamBM - 1) / kStreamBM : 0;
+    // routed groups first in each list, the shared group (g == E) last: since
+    // g ascends with the scan order, this holds automatically.
+    const int om = block_excl_scan(cm, tmp, &tot) + carry_mt;
+    const int tm = tot;
+    const int os = block_excl_scan(cs, tmp, &tot) + carry_sb;
+    const int ts = tot;
+    for (int i = 0; i < cm; ++i) { mt_group[om + i] = g; mt_row0[om + i] = i * kGemmBM; }
+    for (int i = 0; i < cs; ++i) { sb_group[os + i] = g; sb_row0[os + i] = i * kStreamBM; }
+    if (has_shared && g == E) {
+      plan[2] = om;  // routed gemm tiles precede the shared group's
+      plan[3] = os;
+    }
+    carry_mt += tm;
+    carry_sb += ts;
+  }
+  if (threadIdx.x == 0) {
+    plan[0] = carry_mt;
+    plan[1] = carry_sb;
+    if (!has_shared) { plan[2] = carry_mt; plan[3] = carry_sb; }
+  }
+}
+
+inline int max_mtiles(int64_t T, int64_t E, int64_t k, bool shared) {
+  return (int)((T * k + kGemmBM - 1) / kGemmBM + E + (shared ? (T + kGemmBM - 1) / kGemmBM + 1 : 0));
+}
+inline int max_sblocks(int64_t T, int64_t E, int64_t k, bool shared) {
+  return (int)((T * k + kStreamBM - 1) / kStreamBM + E + (shared ? (T + kStreamBM - 1) / kStreamBM + 1 : 0));
+}
+
+int num_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  return cus;
+}
+
+}  // namespace
+
+size_t ffn_plan_ints(int64_t T, int64_t E, int64_t k, bool shared) {
+  return 4 + 2 * (size_t)max_mtiles(T, E, k, shared) + 2 * (size_t)max_sblocks(T, E, k, shared);
+}
+
+void ffn_bind_plan(FfnArgs& a, int32_t* plan) {
+  const bool sh = a.Is > 0;
+  const int mm = max_mtiles(a.T, a.E, a.k, sh), ms = max_sblocks(a.T, a.E, a.k, sh);
+  a.plan = plan;
+  a.mt_group = plan + 4;
+  a.mt_row0 = a.mt_group + mm;
+  a.sb_group = a.mt_row0 + mm;
+  a.sb_row0 = a.sb_group + ms;
+}
+
+hipError_t launch_ffn_plan(const int32_t* offsets, int T, int E, int k, int has_shared, uint32_t flags,
+                           int32_t* plan, hipStream_t s) {
+  const int mm = max_mtiles(T, E, k, has_shared), ms = max_sblocks(T, E, k, has_shared);
+  plan_kernel<<<1, 1024, 0, s>>>(offsets, T, E, has_shared, flags, plan, mm, ms);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_logits_bf16(const void* x, const void* w_router, const void* w_sg, float* logits,
+                                     int T, int H, int E, hipStream_t s) {
+  RouterArgs ra{reinterpret_cast<const bf16*>(x), reinterpret_cast<const bf16*>(w_router),
+                reinterpret_cast<const bf16*>(w_sg), logits, T, H, E, E + (w_sg ? 1 : 0)};
+  const int ntn = (ra.N + BN - 1) / BN;
+  const int tiles = ((T + BM - 1) / BM) * ntn;
+  const int grid = tiles < num_cus() * 2 ? tiles : num_cus() * 2;
+  FfnArgs none{};
+  gemm_kernel<M_ROUTER, false><<<grid, NT, 0, s>>>(none, ra, ntn, -1, 0);
+  return hipGetLastError();
+}
+
+// Tiled MFMA phase of the expert FFN (phase 1: gate/up + SiLU*mul, 2: down).
+hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s) {
+  const bool sh = a.Is > 0;
+  const int mm = max_mtiles(a.T, a.E, a.k, sh);
+  const int wide = a.I > a.Is ? a.I : a.Is;
+  const int ntn = phase == 1 ? (wide + 63) / 64 : (a.H + BN - 1) / BN;
+  const int64_t tiles = (int64_t)mm * ntn;
+  const int grid = (int)(tiles < num_cus() * 2 ? tiles : num_cus() * 2);
+  RouterArgs none{};
+  if (a.fp8) {
+    // routed tiles [0, plan[2]) decode fp8; the shared expert stays bf16
+    if (phase == 1) gemm_kernel<M_GATEUP, true><<<grid, NT, 0, s>>>(a, none, ntn, -1, 2);
+    else gemm_kernel<M_DOWN, true><<<grid, NT, 0, s>>>(a, none, ntn, -1, 2);
+    if (sh) {
+      if (phase == 1) gemm_kernel<M_GATEUP, false><<<grid, NT, 0, s>>>(a, none, ntn, 2, 0);
+      else gemm_kernel<M_DOWN, false><<<grid, NT, 0, s>>>(a, none, ntn, 2, 0);
+    }
+  } else {
+    if (phase == 1) gemm_kernel<M_GATEUP, false><<<grid, NT, 0, s>>>(a, none, ntn, -1, 0);
+    else gemm_kernel<M_DOWN, false><<<grid, NT, 0, s>>>(a, none, ntn, -1, 0);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,58 @@
+// Host-visible launchers of the MoE kernels.  Every launcher enqueues on
+// `stream` and returns hipGetLastError() of its launches.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Rows per MFMA GEMM m-tile and per streaming m-block.
+constexpr int kGemmBM = 128;
+constexpr int kStreamBM = 16;
+// An expert with at most this many rows streams its weights (small-M path).
+constexpr int kStreamMaxRows = 16;
+
+// Everything the grouped expert kernels need to resolve a group (routed
+// expert g < E, or the shared expert g == E) and its operands.
+struct FfnArgs {
+  int T, H, E, k, I, Is;
+  int fp8;                    // routed weights are e4m3fn codes + fp32 block scales
+  const void* x;              // [T, H] bf16
+  const int32_t* offsets;     // [E+1]
+  const int32_t* sorted;      // [R]
+  const void* wg; const void* wu; const void* wd;  // routed, elements: bf16 or u8 codes
+  int64_t sg, su, sd;         // expert strides (elements)
+  const float* scg; const float* scu; const float* scd;  // fp8 block scales
+  const void* shg; const void* shu; const void* shd;     // shared expert (bf16) or null
+  void* h;                    // [R, I]  bf16 hidden of routed rows
+  void* h_sh;                 // [T, Is] bf16 hidden of the shared expert
+  void* y;                    // [R, H]  bf16
+  void* y_sh;                 // [T, H]  bf16 (may be null when Is == 0)
+  // device-built work lists
+  const int32_t* plan;        // plan[0] = #gemm m-tiles, plan[1] = #stream m-blocks
+  const int32_t* mt_group; const int32_t* mt_row0;
+  const int32_t* sb_group; const int32_t* sb_row0;
+};
+
+size_t ffn_plan_ints(int64_t T, int64_t E, int64_t k, bool shared);
+
+hipError_t launch_router_logits_bf16(const void* x, const void* w_router, const void* w_sg,
+                                     float* logits, int T, int H, int E, hipStream_t s);
+hipError_t launch_router_logits_f32(const float* x, const float* w_router, const float* w_sg,
+                                    float* logits, int T, int H, int E, hipStream_t s);
+hipError_t launch_topk(const float* logits, int ldl, int T, int E, int k, int has_sg,
+                       int32_t* ids, float* w, float* shared_logit, hipStream_t s);
+size_t dispatch_ws_ints(int64_t T, int64_t E);
+hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* offsets,
+                           int32_t* sorted, int32_t* pos, int32_t* ws, hipStream_t s);
+hipError_t launch_ffn_plan(const int32_t* offsets, int T, int E, int k, int has_shared, uint32_t flags,
+                           int32_t* plan_ws, hipStream_t s);
+void ffn_bind_plan(FfnArgs& a, int32_t* plan_ws);
+hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s);    // phase 1 gate/up, 2 down
+hipError_t launch_ffn_stream(const FfnArgs& a, int phase, hipStream_t s);  // phase 1 gate/up, 2 down
+hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s);
+hipError_t launch_combine(const void* y, const int32_t* pos, const float* w, const void* y_sh,
+                          const float* shared_logit, void* out, int T, int H, int k, int f32,
+                          hipStream_t s);
+
+}  // namespace moe

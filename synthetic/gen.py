@@ -155,7 +155,7 @@ def hash_stream(keys: torch.Tensor, n: int, device) -> torch.Tensor:
 
 def _keys_tensor(keys, device) -> torch.Tensor:
     arr = [[k & M32, (k >> 32) & M32] for k in keys]
-    return torch.tensor(arr, dtype=torch.int64, device=device)
+    return torch.tensor(arr, dtype=torch.int64, device=device).reshape(-1, 2)
 
 
 def normals(keys, n: int, device) -> torch.Tensor:

@@ -1,0 +1,126 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and
+validates arguments before touching a device (no compute calls here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_moe_layer_amd as lib
+from sparse_moe_layer_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_stage_calls():
+    d = declared()
+    for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_forward"):
+        assert name in d
+
+
+def test_every_declared_symbol_is_exported():
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    syms = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for name in declared():
+        assert name in syms, name
+        assert hasattr(_lib.LIB, name)
+    assert sorted(_lib.EXPORTS) == declared()
+
+
+def test_abi_version_and_status_strings():
+    assert lib.moe_abi_version() == 1
+    for s in range(8):
+        assert _lib.LIB.moe_status_str(s)
+    assert _lib.LIB.moe_status_str(99) == b"unknown status"
+
+
+def test_struct_layout_matches_header():
+    # 6 int64 + 3 int32 + 1 uint32 = 64 bytes; weights: 10 pointers + 3 int64 + 1 pointer
+    assert ctypes.sizeof(_lib.moe_problem) == 64
+    assert ctypes.sizeof(_lib.moe_weights) == 14 * 8
+
+
+OK = _lib.MOE_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), OK),
+    (dict(T=0), OK),
+    (dict(T=-1), _lib.MOE_ERR_SHAPE),
+    (dict(k=0), _lib.MOE_ERR_SHAPE),
+    (dict(k=17), _lib.MOE_ERR_SHAPE),       # k > E
+    (dict(E=2048, k=4), _lib.MOE_ERR_SHAPE),
+    (dict(E=128, k=65), _lib.MOE_ERR_SHAPE),
+    (dict(H=0), _lib.MOE_ERR_SHAPE),
+    (dict(I=0), _lib.MOE_ERR_SHAPE),
+    (dict(I_shared=-8), _lib.MOE_ERR_SHAPE),
+    (dict(act="f32", wdt="bf16"), _lib.MOE_ERR_DTYPE),
+    (dict(act="fp8", wdt="fp8"), _lib.MOE_ERR_DTYPE),
+    (dict(H=252), _lib.MOE_ERR_UNSUPPORTED),  # not a multiple of 8 for bf16
+    (dict(act="f32", wdt="f32", H=252), OK),
+    (dict(wdt="fp8", H=192), _lib.MOE_ERR_UNSUPPORTED),  # fp8 needs multiples of 128
+    (dict(wdt="fp8", scale_block=64), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(wdt="fp8"), OK),
+    (dict(flags=3), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(flags=8), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(T=2 ** 31 // 4), _lib.MOE_ERR_SHAPE),
+])
+def test_validate(kw, status):
+    base = dict(T=64, H=256, E=16, k=4, I=128, I_shared=0, act="bf16", wdt="bf16", scale_block=128, flags=0)
+    base.update(kw)
+    p = lib.problem(**base)
+    assert lib.moe_validate(p) == status
+    assert (lib.moe_workspace_bytes(p) > 0) == (status == OK)
+
+
+def test_workspace_grows_with_tokens():
+    sizes = [lib.moe_workspace_bytes(lib.problem(T, 2560, 512, 10, 640, 640)) for T in (1, 16, 4096)]
+    assert sizes[0] < sizes[1] < sizes[2]
+    assert all(s % 256 == 0 for s in sizes)
+    # the layer call keeps y [R,H] bf16 in the workspace
+    assert sizes[2] >= 4096 * 10 * 2560 * 2
+
+
+def test_entry_points_reject_bad_arguments_before_any_launch():
+    L = _lib.LIB
+    p = lib.problem(64, 256, 16, 4, 128)
+    P = ctypes.byref(p)
+    fake = 1 << 20  # never dereferenced: validation fails first
+    wsz = lib.moe_workspace_bytes(p)
+    assert L.moe_route(None, fake, fake, None, fake, fake, None, fake, wsz, None) == _lib.MOE_ERR_NULL
+    assert L.moe_route(P, None, fake, None, fake, fake, None, fake, wsz, None) == _lib.MOE_ERR_NULL
+    assert L.moe_route(P, fake + 8, fake, None, fake, fake, None, fake, wsz, None) == _lib.MOE_ERR_ALIGN
+    assert L.moe_route(P, fake, fake, None, fake, fake, None, fake, wsz - 1, None) == _lib.MOE_ERR_WORKSPACE
+    assert L.moe_route(P, fake, fake, None, fake, fake, None, fake + 16, wsz, None) == _lib.MOE_ERR_ALIGN
+    assert L.moe_dispatch(P, None, fake, fake, fake, fake, wsz, None) == _lib.MOE_ERR_NULL
+    assert L.moe_combine(P, fake, fake, fake, fake, None, fake, None) == _lib.MOE_ERR_NULL  # y_shared w/o logit
+    w = _lib.moe_weights(fake, fake, fake, None, 0, 0, 0, None, None, None, None, None, None, None)
+    assert L.moe_expert_ffn(P, ctypes.byref(w), fake, fake, fake, fake, None, fake, wsz, None) == _lib.MOE_ERR_NULL
+    w = _lib.moe_weights(fake, fake, fake, fake, 3, 0, 0, None, None, None, None, None, None, None)
+    assert L.moe_expert_ffn(P, ctypes.byref(w), fake, fake, fake, fake, None, fake, wsz, None) == _lib.MOE_ERR_ALIGN
+    w = _lib.moe_weights(fake, fake, fake, fake, -8, 0, 0, None, None, None, None, None, None, None)
+    assert L.moe_expert_ffn(P, ctypes.byref(w), fake, fake, fake, fake, None, fake, wsz, None) == _lib.MOE_ERR_SHAPE
+    # shared expert declared but not passed
+    ps = lib.problem(64, 256, 16, 4, 128, 64)
+    wsz2 = lib.moe_workspace_bytes(ps)
+    w = _lib.moe_weights(fake, fake, fake, fake, 0, 0, 0, None, None, None, None, None, None, None)
+    assert L.moe_layer_forward(ctypes.byref(ps), ctypes.byref(w), fake, fake, None, None, fake, wsz2,
+                               None) == _lib.MOE_ERR_NULL
+    # fp8 needs scales
+    pf = lib.problem(64, 256, 16, 4, 128, 0, "bf16", "fp8")
+    w = _lib.moe_weights(fake, fake, fake, fake, 0, 0, 0, None, None, None, None, None, None, None)
+    assert L.moe_expert_ffn(ctypes.byref(pf), ctypes.byref(w), fake, fake, fake, fake, None, fake,
+                            lib.moe_workspace_bytes(pf), None) == _lib.MOE_ERR_NULL
+    # empty batch: valid no-op, nothing dereferenced
+    p0 = lib.problem(0, 256, 16, 4, 128)
+    assert L.moe_layer_forward(ctypes.byref(p0), ctypes.byref(
+        _lib.moe_weights(fake, fake, fake, fake, 0, 0, 0, None, None, None, None, None, None, None)),
+        fake, fake, None, None, fake, lib.moe_workspace_bytes(p0), None) == OK

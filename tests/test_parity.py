@@ -1,0 +1,218 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Expert ids, the dispatch offsets and permutation must match bit-exact (inputs
+are redrawn until every token's sorted fp32 logits have gaps >= 1e-3 between
+consecutive ranks 1..k+1).  Float outputs must satisfy
+max|gpu - ref| <= tol * max|ref| with tol 2e-2 (bf16), 6e-2 (fp8 weights),
+1e-5 (fp32 layer); routing weights within 1e-5 absolute.
+
+Full-size workloads are checked on every integer output and on sampled
+tokens for the float outputs (the oracle evaluates those tokens one expert at
+a time); small and edge-case layers are checked everywhere.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sparse_moe_layer_amd as lib
+from oracle import adapter
+from sparse_moe_layer_amd.tensors import structs
+from synthetic import CONFIGS, make_problem
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+
+
+def tol(cfg):
+    return TOL["fp8"] if cfg.wdt == "fp8" else TOL[cfg.act]
+
+
+def gpu_problem(cfg, seed=0):
+    print(f"[parity] generating {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I} "
+          f"Is={cfg.I_shared} {cfg.act}/{cfg.wdt} seed={seed}", flush=True)
+    p = make_problem(cfg, seed, device="cuda")
+    adapter.ensure_margin(p, 1e-3)
+    return p
+
+
+def run_stages(p, flags=0):
+    """Each stage through its own entry point, then the whole layer in one call."""
+    c = p.cfg
+    dev = p.x.device
+    T, k, E, H = c.T, c.k, c.E, c.H
+    P, W = structs(p, flags)
+    ws = lib.workspace(P)
+    sh = c.I_shared > 0
+    ids = torch.full((T, k), -1, dtype=torch.int32, device=dev)
+    w = torch.zeros((T, k), dtype=torch.float32, device=dev)
+    sl = torch.zeros(T, dtype=torch.float32, device=dev) if sh else None
+    lib.moe_route(P, p.x, p.w_router, p.sh_gate_w, ids, w, sl, ws)
+    offs = torch.full((E + 1,), -1, dtype=torch.int32, device=dev)
+    sa = torch.full((T * k,), -1, dtype=torch.int32, device=dev)
+    pos = torch.full((T * k,), -1, dtype=torch.int32, device=dev)
+    lib.moe_dispatch(P, ids, offs, sa, pos, ws)
+    y = torch.zeros((T * k, H), dtype=p.x.dtype, device=dev)
+    ysh = torch.zeros((T, H), dtype=p.x.dtype, device=dev) if sh else None
+    lib.moe_expert_ffn(P, W, p.x, offs, sa, y, ysh, ws)
+    out = torch.zeros((T, H), dtype=p.x.dtype, device=dev)
+    lib.moe_combine(P, y, pos, w, ysh, sl, out)
+    out2 = torch.zeros((T, H), dtype=p.x.dtype, device=dev)
+    ids2 = torch.full((T, k), -1, dtype=torch.int32, device=dev)
+    w2 = torch.zeros((T, k), dtype=torch.float32, device=dev)
+    lib.moe_layer_forward(P, W, p.x, out2, ids2, w2, ws)
+    torch.cuda.synchronize()
+    f = lambda t: None if t is None else t.detach().float().cpu().numpy() if t.is_floating_point() else t.cpu().numpy()
+    return dict(ids=f(ids), w=f(w), sl=f(sl), offsets=f(offs), sorted=f(sa), pos=f(pos), y=f(y), ysh=f(ysh),
+                out=f(out), out_layer=f(out2), ids_layer=f(ids2), w_layer=f(w2))
+
+
+def rel_err(a, ref):
+    return np.abs(a - ref).max() / max(np.abs(ref).max(), 1e-30)
+
+
+def check(p, g, tokens=None):
+    c = p.cfg
+    r = adapter.forward(p, tokens)
+    tk = r["tokens"]
+    # integer outputs: bit-exact
+    assert np.array_equal(g["ids"], r["ids"]), "expert ids differ"
+    assert np.array_equal(g["ids_layer"], r["ids"]), "expert ids (layer call) differ"
+    assert np.array_equal(g["offsets"], r["offsets"]), "expert offsets differ"
+    assert np.array_equal(g["sorted"], r["sorted_assign"]), "dispatch permutation differs"
+    assert np.array_equal(g["pos"], r["assign_pos"]), "inverse permutation differs"
+    # routing weights
+    assert np.abs(g["w"] - r["w"]).max() <= 1e-5
+    assert np.abs(g["w_layer"] - r["w"]).max() <= 1e-5
+    if c.I_shared > 0:
+        assert np.abs(g["sl"] - r["shared_logit"]).max() <= 1e-4 * (1 + np.abs(r["shared_logit"]).max())
+    # per-assignment expert outputs (permuted rows) and the shared expert
+    k = c.k
+    rows = g["pos"][(tk[:, None] * k + np.arange(k)[None, :]).reshape(-1)]
+    y_gpu = g["y"][rows].reshape(len(tk), k, c.H)
+    e_y = rel_err(y_gpu, r["y"])
+    assert e_y <= tol(c), f"routed expert outputs rel err {e_y:.3e}"
+    if c.I_shared > 0:
+        e_sh = rel_err(g["ysh"][tk], r["y_shared"])
+        assert e_sh <= tol(c), f"shared expert rel err {e_sh:.3e}"
+    e_out = rel_err(g["out"][tk], r["out"])
+    e_lay = rel_err(g["out_layer"][tk], r["out"])
+    print(f"[parity] {c.name}: y {e_y:.2e} out {e_out:.2e} layer {e_lay:.2e} (tol {tol(c):.0e}) "
+          f"tokens {len(tk)}", flush=True)
+    assert e_out <= tol(c), f"combine output rel err {e_out:.3e}"
+    assert e_lay <= tol(c), f"layer output rel err {e_lay:.3e}"
+    return r
+
+
+def sample_tokens(T, n, seed=0):
+    if n >= T:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(T, n - 2, replace=False).tolist()) | {0, T - 1}
+    return np.array(sorted(pick))
+
+
+# ----------------------------------------------------------------------------
+# The five workloads at full size
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("name,n_tok", [("toy_fp32", None), ("flash_decode", None), ("flash_prefill", 48),
+                                        ("max_fp8", 12), ("max_prefill", 12)])
+def test_workload_parity(name, n_tok):
+    cfg = CONFIGS[name]
+    p = gpu_problem(cfg)
+    g = run_stages(p)
+    check(p, g, None if n_tok is None else sample_tokens(cfg.T, n_tok))
+    del p
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
+# Edge cases (small layers, every token checked)
+# ----------------------------------------------------------------------------
+RAGGED = CONFIGS["flash_prefill"].with_(name="ragged", T=37, H=136, E=12, k=3, I=72, I_shared=40)
+
+
+@pytest.mark.parametrize("flags", [0, lib.MOE_FLAG_FORCE_GEMM, lib.MOE_FLAG_FORCE_STREAM])
+def test_ragged_shapes_both_paths(flags):
+    p = gpu_problem(RAGGED, 1)
+    check(p, run_stages(p, flags))
+
+
+@pytest.mark.parametrize("flags", [lib.MOE_FLAG_FORCE_GEMM, lib.MOE_FLAG_FORCE_STREAM])
+def test_paths_multi_tile_groups(flags):
+    # several m-tiles per expert and several n-tiles, both paths
+    cfg = CONFIGS["flash_prefill"].with_(name="multitile", T=700, H=320, E=4, k=2, I=192, I_shared=96)
+    p = gpu_problem(cfg, 2)
+    check(p, run_stages(p, flags))
+
+
+def test_one_expert_takes_every_token():
+    # a steep per-expert bias: the rank-1 expert wins every token (k = 1)
+    cfg = CONFIGS["max_prefill"].with_(name="all_to_one", T=300, H=256, E=8, k=1, I=128, I_shared=64, zipf_s=8.0)
+    p = gpu_problem(cfg, 3)
+    g = run_stages(p)
+    assert np.count_nonzero(np.diff(g["offsets"])) == 1
+    check(p, g)
+
+
+def test_k_equals_E_and_E1_k1():
+    cfg = CONFIGS["flash_prefill"].with_(name="k_eq_E", T=40, H=128, E=8, k=8, I=64, I_shared=0)
+    p = gpu_problem(cfg, 4)
+    check(p, run_stages(p))
+    cfg = CONFIGS["flash_prefill"].with_(name="E1k1", T=33, H=128, E=1, k=1, I=64, I_shared=64)
+    p = gpu_problem(cfg, 5)
+    g = run_stages(p)
+    assert np.all(g["w"] == 1.0)
+    check(p, g)
+
+
+def test_single_token_and_many_empty_experts():
+    cfg = CONFIGS["flash_decode"].with_(name="one_token", T=1, H=256, E=512, k=10, I=128, I_shared=128)
+    p = gpu_problem(cfg, 6)
+    g = run_stages(p)
+    assert np.count_nonzero(np.diff(g["offsets"])) == 10
+    check(p, g)
+
+
+def test_empty_batch_is_noop():
+    cfg = CONFIGS["flash_prefill"].with_(name="empty", T=0, H=128, E=8, k=2, I=64, I_shared=64)
+    p = make_problem(cfg, 0, device="cuda")
+    P, W = structs(p)
+    ws = lib.workspace(P)
+    out = torch.full((1, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    lib.moe_layer_forward(P, W, p.x, out, None, None, ws)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+@pytest.mark.parametrize("shared", [0, 128])
+def test_fp8_small_with_and_without_shared(shared):
+    cfg = CONFIGS["max_fp8"].with_(name="fp8_small", T=50, H=256, E=8, k=2, I=256, I_shared=shared)
+    for flags in (lib.MOE_FLAG_FORCE_GEMM, lib.MOE_FLAG_FORCE_STREAM):
+        p = gpu_problem(cfg, 7)
+        check(p, run_stages(p, flags))
+
+
+def test_fused_gate_up_strides():
+    cfg = CONFIGS["flash_prefill"].with_(name="fused", T=64, H=128, E=6, k=2, I=64, I_shared=0)
+    p = gpu_problem(cfg, 8)
+    ref = run_stages(p)
+    fused = torch.cat([p.w_gate, p.w_up], dim=1).contiguous()  # [E, 2I, H], gate rows first
+    P, _ = structs(p)
+    W = lib.weights(p.w_router, fused, fused, p.w_down, stride_gate=2 * cfg.I * cfg.H,
+                    stride_up=2 * cfg.I * cfg.H)
+    W.w_up = fused.data_ptr() + cfg.I * cfg.H * fused.element_size()  # up rows follow the gate rows
+    ws = lib.workspace(P)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+    lib.moe_layer_forward(P, W, p.x, out, None, None, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.float().cpu().numpy(), ref["out_layer"])
+
+
+def test_run_to_run_bit_identical():
+    cfg = CONFIGS["flash_prefill"].with_(name="determinism", T=512, H=512, E=64, k=6, I=128, I_shared=128)
+    p = gpu_problem(cfg, 9)
+    a = run_stages(p)
+    b = run_stages(p)
+    for key in ("ids", "w", "offsets", "sorted", "pos", "y", "out", "out_layer"):
+        assert np.array_equal(a[key], b[key]), key
