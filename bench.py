@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Throughput of the routed MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the whole layer over one batch of synthetic input
+resident in HBM: router + top-k, dispatch, grouped gate/up GEMM, grouped down
+GEMM, weighted combine with the gated shared expert, each through its C-ABI
+entry point on the current stream, with HIP events between the stages (the
+same kernels moe_layer_forward launches).  K steps are timed back to back
+between two device synchronisations; stage durations come from the events.
+
+Prints one JSON line: tokens/s for the whole step, the roofline of the
+dominant kernel (algorithmic bytes or FLOPs per launch over its event-timed
+duration), and the fp64 CPU oracle timed on a bounded sample of the same
+workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOADS = ["flash_prefill", "flash_decode", "max_prefill", "max_fp8", "toy_fp32"]
+METRIC = "MoE layer tokens/s + % MFMA peak (prefill) / % HBM BW (decode), 1 MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="flash_prefill", choices=WORKLOADS)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-tokens", type=int, default=192,
+                    help="tokens of the same workload the CPU oracle runs on (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (scale factor for HBM byte counters)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "stream.hip", "common.hpp"):
+        h.update(open(os.path.join(ROOT, "sparse_moe_layer_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_sha") != kernel_source_sha():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(problem, n_tokens):
+    """The fp64 oracle, as it stands, on the first n_tokens tokens of the workload."""
+    import types
+
+    from threadpoolctl import threadpool_info
+
+    from oracle import adapter
+    n = min(n_tokens, problem.cfg.T)
+    sub = types.SimpleNamespace(**{k: getattr(problem, k) for k in (
+        "w_router", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "sh_gate", "sh_up", "sh_down",
+        "sh_gate_w")})
+    sub.cfg = problem.cfg.with_(T=n)
+    sub.x = problem.x[:n]
+    sub.host_raw = problem.host_raw
+    t0 = time.perf_counter()
+    adapter.forward(sub)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {problem.cfg.T} tokens of the same workload, full layer "
+                      f"(route, dispatch, every routed and shared expert, combine) in fp64 NumPy; "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this layer is built and measured on a single MI355X; "
+              "run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import sparse_moe_layer_amd as lib
+    from sparse_moe_layer_amd import accounting as acc
+    from sparse_moe_layer_amd.tensors import structs
+    from synthetic import CONFIGS, make_problem
+
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {cfg.name} on {torch.cuda.get_device_name(dev)}", file=sys.stderr, flush=True)
+    prob = make_problem(cfg, args.seed, device=dev)
+    T, H, E, k, I, Is = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared
+    R = T * k
+    adt = prob.x.dtype
+    sh = Is > 0
+    P, W = structs(prob)
+    ws = lib.workspace(P)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    sl = torch.empty(T, dtype=torch.float32, device=dev) if sh else None
+    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sa = torch.empty(R, dtype=torch.int32, device=dev)
+    pos = torch.empty(R, dtype=torch.int32, device=dev)
+    h = torch.empty((R, I), dtype=adt, device=dev)
+    h_sh = torch.empty((T, Is), dtype=adt, device=dev) if sh else None
+    y = torch.empty((R, H), dtype=adt, device=dev)
+    y_sh = torch.empty((T, H), dtype=adt, device=dev) if sh else None
+    out = torch.empty((T, H), dtype=adt, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev):
+        ev[0].record(stream)
+        lib.moe_route(P, prob.x, prob.w_router, prob.sh_gate_w, ids, tw, sl, ws, stream)
+        ev[1].record(stream)
+        lib.moe_dispatch(P, ids, offs, sa, pos, ws, stream)
+        ev[2].record(stream)
+        lib.moe_expert_gate_up(P, W, prob.x, offs, sa, h, h_sh, ws, stream)
+        ev[3].record(stream)
+        lib.moe_expert_down(P, W, offs, h, h_sh, y, y_sh, ws, stream)
+        ev[4].record(stream)
+        lib.moe_combine(P, y, pos, tw, y_sh, sl, out, stream)
+        ev[5].record(stream)
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for _ in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    evs = [mk() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    names = ["route", "dispatch", "gate_up", "down", "combine"]
+    stage_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, n in enumerate(names)}
+
+    # the whole layer in one call, same buffers (reported beside the staged step)
+    for _ in range(2):
+        lib.moe_layer_forward(P, W, prob.x, out, None, None, ws, stream)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        lib.moe_layer_forward(P, W, prob.x, out, None, None, ws, stream)
+    torch.cuda.synchronize()
+    layer_ms = (time.perf_counter() - t2) * 1e3 / args.steps
+
+    counts = torch.diff(offs).cpu()
+    touched = int((counts > 0).sum())
+    work = acc.layer_work(T, H, E, k, I, Is, cfg.act, cfg.wdt, touched, cfg.scale_block)
+    mfma_peak = acc.PEAK_BF16_TFLOPS  # every contraction runs on bf16 MFMA (fp8 weights are decoded to bf16)
+
+    # dominant kernel: the longer grouped GEMM phase; its bound from its intensity vs the ridge
+    dom = "gate_up" if stage_ms["gate_up"] >= stage_ms["down"] else "down"
+    f_dom = work.flops_gate_up if dom == "gate_up" else work.flops_down
+    b_dom = work.bytes_gate_up if dom == "gate_up" else work.bytes_down
+    t_dom = stage_ms[dom] * 1e-3
+    ridge = mfma_peak * 1e12 / (acc.PEAK_HBM_GBPS * 1e9)
+    if f_dom / b_dom > ridge:
+        ach, peak, unit, bound = f_dom / t_dom / 1e12, mfma_peak, "TFLOP/s", "mfma"
+    else:
+        ach, peak, unit, bound = b_dom / t_dom / 1e9, acc.PEAK_HBM_GBPS, "GB/s", "hbm"
+    kname = "grouped_gemm_" + dom
+    roof = {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
+            "traffic": load_traffic(args.workload, kname), "kernel": kname,
+            "algorithmic": {"flops": f_dom, "bytes": b_dom}}
+
+    t_s = ms_step * 1e-3
+    res = {
+        "metric": METRIC,
+        "value": round(T / t_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.act == "bf16" else "f32",
+        "data": "synthetic (seeded counter-based generator, weights random-init at the pages' shapes)",
+        "config": {"workload": cfg.name, "T": T, "H": H, "E": E, "k": k, "I": I, "I_shared": Is,
+                   "act": cfg.act, "weights": cfg.wdt, "touched_experts": touched,
+                   "max_tokens_per_expert": int(counts.max())},
+        "layer": {"tflops": round(work.flops / t_s / 1e12, 2), "hbm_gbps": round(work.bytes / t_s / 1e9, 1),
+                  "mfma_frac": round(work.flops / t_s / 1e12 / mfma_peak, 4),
+                  "hbm_frac": round(work.bytes / t_s / 1e9 / acc.PEAK_HBM_GBPS, 4),
+                  "single_call_ms": round(layer_ms, 4), "single_call_tokens_per_s": round(T / layer_ms * 1e3, 1)},
+        "stages_ms": {n: round(v, 4) for n, v in stage_ms.items()},
+        "roofline": roof,
+    }
+    if args.cpu_tokens > 0:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(prob, args.cpu_tokens)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

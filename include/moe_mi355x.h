@@ -30,7 +30,8 @@
  *    nothing was enqueued.  MOE_ERR_HIP reports a failed launch
  *    (hipGetLastError); faults during execution surface at the caller's next
  *    synchronisation.  NaN/Inf inputs give unspecified outputs.
- *  - T == 0 is a valid no-op returning MOE_OK; nothing is written.
+ *  - T == 0 is a valid no-op returning MOE_OK once the problem itself is
+ *    valid; no pointer is read or written (they may be NULL).
  *  - Routing ties: experts are ordered by descending fp32 logit, equal logits
  *    by ascending expert id.  Results are deterministic run to run.
  *  - Expert ids, the dispatch permutation and all integer outputs are exact;
@@ -170,6 +171,22 @@ moe_status moe_dispatch(const moe_problem* p, const int32_t* topk_ids,
 moe_status moe_expert_ffn(const moe_problem* p, const moe_weights* w, const void* x,
                           const int32_t* expert_offsets, const int32_t* sorted_assign,
                           void* y, void* y_shared, void* ws, size_t ws_bytes, void* stream);
+
+/* The two grouped GEMM phases of moe_expert_ffn as separate calls (same
+ * kernels; each call plans its own work lists from expert_offsets):
+ *   gate/up: h[r] = SiLU(W_gate[e] x_t) * (W_up[e] x_t) for every dispatched
+ *            row r (h [R, I] act, permuted order) and, if h_shared != NULL and
+ *            the problem has a shared expert, h_shared[t] ([T, I_shared] act);
+ *   down   : y[r] = W_down[e] h[r] (y [R, H] act) and, if y_shared and
+ *            h_shared are non-NULL, y_shared[t] = S_down h_shared[t].
+ * h is rounded to the activation dtype between the phases, exactly as inside
+ * moe_expert_ffn.                                                            */
+moe_status moe_expert_gate_up(const moe_problem* p, const moe_weights* w, const void* x,
+                              const int32_t* expert_offsets, const int32_t* sorted_assign,
+                              void* h, void* h_shared, void* ws, size_t ws_bytes, void* stream);
+moe_status moe_expert_down(const moe_problem* p, const moe_weights* w, const int32_t* expert_offsets,
+                           const void* h, const void* h_shared, void* y, void* y_shared,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /* Weighted combine + gated shared expert ("Weighted combine + gated shared
  * expert"; eq. MoE(x)):

@@ -89,6 +89,17 @@ def moe_expert_ffn(p, w: moe_weights, x, expert_offsets, sorted_assign, y, y_sha
                               _ptr(y), _ptr(y_shared), _ptr(ws), ws.numel(), _stream(stream)), "moe_expert_ffn")
 
 
+def moe_expert_gate_up(p, w: moe_weights, x, expert_offsets, sorted_assign, h, h_shared, ws, stream=None):
+    _check(LIB.moe_expert_gate_up(ctypes.byref(p), ctypes.byref(w), _ptr(x), _ptr(expert_offsets),
+                                  _ptr(sorted_assign), _ptr(h), _ptr(h_shared), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "moe_expert_gate_up")
+
+
+def moe_expert_down(p, w: moe_weights, expert_offsets, h, h_shared, y, y_shared, ws, stream=None):
+    _check(LIB.moe_expert_down(ctypes.byref(p), ctypes.byref(w), _ptr(expert_offsets), _ptr(h), _ptr(h_shared),
+                               _ptr(y), _ptr(y_shared), _ptr(ws), ws.numel(), _stream(stream)), "moe_expert_down")
+
+
 def moe_combine(p, y, assign_pos, topk_w, y_shared, shared_logit, out, stream=None):
     _check(LIB.moe_combine(ctypes.byref(p), _ptr(y), _ptr(assign_pos), _ptr(topk_w), _ptr(y_shared),
                            _ptr(shared_logit), _ptr(out), _stream(stream)), "moe_combine")

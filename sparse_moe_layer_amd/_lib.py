@@ -20,7 +20,8 @@ MOE_FLAG_FORCE_GEMM = 1
 MOE_FLAG_FORCE_STREAM = 2
 
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_validate", "moe_workspace_bytes", "moe_route",
-           "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_forward"]
+           "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",
+           "moe_layer_forward"]
 
 
 class moe_problem(ctypes.Structure):
@@ -39,7 +40,7 @@ class moe_weights(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_moe_layer_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python sparse_moe_layer_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(moe_problem)
     W = ctypes.POINTER(moe_weights)
@@ -52,6 +53,8 @@ def _load():
         "moe_route": (i32, [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moe_dispatch": (i32, [P, vp, vp, vp, vp, vp, sz, vp]),
         "moe_expert_ffn": (i32, [P, W, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_expert_gate_up": (i32, [P, W, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_expert_down": (i32, [P, W, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moe_combine": (i32, [P, vp, vp, vp, vp, vp, vp, vp]),
         "moe_layer_forward": (i32, [P, W, vp, vp, vp, vp, vp, sz, vp]),
     }

@@ -1,0 +1,71 @@
+"""Algorithmic work of the routed MoE layer: FLOPs and HBM bytes that the
+method must spend (no padding, no re-reads, no intermediates beyond the
+stage boundaries).  Used to turn measured times into TFLOP/s, GB/s and
+roofline fractions.
+
+Weight counts follow the Qwen3.8-Flash-Next study's MoE section ("routed
+bank = 48 x 512 x 3 x 2560 x 640"; ten experts per token select 2.359B
+weights across layers) and the byte accounting of "Qwen3.8, weights in
+hand", section "What FP8 actually quantizes" (routed parameters at one byte
+in FP8, everything else at two).
+"""
+from __future__ import annotations
+
+import dataclasses
+
+# MI355X published peaks (dense): bf16 MFMA 2.5 PFLOP/s, fp8 5.0, HBM3E 8 TB/s
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBPS = 8000.0
+
+WBYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+
+
+def routed_params_per_layer(E: int, H: int, I: int) -> int:
+    """gate, up and down matrices of every routed expert: E * 3 * H * I."""
+    return E * 3 * H * I
+
+
+def selected_params_per_token(k: int, H: int, I: int) -> int:
+    return k * 3 * H * I
+
+
+@dataclasses.dataclass
+class Work:
+    flops: float          # whole layer
+    bytes: float          # whole layer
+    flops_gate_up: float
+    bytes_gate_up: float
+    flops_down: float
+    bytes_down: float
+
+
+def layer_work(T, H, E, k, I, I_shared, act="bf16", wdt="bf16", touched=None, scale_block=128) -> Work:
+    """touched: number of experts with at least one token (default: min(E, T*k))."""
+    R = T * k
+    if touched is None:
+        touched = min(E, R)
+    a = WBYTES[act]
+    wb = WBYTES[wdt]
+    sh = I_shared > 0
+    # FLOPs: router (E columns + the shared gate column), routed SwiGLU, shared SwiGLU
+    f_router = 2.0 * T * H * (E + (1 if sh else 0))
+    f_gu = 4.0 * R * H * I + (4.0 * T * H * I_shared if sh else 0.0)
+    f_dn = 2.0 * R * H * I + (2.0 * T * H * I_shared if sh else 0.0)
+    # bytes of weights read once per touched expert
+    w_gu = touched * 2.0 * I * H * wb
+    w_dn = touched * 1.0 * H * I * wb
+    if wdt == "fp8":
+        nb = (I // scale_block) * (H // scale_block) * 4.0
+        w_gu += touched * 2 * nb
+        w_dn += touched * nb
+    sh_gu = 2.0 * I_shared * H * a if sh else 0.0
+    sh_dn = 1.0 * H * I_shared * a if sh else 0.0
+    x_b = 1.0 * T * H * a
+    h_b = (1.0 * R * I + (T * I_shared if sh else 0)) * a
+    y_b = (1.0 * R * H + (T * H if sh else 0)) * a
+    b_gu = w_gu + sh_gu + x_b + h_b
+    b_dn = w_dn + sh_dn + h_b + y_b
+    b_layer = w_gu + w_dn + sh_gu + sh_dn + E * H * a + (H * a if sh else 0) + x_b + 1.0 * T * H * a
+    return Work(flops=f_router + f_gu + f_dn, bytes=b_layer, flops_gate_up=f_gu, bytes_gate_up=b_gu,
+                flops_down=f_dn, bytes_down=b_dn)

@@ -1,6 +1,7 @@
 """Build the HIP library libmoe_mi355x.so in-tree for gfx950.
 
-    python -m sparse_moe_layer_amd.build        (or build() from Python)
+    python sparse_moe_layer_amd/build.py   (runs without importing the package,
+                                           which needs the built library)
 
 Every source is compiled with hipcc for --offload-arch=gfx950 only.
 """

@@ -156,15 +156,15 @@ moe_status do_route(const moe_problem* p, const void* x, const void* w_router, c
   return hip_status(moe::launch_topk(logits, E + (wsg ? 1 : 0), T, E, k, wsg ? 1 : 0, ids, w, sl, s));
 }
 
-moe_status do_ffn(const moe_problem* p, const moe_weights* w, const void* x, const int32_t* offsets,
-                  const int32_t* sorted, void* y, void* y_sh, void* stage, hipStream_t s) {
+FfnArgs ffn_args(const moe_problem* p, const moe_weights* w, const void* x, const int32_t* offsets,
+                 const int32_t* sorted, bool shared) {
   FfnArgs a{};
   a.T = (int)p->T;
   a.H = (int)p->H;
   a.E = (int)p->E;
   a.k = (int)p->k;
   a.I = (int)p->I;
-  a.Is = (p->I_shared > 0 && y_sh) ? (int)p->I_shared : 0;
+  a.Is = (p->I_shared > 0 && shared) ? (int)p->I_shared : 0;
   a.fp8 = p->w_dtype == MOE_FP8_E4M3FN;
   a.x = x;
   a.offsets = offsets;
@@ -181,23 +181,38 @@ moe_status do_ffn(const moe_problem* p, const moe_weights* w, const void* x, con
   a.shg = w->sh_gate;
   a.shu = w->sh_up;
   a.shd = w->sh_down;
+  return a;
+}
+
+// phases: bit 0 gate/up, bit 1 down.  The plan kernel runs first (bf16/fp8).
+moe_status run_ffn(const moe_problem* p, FfnArgs& a, int phases, void* plan_ws, hipStream_t s) {
+  if (p->act_dtype == MOE_F32) return hip_status(moe::launch_ffn_f32(a, phases, s));
+  int32_t* plan = static_cast<int32_t*>(plan_ws);
+  if (moe::launch_ffn_plan(a.offsets, a.T, a.E, a.k, a.Is > 0 ? 1 : 0, p->flags, plan, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  moe::ffn_bind_plan(a, plan);
+  if (phases & 1) {
+    if (moe::launch_ffn_gemm(a, 1, s) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_ffn_stream(a, 1, s) != hipSuccess) return MOE_ERR_HIP;
+  }
+  if (phases & 2) {
+    if (moe::launch_ffn_gemm(a, 2, s) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_ffn_stream(a, 2, s) != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+moe_status do_ffn(const moe_problem* p, const moe_weights* w, const void* x, const int32_t* offsets,
+                  const int32_t* sorted, void* y, void* y_sh, void* stage, hipStream_t s) {
+  FfnArgs a = ffn_args(p, w, x, offsets, sorted, y_sh != nullptr);
   a.y = y;
   a.y_sh = a.Is ? y_sh : nullptr;
   // stage scratch: plan ints | h | h_sh
   char* b = static_cast<char*>(stage);
   const size_t plan_bytes = up(moe::ffn_plan_ints(p->T, p->E, p->k, a.Is > 0) * 4);
-  int32_t* plan = reinterpret_cast<int32_t*>(b);
   a.h = b + plan_bytes;
   a.h_sh = b + plan_bytes + up((size_t)p->T * p->k * p->I * act_bytes(p));
-  if (p->act_dtype == MOE_F32) return hip_status(moe::launch_ffn_f32(a, s));
-  hipError_t e = moe::launch_ffn_plan(offsets, a.T, a.E, a.k, a.Is > 0 ? 1 : 0, p->flags, plan, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  moe::ffn_bind_plan(a, plan);
-  if ((e = moe::launch_ffn_gemm(a, 1, s)) != hipSuccess) return MOE_ERR_HIP;
-  if ((e = moe::launch_ffn_stream(a, 1, s)) != hipSuccess) return MOE_ERR_HIP;
-  if ((e = moe::launch_ffn_gemm(a, 2, s)) != hipSuccess) return MOE_ERR_HIP;
-  if ((e = moe::launch_ffn_stream(a, 2, s)) != hipSuccess) return MOE_ERR_HIP;
-  return MOE_OK;
+  return run_ffn(p, a, 3, b, s);
 }
 
 }  // namespace
@@ -232,10 +247,10 @@ moe_status moe_route(const moe_problem* p, const void* x, const void* w_router, 
                      void* stream) {
   moe_status st = check_problem(p);
   if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;  // empty batch: nothing to read or write
   if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_NULL;
   if (!al16(x) || !al16(w_router) || (sh_gate_w && !al16(sh_gate_w))) return MOE_ERR_ALIGN;
   if ((st = check_ws(p, ws, ws_bytes)) != MOE_OK) return st;
-  if (p->T == 0) return MOE_OK;
   return do_route(p, x, w_router, sh_gate_w, topk_ids, topk_w, shared_logit, ws, (hipStream_t)stream);
 }
 
@@ -243,9 +258,9 @@ moe_status moe_dispatch(const moe_problem* p, const int32_t* topk_ids, int32_t* 
                         int32_t* sorted_assign, int32_t* assign_pos, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_problem(p);
   if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;  // empty batch: nothing to read or write
   if (!topk_ids || !expert_offsets || !sorted_assign || !assign_pos) return MOE_ERR_NULL;
   if ((st = check_ws(p, ws, ws_bytes)) != MOE_OK) return st;
-  if (p->T == 0) return MOE_OK;
   return hip_status(moe::launch_dispatch(topk_ids, (int)p->T, (int)p->E, (int)p->k, expert_offsets, sorted_assign,
                                          assign_pos, static_cast<int32_t*>(ws), (hipStream_t)stream));
 }
@@ -255,22 +270,57 @@ moe_status moe_expert_ffn(const moe_problem* p, const moe_weights* w, const void
                           void* stream) {
   moe_status st = check_problem(p);
   if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;  // empty batch: nothing to read or write
   if ((st = check_weights(p, w, false, true)) != MOE_OK) return st;
   if (!x || !expert_offsets || !sorted_assign || !y) return MOE_ERR_NULL;
   if (!al16(x) || !al16(y) || (y_shared && !al16(y_shared))) return MOE_ERR_ALIGN;
   if ((st = check_ws(p, ws, ws_bytes)) != MOE_OK) return st;
-  if (p->T == 0) return MOE_OK;
   return do_ffn(p, w, x, expert_offsets, sorted_assign, y, y_shared, ws, (hipStream_t)stream);
+}
+
+moe_status moe_expert_gate_up(const moe_problem* p, const moe_weights* w, const void* x,
+                              const int32_t* expert_offsets, const int32_t* sorted_assign, void* h, void* h_shared,
+                              void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;  // empty batch: nothing to read or write
+  if ((st = check_weights(p, w, false, true)) != MOE_OK) return st;
+  if (!x || !expert_offsets || !sorted_assign || !h) return MOE_ERR_NULL;
+  if (!al16(x) || !al16(h) || (h_shared && !al16(h_shared))) return MOE_ERR_ALIGN;
+  if ((st = check_ws(p, ws, ws_bytes)) != MOE_OK) return st;
+  FfnArgs a = ffn_args(p, w, x, expert_offsets, sorted_assign, h_shared != nullptr);
+  a.h = h;
+  a.h_sh = a.Is ? h_shared : nullptr;
+  return run_ffn(p, a, 1, ws, (hipStream_t)stream);
+}
+
+moe_status moe_expert_down(const moe_problem* p, const moe_weights* w, const int32_t* expert_offsets,
+                           const void* h, const void* h_shared, void* y, void* y_shared, void* ws, size_t ws_bytes,
+                           void* stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;  // empty batch: nothing to read or write
+  if ((st = check_weights(p, w, false, true)) != MOE_OK) return st;
+  if (!expert_offsets || !h || !y) return MOE_ERR_NULL;
+  if ((h_shared == nullptr) != (y_shared == nullptr)) return MOE_ERR_NULL;
+  if (!al16(h) || !al16(y) || (h_shared && !al16(h_shared)) || (y_shared && !al16(y_shared))) return MOE_ERR_ALIGN;
+  if ((st = check_ws(p, ws, ws_bytes)) != MOE_OK) return st;
+  FfnArgs a = ffn_args(p, w, nullptr, expert_offsets, nullptr, y_shared != nullptr);
+  a.h = const_cast<void*>(h);
+  a.h_sh = a.Is ? const_cast<void*>(h_shared) : nullptr;
+  a.y = y;
+  a.y_sh = a.Is ? y_shared : nullptr;
+  return run_ffn(p, a, 2, ws, (hipStream_t)stream);
 }
 
 moe_status moe_combine(const moe_problem* p, const void* y, const int32_t* assign_pos, const float* topk_w,
                        const void* y_shared, const float* shared_logit, void* out, void* stream) {
   moe_status st = check_problem(p);
   if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;  // empty batch: nothing to read or write
   if (!y || !assign_pos || !topk_w || !out) return MOE_ERR_NULL;
   if ((y_shared == nullptr) != (shared_logit == nullptr)) return MOE_ERR_NULL;
   if (!al16(y) || !al16(out) || (y_shared && !al16(y_shared))) return MOE_ERR_ALIGN;
-  if (p->T == 0) return MOE_OK;
   return hip_status(moe::launch_combine(y, assign_pos, topk_w, y_shared, shared_logit, out, (int)p->T, (int)p->H,
                                         (int)p->k, p->act_dtype == MOE_F32 ? 1 : 0, (hipStream_t)stream));
 }
@@ -279,11 +329,11 @@ moe_status moe_layer_forward(const moe_problem* p, const moe_weights* w, const v
                              int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_problem(p);
   if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;  // empty batch: nothing to read or write
   if ((st = check_weights(p, w, true, true)) != MOE_OK) return st;
   if (!x || !out) return MOE_ERR_NULL;
   if (!al16(x) || !al16(out)) return MOE_ERR_ALIGN;
   if ((st = check_ws(p, ws, ws_bytes)) != MOE_OK) return st;
-  if (p->T == 0) return MOE_OK;
   hipStream_t s = (hipStream_t)stream;
   LayerWs L = layer_layout(p, ws);
   int32_t* ids = topk_ids ? topk_ids : L.ids;

@@ -10,12 +10,27 @@
 namespace moe {
 namespace {
 
+// acc[0..VEC) += wgt * (16 bytes of y: 4 fp32 or 8 bf16)
+template <bool F32>
+__device__ __forceinline__ void accumulate(float* acc, float wgt, u32x4 v) {
+  if constexpr (F32) {
+    const f32x4 f = __builtin_bit_cast(f32x4, v);  // whole-vector cast (not per element)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(wgt, f[i], acc[i]);
+  } else {
+    const bf16x8 b = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt, bf2f(b[i]), acc[i]);
+  }
+}
+
 template <bool F32>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y, const int32_t* __restrict__ pos,
                                                       const float* __restrict__ w, const void* __restrict__ y_sh,
                                                       const float* __restrict__ sl, void* __restrict__ out, int H,
                                                       int k) {
   constexpr int VEC = F32 ? 4 : 8;
+  constexpr int ESZ = F32 ? 4 : 2;
   const int t = blockIdx.x;
   const float gamma = y_sh ? sigmoid(sl[t]) : 0.f;
   const int nchunk = H / VEC;
@@ -27,31 +42,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
       const int64_t a = (int64_t)t * k + j;
       const float wj = w[a];
       const int64_t p = pos[a];
-      const u32x4 v = ld16(reinterpret_cast<const char*>(y) + (p * H + (int64_t)c * VEC) * (F32 ? 4 : 2));
-      if (F32) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = fmaf(wj, __builtin_bit_cast(float, v[i]), acc[i]);
-      } else {
-        const bf16x8 b = __builtin_bit_cast(bf16x8, v);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, bf2f(b[i]), acc[i]);
-      }
+      const u32x4 v = ld16(reinterpret_cast<const char*>(y) + (p * H + (int64_t)c * VEC) * ESZ);
+      accumulate<F32>(acc, wj, v);
     }
     if (y_sh) {
-      const u32x4 v = ld16(reinterpret_cast<const char*>(y_sh) + ((int64_t)t * H + (int64_t)c * VEC) * (F32 ? 4 : 2));
-      if (F32) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = fmaf(gamma, __builtin_bit_cast(float, v[i]), acc[i]);
-      } else {
-        const bf16x8 b = __builtin_bit_cast(bf16x8, v);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(gamma, bf2f(b[i]), acc[i]);
-      }
+      const u32x4 v = ld16(reinterpret_cast<const char*>(y_sh) + ((int64_t)t * H + (int64_t)c * VEC) * ESZ);
+      accumulate<F32>(acc, gamma, v);
     }
-    char* dst = reinterpret_cast<char*>(out) + ((int64_t)t * H + (int64_t)c * VEC) * (F32 ? 4 : 2);
-    if (F32) {
-      st16(dst, u32x4{__builtin_bit_cast(uint32_t, acc[0]), __builtin_bit_cast(uint32_t, acc[1]),
-                      __builtin_bit_cast(uint32_t, acc[2]), __builtin_bit_cast(uint32_t, acc[3])});
+    char* dst = reinterpret_cast<char*>(out) + ((int64_t)t * H + (int64_t)c * VEC) * ESZ;
+    if constexpr (F32) {
+      st16(dst, __builtin_bit_cast(u32x4, f32x4{acc[0], acc[1], acc[2], acc[3]}));
     } else {
       bf16x8 o;
 #pragma unroll

@@ -50,7 +50,7 @@ hipError_t launch_ffn_plan(const int32_t* offsets, int T, int E, int k, int has_
 void ffn_bind_plan(FfnArgs& a, int32_t* plan_ws);
 hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s);    // phase 1 gate/up, 2 down
 hipError_t launch_ffn_stream(const FfnArgs& a, int phase, hipStream_t s);  // phase 1 gate/up, 2 down
-hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn_f32(const FfnArgs& a, int phases, hipStream_t s);  // bit 0 gate/up, bit 1 down
 hipError_t launch_combine(const void* y, const int32_t* pos, const float* w, const void* y_sh,
                           const float* shared_logit, void* out, int T, int H, int k, int f32,
                           hipStream_t s);

@@ -80,13 +80,13 @@ __global__ void down_f32(FfnArgs f, int R, int rows) {
 
 }  // namespace
 
-hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_ffn_f32(const FfnArgs& a, int phases, hipStream_t s) {
   const int R = a.T * a.k;
-  const int rows = R + (a.Is > 0 && a.y_sh ? a.T : 0);
+  const int rows = R + (a.Is > 0 ? a.T : 0);
   const int wide = a.I > a.Is ? a.I : a.Is;
   const int64_t n1 = (int64_t)rows * wide, n2 = (int64_t)rows * a.H;
-  if (n1 > 0) gateup_f32<<<(unsigned)((n1 + 255) / 256), 256, 0, s>>>(a, R, rows);
-  if (n2 > 0) down_f32<<<(unsigned)((n2 + 255) / 256), 256, 0, s>>>(a, R, rows);
+  if ((phases & 1) && n1 > 0) gateup_f32<<<(unsigned)((n1 + 255) / 256), 256, 0, s>>>(a, R, rows);
+  if ((phases & 2) && n2 > 0) down_f32<<<(unsigned)((n2 + 255) / 256), 256, 0, s>>>(a, R, rows);
   return hipGetLastError();
 }
 

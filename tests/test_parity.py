@@ -55,6 +55,13 @@ def run_stages(p, flags=0):
     y = torch.zeros((T * k, H), dtype=p.x.dtype, device=dev)
     ysh = torch.zeros((T, H), dtype=p.x.dtype, device=dev) if sh else None
     lib.moe_expert_ffn(P, W, p.x, offs, sa, y, ysh, ws)
+    # the two GEMM phases as separate calls must give the same bits
+    hh = torch.zeros((T * k, c.I), dtype=p.x.dtype, device=dev)
+    hh_sh = torch.zeros((T, c.I_shared), dtype=p.x.dtype, device=dev) if sh else None
+    y2 = torch.zeros_like(y)
+    y2_sh = torch.zeros_like(ysh) if sh else None
+    lib.moe_expert_gate_up(P, W, p.x, offs, sa, hh, hh_sh, ws)
+    lib.moe_expert_down(P, W, offs, hh, hh_sh, y2, y2_sh, ws)
     out = torch.zeros((T, H), dtype=p.x.dtype, device=dev)
     lib.moe_combine(P, y, pos, w, ysh, sl, out)
     out2 = torch.zeros((T, H), dtype=p.x.dtype, device=dev)
@@ -63,6 +70,10 @@ def run_stages(p, flags=0):
     lib.moe_layer_forward(P, W, p.x, out2, ids2, w2, ws)
     torch.cuda.synchronize()
     f = lambda t: None if t is None else t.detach().float().cpu().numpy() if t.is_floating_point() else t.cpu().numpy()
+    assert torch.equal(y.view(torch.int16) if y.dtype == torch.bfloat16 else y,
+                       y2.view(torch.int16) if y2.dtype == torch.bfloat16 else y2), "split GEMM phases differ"
+    if sh:
+        assert torch.equal(ysh.float(), y2_sh.float()), "split GEMM phases differ (shared)"
     return dict(ids=f(ids), w=f(w), sl=f(sl), offsets=f(offs), sorted=f(sa), pos=f(pos), y=f(y), ysh=f(ysh),
                 out=f(out), out_layer=f(out2), ids_layer=f(ids2), w_layer=f(w2))
 
