@@ -38,6 +38,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="flash_prefill", choices=WORKLOADS)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--gemm-tile", default="auto", choices=["auto", "128", "256"],
+                    help="pin the MFMA GEMM kernel (A/B runs); default picks by rows per expert")
+    ap.add_argument("--path", default="auto", choices=["auto", "gemm", "stream"],
+                    help="pin every expert to one path (A/B runs); default picks per expert by rows")
     ap.add_argument("--cpu-tokens", type=int, default=192,
                     help="tokens of the same workload the CPU oracle runs on (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -59,7 +63,7 @@ def copy_calibration():
 
 def kernel_source_sha():
     h = hashlib.sha256()
-    for f in ("gemm.hip", "stream.hip", "common.hpp"):
+    for f in ("gemm.hip", "gemm_big.hip", "stream.hip", "common.hpp"):
         h.update(open(os.path.join(ROOT, "sparse_moe_layer_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -127,7 +131,9 @@ def main():
     R = T * k
     adt = prob.x.dtype
     sh = Is > 0
-    P, W = structs(prob)
+    flags = {"auto": 0, "128": lib.MOE_FLAG_GEMM_TILE_128, "256": lib.MOE_FLAG_GEMM_TILE_256}[args.gemm_tile]
+    flags |= {"auto": 0, "gemm": lib.MOE_FLAG_FORCE_GEMM, "stream": lib.MOE_FLAG_FORCE_STREAM}[args.path]
+    P, W = structs(prob, flags)
     ws = lib.workspace(P)
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     tw = torch.empty((T, k), dtype=torch.float32, device=dev)
@@ -216,7 +222,7 @@ def main():
         "data": "synthetic (seeded counter-based generator, weights random-init at the pages' shapes)",
         "config": {"workload": cfg.name, "T": T, "H": H, "E": E, "k": k, "I": I, "I_shared": Is,
                    "act": cfg.act, "weights": cfg.wdt, "touched_experts": touched,
-                   "max_tokens_per_expert": int(counts.max())},
+                   "max_tokens_per_expert": int(counts.max()), "gemm_tile": args.gemm_tile, "path": args.path},
         "layer": {"tflops": round(work.flops / t_s / 1e12, 2), "hbm_gbps": round(work.bytes / t_s / 1e9, 1),
                   "mfma_frac": round(work.flops / t_s / 1e12 / mfma_peak, 4),
                   "hbm_frac": round(work.bytes / t_s / 1e9 / acc.PEAK_HBM_GBPS, 4),

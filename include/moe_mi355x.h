@@ -75,7 +75,8 @@ typedef enum {
  *       section "What FP8 actually quantizes"); scale_block must be 128 and
  *       H, I multiples of 128.
  * Limits: 1 <= E <= 1024, 1 <= k <= min(E, 64), H and I multiples of 8 (bf16)
- * or of 4 (f32), I_shared 0 or a multiple of 8; T*k < 2^31.                  */
+ * or of 4 (f32), I_shared 0 or a multiple of 8; every tensor below 2^31
+ * elements (T*H, T*k*H, T*k*I, T*I_shared, I*H, I_shared*H).                 */
 typedef struct {
   int64_t T;          /* tokens                                               */
   int64_t H;          /* hidden width                                          */
@@ -93,6 +94,12 @@ typedef struct {
  * streaming path (default: per expert, by its token count).  For A/B tests. */
 #define MOE_FLAG_FORCE_GEMM   (1u << 0)
 #define MOE_FLAG_FORCE_STREAM (1u << 1)
+/* Tile height of the MFMA GEMM path: 128-row LDS-tiled kernel or 256-row
+ * direct-load kernel (default: 256 when experts average >= 256 rows).  The
+ * 256-row kernel needs bf16 weights and H, I, I_shared multiples of 64;
+ * otherwise the 128-row kernel runs whatever the flag says.  For A/B tests. */
+#define MOE_FLAG_GEMM_TILE_128 (1u << 2)
+#define MOE_FLAG_GEMM_TILE_256 (1u << 3)
 
 /* Weights.  Layouts follow PyTorch Linear (out x in), which matches the GGUF
  * shapes on the Qwen3.8-2.4T-A95B hub discussion's zero-fraction table

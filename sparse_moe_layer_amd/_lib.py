@@ -18,6 +18,8 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKS
 MOE_F32, MOE_BF16, MOE_FP8_E4M3FN = 0, 1, 2
 MOE_FLAG_FORCE_GEMM = 1
 MOE_FLAG_FORCE_STREAM = 2
+MOE_FLAG_GEMM_TILE_128 = 4
+MOE_FLAG_GEMM_TILE_256 = 8
 
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_validate", "moe_workspace_bytes", "moe_route",
            "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",

@@ -24,6 +24,22 @@ size_t w_bytes(const moe_problem* p) {
 }
 
 // ---------------------------------------------------------------------------
+// router form: fp32 SIMT (fp32 layers), split-K weight streaming (T <= 16, the
+// router is a GEMV bound by reading W_r), or split-K MFMA GEMM (larger T).
+// The logits land as nsplit fp32 partials that the top-k kernel adds.
+// ---------------------------------------------------------------------------
+struct RoutePlan {
+  bool stream;
+  int nsplit;
+};
+
+RoutePlan route_plan(const moe_problem* p) {
+  if (p->act_dtype == MOE_F32) return {false, 1};
+  if (p->T <= moe::kStreamMaxRows) return {true, 1};
+  return {false, moe::router_gemm_split((int)p->T, (int)p->H, (int)p->E)};
+}
+
+// ---------------------------------------------------------------------------
 // workspace layout
 // ---------------------------------------------------------------------------
 struct StageSizes {
@@ -34,7 +50,7 @@ StageSizes stage_sizes(const moe_problem* p) {
   StageSizes s{};
   const size_t T = (size_t)p->T, E = (size_t)p->E, k = (size_t)p->k;
   const size_t R = T * k;
-  s.route = up(T * (E + 1) * 4);
+  s.route = up((size_t)route_plan(p).nsplit * T * (E + 1) * 4);
   s.dispatch = up(moe::dispatch_ws_ints(p->T, p->E) * 4);
   s.ffn = up(moe::ffn_plan_ints(p->T, p->E, p->k, p->I_shared > 0) * 4) + up(R * (size_t)p->I * act_bytes(p)) +
           up(T * (size_t)p->I_shared * act_bytes(p));
@@ -91,6 +107,12 @@ moe_status check_problem(const moe_problem* p) {
     return MOE_ERR_SHAPE;
   if (p->T > (int64_t)INT32_MAX / p->k || p->H > (1 << 24) || p->I > (1 << 24) || p->I_shared > (1 << 24))
     return MOE_ERR_SHAPE;
+  // kernels address rows with 32-bit element offsets inside one tensor
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t R = p->T * p->k;
+  if (p->T * p->H >= lim || R * p->I >= lim || R * p->H >= lim || p->T * p->I_shared >= lim || p->I * p->H >= lim ||
+      p->I_shared * p->H >= lim)
+    return MOE_ERR_UNSUPPORTED;
   const bool f32 = p->act_dtype == MOE_F32 && p->w_dtype == MOE_F32;
   const bool bf = p->act_dtype == MOE_BF16 && p->w_dtype == MOE_BF16;
   const bool fp8 = p->act_dtype == MOE_BF16 && p->w_dtype == MOE_FP8_E4M3FN;
@@ -98,8 +120,10 @@ moe_status check_problem(const moe_problem* p) {
   const int64_t q = f32 ? 4 : 8;  // 16-byte vectors along every K-contiguous row
   if (p->H % q || p->I % q || p->I_shared % q) return MOE_ERR_UNSUPPORTED;
   if (fp8 && (p->scale_block != 128 || p->H % 128 || p->I % 128)) return MOE_ERR_UNSUPPORTED;
-  if (p->flags & ~(uint32_t)(MOE_FLAG_FORCE_GEMM | MOE_FLAG_FORCE_STREAM)) return MOE_ERR_UNSUPPORTED;
+  const uint32_t known = MOE_FLAG_FORCE_GEMM | MOE_FLAG_FORCE_STREAM | MOE_FLAG_GEMM_TILE_128 | MOE_FLAG_GEMM_TILE_256;
+  if (p->flags & ~known) return MOE_ERR_UNSUPPORTED;
   if ((p->flags & MOE_FLAG_FORCE_GEMM) && (p->flags & MOE_FLAG_FORCE_STREAM)) return MOE_ERR_UNSUPPORTED;
+  if ((p->flags & MOE_FLAG_GEMM_TILE_128) && (p->flags & MOE_FLAG_GEMM_TILE_256)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -145,15 +169,19 @@ moe_status do_route(const moe_problem* p, const void* x, const void* w_router, c
                     int32_t* ids, float* w, float* sl, void* stage, hipStream_t s) {
   const int T = (int)p->T, H = (int)p->H, E = (int)p->E, k = (int)p->k;
   const void* wsg = (sh_gate_w && sl) ? sh_gate_w : nullptr;
-  float* logits = static_cast<float*>(stage);
+  float* partial = static_cast<float*>(stage);
+  const RoutePlan rp = route_plan(p);
   hipError_t e;
   if (p->act_dtype == MOE_F32)
     e = moe::launch_router_logits_f32(static_cast<const float*>(x), static_cast<const float*>(w_router),
-                                      static_cast<const float*>(wsg), logits, T, H, E, s);
+                                      static_cast<const float*>(wsg), partial, T, H, E, s);
+  else if (rp.stream)
+    e = moe::launch_router_stream(x, w_router, wsg, partial, T, H, E, s);
   else
-    e = moe::launch_router_logits_bf16(x, w_router, wsg, logits, T, H, E, s);
+    e = moe::launch_router_logits_bf16(x, w_router, wsg, partial, T, H, E, rp.nsplit, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(moe::launch_topk(logits, E + (wsg ? 1 : 0), T, E, k, wsg ? 1 : 0, ids, w, sl, s));
+  return hip_status(
+      moe::launch_topk(partial, rp.nsplit, E + (wsg ? 1 : 0), T, E, k, wsg ? 1 : 0, ids, w, sl, s));
 }
 
 FfnArgs ffn_args(const moe_problem* p, const moe_weights* w, const void* x, const int32_t* offsets,
@@ -184,20 +212,37 @@ FfnArgs ffn_args(const moe_problem* p, const moe_weights* w, const void* x, cons
   return a;
 }
 
+// Tile height of the MFMA GEMM path: 256-row tiles pay off once experts hold
+// hundreds of rows; the caller can pin either kernel for A/B runs.
+bool use_big_tiles(const moe_problem* p, const FfnArgs& a) {
+  if (!moe::ffn_big_supported(a)) return false;
+  if (p->flags & MOE_FLAG_GEMM_TILE_128) return false;
+  if (p->flags & MOE_FLAG_GEMM_TILE_256) return true;
+  return p->T * p->k >= 256 * p->E;  // average rows per expert >= 256
+}
+
 // phases: bit 0 gate/up, bit 1 down.  The plan kernel runs first (bf16/fp8).
 moe_status run_ffn(const moe_problem* p, FfnArgs& a, int phases, void* plan_ws, hipStream_t s) {
   if (p->act_dtype == MOE_F32) return hip_status(moe::launch_ffn_f32(a, phases, s));
   int32_t* plan = static_cast<int32_t*>(plan_ws);
-  if (moe::launch_ffn_plan(a.offsets, a.T, a.E, a.k, a.Is > 0 ? 1 : 0, p->flags, plan, s) != hipSuccess)
+  const bool big = use_big_tiles(p, a);
+  if (moe::launch_ffn_plan(a.offsets, a.sorted, a.T, a.E, a.k, a.Is > 0 ? 1 : 0, p->flags,
+                           big ? moe::kGemmBigBM : moe::kGemmBM, plan, s) != hipSuccess)
     return MOE_ERR_HIP;
   moe::ffn_bind_plan(a, plan);
-  if (phases & 1) {
-    if (moe::launch_ffn_gemm(a, 1, s) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_ffn_stream(a, 1, s) != hipSuccess) return MOE_ERR_HIP;
-  }
-  if (phases & 2) {
-    if (moe::launch_ffn_gemm(a, 2, s) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_ffn_stream(a, 2, s) != hipSuccess) return MOE_ERR_HIP;
+  // A group holds at most T rows, so with T <= kStreamMaxRows no group can
+  // reach the GEMM path unless it is forced; with the GEMM path forced no
+  // group streams.  Launches that cannot have work are skipped.
+  const bool any_gemm = (p->flags & MOE_FLAG_FORCE_GEMM) ||
+                        (!(p->flags & MOE_FLAG_FORCE_STREAM) && p->T > moe::kStreamMaxRows);
+  const bool any_stream = !(p->flags & MOE_FLAG_FORCE_GEMM);
+  for (int phase = 1; phase <= 2; ++phase) {
+    if (!(phases & phase)) continue;
+    if (any_gemm) {
+      const hipError_t e = big ? moe::launch_ffn_gemm_big(a, phase, s) : moe::launch_ffn_gemm(a, phase, s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    if (any_stream && moe::launch_ffn_stream(a, phase, s) != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;
 }

@@ -4,13 +4,14 @@
 //
 //  1. count  : one workgroup per chunk of 32 tokens; per-expert counts of
 //              the chunk in LDS (LDS atomics only count, order comes later).
-//  2. scan   : one 1024-thread workgroup; for every expert an exclusive scan
-//              over chunks, then a workgroup scan of the per-expert totals
-//              gives expert_offsets; chunk bases = offset + prefix.
-//  3. scatter: one wave per chunk walks its tokens in order; the k lanes of
-//              a token hit k distinct experts, so each lane bumps its expert's
-//              LDS cursor without conflict, and positions come out ascending
-//              in a within every expert (stable).
+//  2. scan   : per expert, an exclusive scan of its chunk counts over the
+//              chunks (64 experts per workgroup, chunks split over 16 waves)
+//              and the expert's total.
+//  3. scatter: one wave per chunk scans the E totals into expert_offsets,
+//              then walks its tokens in order; the k lanes of a token hit k
+//              distinct experts, so each lane bumps its expert's LDS cursor
+//              without conflict, and positions come out ascending in a
+//              within every expert (stable).
 // Expert ids outside [0, E) are clamped into range so the result is always a
 // permutation (memory-safe); ids repeated within a token give an
 // unspecified (still in-range) order.
@@ -38,56 +39,80 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
   for (int e = threadIdx.x; e < E; e += blockDim.x) chunk_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
-__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ chunk_counts, int nch, int E, int R,
-                                                    int32_t* __restrict__ offsets) {
-  __shared__ int wsum[16];
-  const int tid = threadIdx.x;
-  // per-expert exclusive scan over chunks (E <= 1024: one expert per thread)
-  int run = 0;
-  if (tid < E) {
-    for (int c = 0; c < nch; ++c) {
-      int32_t* p = chunk_counts + (int64_t)c * E + tid;
-      const int v = *p;
-      *p = run;
-      run += v;
+// Per expert, exclusive prefix of its chunk counts over chunks, in place, and
+// the expert's total.  Block = 16 waves covering 64 experts (lane = expert);
+// wave w owns a contiguous run of chunks, loads it with independent loads,
+// then the 16 wave partials are scanned through LDS.
+__global__ __launch_bounds__(1024) void chunk_scan_kernel(int32_t* __restrict__ chunk_counts, int nch, int E,
+                                                          int32_t* __restrict__ totals) {
+  __shared__ int part[16][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  const int cpw = (nch + 15) / 16;
+  const int c0 = w * cpw;
+  const int c1 = c0 + cpw < nch ? c0 + cpw : nch;
+  int sum = 0;
+  if (e < E) {
+    for (int c = c0; c < c1; c += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = c + i < c1 ? chunk_counts[(int64_t)(c + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sum += v[i];
     }
   }
-  // workgroup exclusive scan of totals
-  const int lane = tid & 63, w = tid >> 6;
-  int s = run;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(s, o, 64);
-    if (lane >= o) s += t;
-  }
-  if (lane == 63) wsum[w] = s;
+  part[w][lane] = sum;
   __syncthreads();
-  if (w == 0) {
-    const int t = lane < 16 ? wsum[lane] : 0;
-    int u = t;
+  int pre = 0;
+  for (int i = 0; i < w; ++i) pre += part[i][lane];
+  if (e < E) {
+    if (w == 15) totals[e] = pre + sum;
+    int run = pre;
+    for (int c = c0; c < c1; c += 8) {
+      int v[8];
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int q = __shfl_up(u, o, 64);
-      if (lane >= o) u += q;
+      for (int i = 0; i < 8; ++i) v[i] = c + i < c1 ? chunk_counts[(int64_t)(c + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (c + i < c1) chunk_counts[(int64_t)(c + i) * E + e] = run;
+        run += v[i];
+      }
     }
-    if (lane < 16) wsum[lane] = u - t;
-  }
-  __syncthreads();
-  const int excl = s - run + wsum[w];
-  if (tid < E) offsets[tid] = excl;
-  if (tid == 0) offsets[E] = R;
-  __syncthreads();
-  if (tid < E) {
-    for (int c = 0; c < nch; ++c) chunk_counts[(int64_t)c * E + tid] += excl;
   }
 }
 
+// One wave per chunk.  The wave first turns the per-expert totals into
+// expert offsets (every block redoes this small scan; block 0 publishes
+// them), then walks its tokens in order: the k lanes of a token hit k
+// distinct experts, so each bumps its expert's LDS cursor without conflict.
 __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
-                                                     const int32_t* __restrict__ chunk_base,
-                                                     int32_t* __restrict__ sorted, int32_t* __restrict__ pos) {
+                                                     const int32_t* __restrict__ chunk_prefix,
+                                                     const int32_t* __restrict__ totals,
+                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
+                                                     int32_t* __restrict__ pos) {
   extern __shared__ int cur[];
   const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) cur[e] = chunk_base[(int64_t)blockIdx.x * E + e];
+  // lane owns experts [lane*per, lane*per + per)
+  const int per = (E + 63) / 64;
+  const int e0 = lane * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i) local += e0 + i < E ? totals[e0 + i] : 0;
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  int run = incl - local;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      if (blockIdx.x == 0) offsets[e] = run;
+      cur[e] = run + chunk_prefix[(int64_t)blockIdx.x * E + e];
+      run += totals[e];
+    }
+  }
+  if (blockIdx.x == 0 && lane == 63) offsets[E] = incl;
   __syncthreads();
   const int t0 = blockIdx.x * CH;
   const int t1 = t0 + CH < T ? t0 + CH : T;
@@ -104,16 +129,78 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
   }
 }
 
+// Whole dispatch of a batch of at most CH tokens in one 1024-thread
+// workgroup (decode): LDS counts, workgroup scan into expert_offsets, then
+// wave 0 walks the tokens in order as in scatter_kernel.
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ sorted, int32_t* __restrict__ pos) {
+  __shared__ int cur[1024];
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x;
+  cur[tid] = 0;
+  __syncthreads();
+  const int R = T * k;
+  for (int a = tid; a < R; a += blockDim.x) atomicAdd(&cur[clamp_e(ids[a], E)], 1);
+  __syncthreads();
+  const int v = tid < E ? cur[tid] : 0;
+  const int lane = tid & 63, w = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  if (w == 0) {
+    const int t = lane < 16 ? wsum[lane] : 0;
+    int u = t;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int q = __shfl_up(u, o, 64);
+      if (lane >= o) u += q;
+    }
+    if (lane < 16) wsum[lane] = u - t;
+  }
+  __syncthreads();
+  const int excl = incl - v + wsum[w];
+  if (tid < E) {
+    offsets[tid] = excl;
+    cur[tid] = excl;
+  }
+  if (tid == 0) offsets[E] = R;
+  __syncthreads();
+  if (w == 0) {
+    for (int t = 0; t < T; ++t) {
+      if (lane < k) {
+        const int a = t * k + lane;
+        const int e = clamp_e(ids[a], E);
+        const int p = cur[e];
+        cur[e] = p + 1;
+        sorted[p] = a;
+        pos[a] = p;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
 }  // namespace
 
-size_t dispatch_ws_ints(int64_t T, int64_t E) { return (size_t)((T + CH - 1) / CH) * (size_t)E; }
+size_t dispatch_ws_ints(int64_t T, int64_t E) { return (size_t)((T + CH - 1) / CH) * (size_t)E + (size_t)E; }
 
 hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* offsets, int32_t* sorted,
                            int32_t* pos, int32_t* ws, hipStream_t s) {
+  if (T <= CH) {
+    dispatch_small_kernel<<<1, 1024, 0, s>>>(ids, T, E, k, offsets, sorted, pos);
+    return hipGetLastError();
+  }
   const int nch = (T + CH - 1) / CH;
+  int32_t* totals = ws + (size_t)nch * E;
   count_kernel<<<nch, 256, E * sizeof(int), s>>>(ids, T, E, k, ws);
-  scan_kernel<<<1, 1024, 0, s>>>(ws, nch, E, T * k, offsets);
-  scatter_kernel<<<nch, 64, E * sizeof(int), s>>>(ids, T, E, k, ws, sorted, pos);
+  chunk_scan_kernel<<<(E + 63) / 64, 1024, 0, s>>>(ws, nch, E, totals);
+  scatter_kernel<<<nch, 64, E * sizeof(int), s>>>(ids, T, E, k, ws, totals, offsets, sorted, pos);
   return hipGetLastError();
 }
 

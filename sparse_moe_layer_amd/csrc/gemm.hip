@@ -34,12 +34,17 @@ struct RouterArgs {
   const bf16* x;
   const bf16* wr;
   const bf16* wsg;  // may be null
-  float* logits;    // [T, N]
+  float* logits;    // [nsplit][T, N] partial logits (K split into nsplit chunks)
   int T, H, E, N;
+  int nsplit, kchunk;
 };
 
-// Element offset of the 16-byte chunk `c` of tile row `r` (XOR swizzle).
-__device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ (r & 7)) << 3); }
+// Element offset of the 16-byte chunk `c` of tile row `r`.  Rows are 128 B;
+// gfx950 serves a 16-byte-per-lane LDS read 16 lanes at a time over 64 banks
+// (256 B), i.e. two rows per bank sweep, so the chunk is XOR-ed with
+// (r >> 1) & 7: the 16 rows a half-wave reads land on 16 distinct 16-byte
+// bank groups.
+__device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ ((r >> 1) & 7)) << 3); }
 
 template <int MODE, bool FP8>
 __global__ __launch_bounds__(NT, 2) void gemm_kernel(FfnArgs f, RouterArgs ra, int n_tiles_n,
@@ -60,18 +65,23 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(FfnArgs f, RouterArgs ra, i
     mt_begin = list_begin_idx < 0 ? 0 : f.plan[list_begin_idx];
     mt_end = f.plan[list_end_idx];
   }
-  const int total = (mt_end - mt_begin) * n_tiles_n;
+  const int nsplit = MODE == M_ROUTER ? ra.nsplit : 1;
+  const int total = (mt_end - mt_begin) * n_tiles_n * nsplit;
 
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int mt = mt_begin + tile / n_tiles_n;
-    const int nt = tile % n_tiles_n;
+    const int mt = mt_begin + tile / (n_tiles_n * nsplit);
+    const int rem = tile % (n_tiles_n * nsplit);
+    const int nt = rem % n_tiles_n;
+    const int kc = rem / n_tiles_n;  // K chunk (router split-K)
 
     // ---------------- resolve the group of this m-tile ----------------
     int g = 0, base = 0, r0, nrows, K, Ncols;
+    int kbeg = 0;
     if (MODE == M_ROUTER) {
       r0 = mt * BM;
       nrows = ra.T - r0;
-      K = ra.H;
+      kbeg = kc * ra.kchunk;
+      K = kbeg + ra.kchunk < ra.H ? kbeg + ra.kchunk : ra.H;  // end of this K chunk
       Ncols = ra.N;
     } else {
       g = f.mt_group[mt];
@@ -178,14 +188,14 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(FfnArgs f, RouterArgs ra, i
 
     u32x4 ra_reg[4], rb_reg[4];
     float rs_reg[2];
-    const int kc = tid & 7;
-    const int nk = (K + BK - 1) / BK;
+    const int kcol = tid & 7;
+    const int nk = (K - kbeg + BK - 1) / BK;
 
     auto gload = [&](int kt) {
-      const int k0 = kt * BK;
+      const int k0 = kbeg + kt * BK;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int kk = k0 + kc * 8;
+        const int kk = k0 + kcol * 8;
         ra_reg[i] = kk < K ? ld16(a_ptr[i] + kk) : u32x4{0, 0, 0, 0};
       }
       if (fp8_tile) {
@@ -198,7 +208,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(FfnArgs f, RouterArgs ra, i
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int kk = k0 + kc * 8;
+          const int kk = k0 + kcol * 8;
           rb_reg[i] = kk < K ? ld16(reinterpret_cast<const bf16*>(b_ptr[i]) + kk) : u32x4{0, 0, 0, 0};
         }
       }
@@ -209,7 +219,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(FfnArgs f, RouterArgs ra, i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = (tid >> 3) + 32 * i;
-        *reinterpret_cast<u32x4*>(a + lds_off(r, kc)) = ra_reg[i];
+        *reinterpret_cast<u32x4*>(a + lds_off(r, kcol)) = ra_reg[i];
       }
       if (fp8_tile) {
 #pragma unroll
@@ -225,7 +235,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(FfnArgs f, RouterArgs ra, i
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = (tid >> 3) + 32 * i;
-          *reinterpret_cast<u32x4*>(b + lds_off(r, kc)) = rb_reg[i];
+          *reinterpret_cast<u32x4*>(b + lds_off(r, kcol)) = rb_reg[i];
         }
       }
     };
@@ -285,7 +295,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(FfnArgs f, RouterArgs ra, i
             const int col = nt * BN + wn * 64 + j * 32 + (lane & 31);
             if (col >= Ncols) continue;
             if (MODE == M_ROUTER) {
-              ra.logits[gr * ra.N + col] = acc[i][j][v];
+              ra.logits[((int64_t)kc * ra.T + gr) * ra.N + col] = acc[i][j][v];
             } else {
               bf16* dst = shared ? reinterpret_cast<bf16*>(f.y_sh) : reinterpret_cast<bf16*>(f.y);
               dst[gr * f.H + col] = f2bf(acc[i][j][v]);
@@ -304,7 +314,8 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(FfnArgs f, RouterArgs ra, i
 //   [0] gemm m-tiles total        [1] stream m-blocks total
 //   [2] gemm m-tiles of routed groups (shared group's tiles follow)
 //   [3] stream m-blocks of routed groups
-//   [4..]  mt_group[max_mt], mt_row0[max_mt], sb_group[max_sb], sb_row0[max_sb]
+//   [4..]  mt_group[max_mt], mt_row0[max_mt], sb_group[max_sb], sb_row0[max_sb],
+//          sb_base[max_sb], sb_nrows[max_sb], sb_tok[max_sb][kStreamBM]
 // ---------------------------------------------------------------------------
 __device__ int block_excl_scan(int v, int* tmp, int* total) {
   // blockDim.x == 1024 (16 waves)
@@ -334,14 +345,18 @@ __device__ int block_excl_scan(int v, int* tmp, int* total) {
   return r;
 }
 
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* offsets, int T, int E, int has_shared,
-                                                    uint32_t flags, int32_t* plan, int max_mt, int max_sb) {
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* offsets, const int32_t* sorted, int T, int E,
+                                                    int k, int has_shared, uint32_t flags, int bm, int32_t* plan,
+                                                    int max_mt, int max_sb) {
   __shared__ int tmp[32];
   __shared__ int tot;
   int32_t* mt_group = plan + 4;
   int32_t* mt_row0 = mt_group + max_mt;
   int32_t* sb_group = mt_row0 + max_mt;
   int32_t* sb_row0 = sb_group + max_sb;
+  int32_t* sb_base = sb_row0 + max_sb;
+  int32_t* sb_nrows = sb_base + max_sb;
+  int32_t* sb_tok = sb_nrows + max_sb;
   const int G = E + (has_shared ? 1 : 0);
   int carry_mt = 0, carry_sb = 0;
   for (int g0 = 0; g0 < G; g0 += 1024) {
@@ -355,7 +370,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* offsets, int 
       else if (flags & 2u) gemm = false;      // force streaming
       else gemm = n > kStreamMaxRows;
     }
-    const int cm = gemm ? (n + kGemmBM - 1) / kGemmBM : 0;
+    const int cm = gemm ? (n + bm - 1) / bm : 0;
     const int cs = (n > 0 && !gemm) ? (n + kStreamBM - 1) / kStreamBM : 0;
     // routed groups first in each list, the shared group (g == E) last: since
     // g ascends with the scan order, this holds automatically.
@@ -363,8 +378,24 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* offsets, int 
     const int tm = tot;
     const int os = block_excl_scan(cs, tmp, &tot) + carry_sb;
     const int ts = tot;
-    for (int i = 0; i < cm; ++i) { mt_group[om + i] = g; mt_row0[om + i] = i * kGemmBM; }
-    for (int i = 0; i < cs; ++i) { sb_group[os + i] = g; sb_row0[os + i] = i * kStreamBM; }
+    for (int i = 0; i < cm; ++i) { mt_group[om + i] = g; mt_row0[om + i] = i * bm; }
+    const int gbase = g < E ? offsets[g] : 0;
+    for (int i = 0; i < cs; ++i) {
+      const int sb = os + i, r0 = i * kStreamBM;
+      const int nr = n - r0 < kStreamBM ? n - r0 : kStreamBM;
+      sb_group[sb] = g;
+      sb_row0[sb] = r0;
+      sb_base[sb] = gbase;
+      sb_nrows[sb] = nr;
+      for (int m = 0; m < kStreamBM; ++m) {
+        int tok = 0;
+        if (m < nr) {  // sorted is null for the down phase alone, which needs no tokens
+          tok = g < E ? (sorted ? sorted[gbase + r0 + m] / k : 0) : r0 + m;
+          tok = tok < T ? tok : T - 1;
+        }
+        sb_tok[sb * kStreamBM + m] = tok;
+      }
+    }
     if (has_shared && g == E) {
       plan[2] = om;  // routed gemm tiles precede the shared group's
       plan[3] = os;
@@ -400,7 +431,7 @@ int num_cus() {
 }  // namespace
 
 size_t ffn_plan_ints(int64_t T, int64_t E, int64_t k, bool shared) {
-  return 4 + 2 * (size_t)max_mtiles(T, E, k, shared) + 2 * (size_t)max_sblocks(T, E, k, shared);
+  return 4 + 2 * (size_t)max_mtiles(T, E, k, shared) + (4 + kStreamBM) * (size_t)max_sblocks(T, E, k, shared);
 }
 
 void ffn_bind_plan(FfnArgs& a, int32_t* plan) {
@@ -411,21 +442,38 @@ void ffn_bind_plan(FfnArgs& a, int32_t* plan) {
   a.mt_row0 = a.mt_group + mm;
   a.sb_group = a.mt_row0 + mm;
   a.sb_row0 = a.sb_group + ms;
+  a.sb_base = a.sb_row0 + ms;
+  a.sb_nrows = a.sb_base + ms;
+  a.sb_tok = a.sb_nrows + ms;
 }
 
-hipError_t launch_ffn_plan(const int32_t* offsets, int T, int E, int k, int has_shared, uint32_t flags,
-                           int32_t* plan, hipStream_t s) {
+hipError_t launch_ffn_plan(const int32_t* offsets, const int32_t* sorted, int T, int E, int k, int has_shared,
+                           uint32_t flags, int bm, int32_t* plan, hipStream_t s) {
+  // list capacity is sized for the smallest tile height (kGemmBM <= bm)
   const int mm = max_mtiles(T, E, k, has_shared), ms = max_sblocks(T, E, k, has_shared);
-  plan_kernel<<<1, 1024, 0, s>>>(offsets, T, E, has_shared, flags, plan, mm, ms);
+  plan_kernel<<<1, 1024, 0, s>>>(offsets, sorted, T, E, k, has_shared, flags, bm, plan, mm, ms);
   return hipGetLastError();
 }
 
+int router_gemm_split(int T, int H, int E) {
+  // enough (m, n, K-chunk) tiles to cover the chip; chunks of whole 64-wide K steps
+  const int tiles = ((T + BM - 1) / BM) * ((E + 1 + BN - 1) / BN);
+  int ns = (2 * num_cus() + tiles - 1) / tiles;
+  const int maxs = H / (4 * BK) > 0 ? H / (4 * BK) : 1;
+  ns = ns < 1 ? 1 : (ns > maxs ? maxs : ns);
+  int kchunk = (H + ns - 1) / ns;
+  kchunk = (kchunk + BK - 1) / BK * BK;
+  return (H + kchunk - 1) / kchunk;
+}
+
 hipError_t launch_router_logits_bf16(const void* x, const void* w_router, const void* w_sg, float* logits,
-                                     int T, int H, int E, hipStream_t s) {
+                                     int T, int H, int E, int nsplit, hipStream_t s) {
+  int kchunk = (H + nsplit - 1) / nsplit;
+  kchunk = (kchunk + BK - 1) / BK * BK;
   RouterArgs ra{reinterpret_cast<const bf16*>(x), reinterpret_cast<const bf16*>(w_router),
-                reinterpret_cast<const bf16*>(w_sg), logits, T, H, E, E + (w_sg ? 1 : 0)};
+                reinterpret_cast<const bf16*>(w_sg), logits, T, H, E, E + (w_sg ? 1 : 0), nsplit, kchunk};
   const int ntn = (ra.N + BN - 1) / BN;
-  const int tiles = ((T + BM - 1) / BM) * ntn;
+  const int tiles = ((T + BM - 1) / BM) * ntn * nsplit;
   const int grid = tiles < num_cus() * 2 ? tiles : num_cus() * 2;
   FfnArgs none{};
   gemm_kernel<M_ROUTER, false><<<grid, NT, 0, s>>>(none, ra, ntn, -1, 0);

@@ -6,8 +6,10 @@
 
 namespace moe {
 
-// Rows per MFMA GEMM m-tile and per streaming m-block.
+// Rows per MFMA GEMM m-tile (LDS-tiled kernel / big-tile kernel) and per
+// streaming m-block.
 constexpr int kGemmBM = 128;
+constexpr int kGemmBigBM = 256;
 constexpr int kStreamBM = 16;
 // An expert with at most this many rows streams its weights (small-M path).
 constexpr int kStreamMaxRows = 16;
@@ -32,23 +34,35 @@ struct FfnArgs {
   const int32_t* plan;        // plan[0] = #gemm m-tiles, plan[1] = #stream m-blocks
   const int32_t* mt_group; const int32_t* mt_row0;
   const int32_t* sb_group; const int32_t* sb_row0;
+  const int32_t* sb_base;   // first dispatched row of the group (0 for the shared expert)
+  const int32_t* sb_nrows;  // rows of the m-block (<= kStreamBM)
+  const int32_t* sb_tok;    // [sb][kStreamBM] token of each row (gate/up gather)
 };
 
 size_t ffn_plan_ints(int64_t T, int64_t E, int64_t k, bool shared);
 
+// Router logits as nsplit fp32 partial sums over K chunks: partial[c][t][n],
+// n < E router rows, n == E the shared gate (when w_sg != null).  The top-k
+// kernel adds the chunks in order c = 0..nsplit-1.  The small-batch
+// streaming router writes complete logits (nsplit = 1).
+int router_gemm_split(int T, int H, int E);
 hipError_t launch_router_logits_bf16(const void* x, const void* w_router, const void* w_sg,
-                                     float* logits, int T, int H, int E, hipStream_t s);
+                                     float* partial, int T, int H, int E, int nsplit, hipStream_t s);
+hipError_t launch_router_stream(const void* x, const void* w_router, const void* w_sg, float* logits, int T,
+                                int H, int E, hipStream_t s);
 hipError_t launch_router_logits_f32(const float* x, const float* w_router, const float* w_sg,
                                     float* logits, int T, int H, int E, hipStream_t s);
-hipError_t launch_topk(const float* logits, int ldl, int T, int E, int k, int has_sg,
+hipError_t launch_topk(const float* partial, int nsplit, int ldl, int T, int E, int k, int has_sg,
                        int32_t* ids, float* w, float* shared_logit, hipStream_t s);
 size_t dispatch_ws_ints(int64_t T, int64_t E);
 hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* offsets,
                            int32_t* sorted, int32_t* pos, int32_t* ws, hipStream_t s);
-hipError_t launch_ffn_plan(const int32_t* offsets, int T, int E, int k, int has_shared, uint32_t flags,
-                           int32_t* plan_ws, hipStream_t s);
+hipError_t launch_ffn_plan(const int32_t* offsets, const int32_t* sorted, int T, int E, int k, int has_shared,
+                           uint32_t flags, int bm, int32_t* plan_ws, hipStream_t s);
 void ffn_bind_plan(FfnArgs& a, int32_t* plan_ws);
 hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s);    // phase 1 gate/up, 2 down
+bool ffn_big_supported(const FfnArgs& a);
+hipError_t launch_ffn_gemm_big(const FfnArgs& a, int phase, hipStream_t s);
 hipError_t launch_ffn_stream(const FfnArgs& a, int phase, hipStream_t s);  // phase 1 gate/up, 2 down
 hipError_t launch_ffn_f32(const FfnArgs& a, int phases, hipStream_t s);  // bit 0 gate/up, bit 1 down
 hipError_t launch_combine(const void* y, const int32_t* pos, const float* w, const void* y_sh,

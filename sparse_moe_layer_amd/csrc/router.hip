@@ -1,4 +1,5 @@
-// Router epilogue: softmax, top-k and renormalisation, one wavefront per token
+// Router epilogue: the fp32 logits (sum of K-chunk partials, chunk order
+// fixed), softmax, top-k and renormalisation, one wavefront per token
 // (Qwen3.8-Flash-Next study, MoE section: "Top 10 + normalize" in the
 // pipeline figure; "Selected router probabilities are normalized").
 //
@@ -18,18 +19,23 @@ namespace moe {
 namespace {
 
 template <int PER_LANE>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int ldl, int T, int E, int k,
-                                                   int has_sg, int32_t* __restrict__ ids, float* __restrict__ w,
-                                                   float* __restrict__ shared_logit) {
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ partial, int nsplit, int ldl, int T,
+                                                   int E, int k, int has_sg, int32_t* __restrict__ ids,
+                                                   float* __restrict__ w, float* __restrict__ shared_logit) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= T) return;  // whole wave
-  const float* row = logits + (int64_t)t * ldl;
+  // logits = sum of the K-chunk partials, chunk order fixed
+  const int64_t cstride = (int64_t)T * ldl;
+  const float* row = partial + (int64_t)t * ldl;
   float v[PER_LANE];
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? row[e] : -FLT_MAX;
+    float a = 0.f;
+    if (e < E)
+      for (int c = 0; c < nsplit; ++c) a += row[c * cstride + e];
+    v[i] = e < E ? a : -FLT_MAX;
   }
   uint32_t taken = 0;
   float sel_v = 0.f;
@@ -67,7 +73,11 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     ids[(int64_t)t * k + lane] = sel_e;
     w[(int64_t)t * k + lane] = ex / sum;
   }
-  if (has_sg && lane == 0) shared_logit[t] = row[E];
+  if (has_sg && lane == 0) {
+    float a = 0.f;
+    for (int c = 0; c < nsplit; ++c) a += row[c * cstride + E];
+    shared_logit[t] = a;
+  }
 }
 
 // fp32 logits for fp32 layers: one thread per (token, column), h ascending.
@@ -86,15 +96,17 @@ __global__ void router_f32_kernel(const float* __restrict__ x, const float* __re
 
 }  // namespace
 
-hipError_t launch_topk(const float* logits, int ldl, int T, int E, int k, int has_sg, int32_t* ids, float* w,
-                       float* shared_logit, hipStream_t s) {
+hipError_t launch_topk(const float* partial, int nsplit, int ldl, int T, int E, int k, int has_sg, int32_t* ids,
+                       float* w, float* shared_logit, hipStream_t s) {
   const int grid = (T + 3) / 4;
   const int per = (E + 63) / 64;
-  if (per <= 1) topk_kernel<1><<<grid, 256, 0, s>>>(logits, ldl, T, E, k, has_sg, ids, w, shared_logit);
-  else if (per <= 2) topk_kernel<2><<<grid, 256, 0, s>>>(logits, ldl, T, E, k, has_sg, ids, w, shared_logit);
-  else if (per <= 4) topk_kernel<4><<<grid, 256, 0, s>>>(logits, ldl, T, E, k, has_sg, ids, w, shared_logit);
-  else if (per <= 8) topk_kernel<8><<<grid, 256, 0, s>>>(logits, ldl, T, E, k, has_sg, ids, w, shared_logit);
-  else topk_kernel<16><<<grid, 256, 0, s>>>(logits, ldl, T, E, k, has_sg, ids, w, shared_logit);
+#define MOE_TOPK(P) topk_kernel<P><<<grid, 256, 0, s>>>(partial, nsplit, ldl, T, E, k, has_sg, ids, w, shared_logit)
+  if (per <= 1) MOE_TOPK(1);
+  else if (per <= 2) MOE_TOPK(2);
+  else if (per <= 4) MOE_TOPK(4);
+  else if (per <= 8) MOE_TOPK(8);
+  else MOE_TOPK(16);
+#undef MOE_TOPK
   return hipGetLastError();
 }
 

@@ -1,16 +1,23 @@
-// Weight-streaming expert FFN for groups with few rows (decode, skew tails).
+// Weight-streaming contractions for groups with few rows (decode, skew tails)
+// and the split-K router for small batches.
 //
 // When an expert holds only a handful of tokens the expert GEMMs of
 // eq. expert(x) (Qwen3.8-Flash-Next study, MoE section) are bound by reading
-// its weights once from HBM.  Here each wave owns one (16-row m-block,
-// weight slab) item and streams the slab's weight rows straight from HBM into
-// MFMA B fragments (v_mfma_f32_16x16x32_bf16: lane = weight row l%16, 8
-// consecutive K values), with no LDS staging: every weight byte is used by
-// exactly one wave.  The 16 activation rows (A fragments) come from L2.
-// Loads for 8 K-steps are issued before their MFMAs so each lane keeps
-// several 16-byte loads in flight.
+// its weights once from HBM.  Each wave owns one (16-row m-block, weight slab)
+// item and streams the slab's weight rows once from HBM (every weight byte
+// is used by exactly one wave) into v_mfma_f32_16x16x32_bf16 B fragments
+// (lane = weight row l%16, 8 consecutive K values).  HBM wants long runs per
+// row: a fragment-shaped load touches 16 rows x 64 B and runs at well under
+// half the bandwidth of 512-byte runs, so bf16 weights are loaded in 512-byte
+// runs (each 16-byte-per-lane load covers 2 rows x 512 B), one batch of 256 K
+// values ahead in registers, and re-laid into MFMA fragments through a
+// wave-private LDS stage (no barriers).
+// fp8 codes stream through registers in batches of U K steps instead.  The
+// (at most 16) activation rows come from L2.
 //   gate/up item: 16 hidden columns (16 gate rows + 16 up rows), SiLU*mul in registers
-//   down item   : 64 output columns (4 blocks of 16 W_down rows)
+//   down item   : 32 output columns (2 blocks of 16 W_down rows)
+//   router item : 16 router rows (the shared-gate row last) over one K chunk,
+//                 fp32 partial logits, reduced in fixed order by the top-k kernel
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -18,24 +25,189 @@ namespace moe {
 namespace {
 
 constexpr int WAVES = 4;
-constexpr int UNROLL = 8;
+constexpr int U = 4;  // K steps per batch
 constexpr int KSTEP = 32;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Raw storage of one lane's 8 B-operand values: 16 bytes of bf16, or 8 bytes
+// of e4m3fn codes (decoded with the block scale right before the MFMA so the
+// load stays asynchronous).
+template <bool FP8>
+struct BRaw;
+template <>
+struct BRaw<false> {
+  u32x4 v;
+};
+template <>
+struct BRaw<true> {
+  u32x2 v;
+  float s;
+};
+
+// acc[j] += A[16 rows, kbeg..kend) x B_j[16 rows, kbeg..kend)^T for NB weight
+// blocks.  a_row: this lane's A row (row lane%16) or null (zero row);
+// b_row[j]: this lane's row of weight block j; s_row[j]: its fp8 scale row.
+// kq = 8*(lane/16) is the lane's K offset inside a 32-wide step.
+template <int NB, bool FP8>
+__device__ __forceinline__ void stream_dot(const bf16* a_row, const void* const* b_row, const float* const* s_row,
+                                           int kbeg, int kend, int kq, f32x4* acc) {
+  u32x4 av[2][U];
+  BRaw<FP8> bv[2][U][NB];
+  const int nsteps = (kend - kbeg + KSTEP - 1) / KSTEP;
+  auto load = [&](int buf, int s0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = kbeg + (s0 + u) * KSTEP + kq;
+      const bool in = kk < kend;
+      av[buf][u] = (in && a_row) ? ld16(a_row + kk) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if constexpr (FP8) {
+          bv[buf][u][j].v = in ? *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(b_row[j]) + kk)
+                               : u32x2{0, 0};
+          bv[buf][u][j].s = in ? s_row[j][kk / 128] : 0.f;
+        } else {
+          bv[buf][u][j].v = in ? ld16(reinterpret_cast<const bf16*>(b_row[j]) + kk) : u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+  };
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        u32x4 b;
+        if constexpr (FP8) b = fp8x8_to_bf16x8(bv[buf][u][j].v, bv[buf][u][j].s);
+        else b = bv[buf][u][j].v;
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[buf][u]), as_bf16x8(b), acc[j], 0, 0, 0);
+      }
+  };
+  load(0, 0);
+  for (int s0 = 0; s0 < nsteps; s0 += 2 * U) {
+    const bool more = s0 + U < nsteps;
+    if (more) load(1, s0 + U);
+    mma(0);
+    if (more) {
+      if (s0 + 2 * U < nsteps) load(0, s0 + 2 * U);
+      mma(1);
+    }
+  }
+}
+
+// ---- LDS-staged bf16 streaming -------------------------------------------
+// A batch holds SB = 256 K values (512 B) of NB*16 weight rows.  Rows 2i and
+// 2i+1 of the batch sit in 1 KB at i * 1040 B (1 KB + 16 B pad); odd rows
+// store 16-byte chunk c at position c ^ 8.  A half-wave reading 16 rows of
+// one chunk then hits 16 different 16-byte bank groups of the 64-bank LDS.
+constexpr int SB = 256;
+constexpr int PAIR = 1040;
+
+// acc[j] += A[16 rows, kbeg..kend) x W_j[16 rows, kbeg..kend)^T.  a_row: this
+// lane's activation row (row lane%16) or null (zero row); wrow0[j]: row 0 of
+// weight block j (rows ldw elements apart), of which nvalid[j] rows exist
+// (rows past them re-read the last one; their outputs are never stored);
+// lds: this wave's NB*8*PAIR-byte stage buffer.
+// Per batch each lane loads 16 B of weights per row pair (lanes 0-31 the even
+// row, 32-63 the odd row: 512 contiguous bytes per row and instruction) into
+// registers one batch ahead, writes them to the wave's LDS stage, and reads
+// MFMA fragments back.  The steady-state loop is branch-free; every load is
+// unconditional (clamped addresses, values zeroed after loading).
+template <int NB>
+__device__ __forceinline__ void stream_dot_lds(const bf16* a_row, const bf16* a_any, const bf16* const* wrow0,
+                                               const int* nvalid, int ldw, int kbeg, int kend, int lane, char* lds,
+                                               f32x4* acc) {
+  constexpr int NL = NB * 8;      // weight loads per batch
+  constexpr int NA = SB / KSTEP;  // activation loads per batch
+  const int kq = (lane >> 4) * 8;
+  const int h = lane >> 5;        // row of the pair this lane loads
+  const int c = lane & 31;        // its 16-byte chunk of the 512-byte run
+  const int nbatch = (kend - kbeg + SB - 1) / SB;
+  const bf16* arow = a_row ? a_row : a_any;
+  u32x4 wb[NL];     // weights of the batch in flight
+  u32x4 av[2][NA];  // activations, double-buffered
+  auto load_w = [&](int b) {
+    int k = kbeg + b * SB + c * 8;
+    k = k < kend ? k : kend - 8;  // past the end: any in-row chunk (its A is zero)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 2 * i + h < nvalid[j] ? 2 * i + h : nvalid[j] - 1;
+        wb[j * 8 + i] = ld16(wrow0[j] + (uint32_t)(r * ldw + k));
+      }
+  };
+  auto load_a = [&](int x, int b) {
+#pragma unroll
+    for (int s = 0; s < NA; ++s) {
+      const int kk = kbeg + b * SB + s * KSTEP + kq;
+      av[x][s] = ld16(arow + (kk < kend ? kk : kend - 8));
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int q = 0; q < NL; ++q)
+      *reinterpret_cast<u32x4*>(lds + q * PAIR + h * 512 + ((c ^ (h << 3)) << 4)) = wb[q];
+  };
+  auto compute = [&](int x, int b) {
+#pragma unroll
+    for (int s = 0; s < NA; ++s) {
+      const int kk = kbeg + b * SB + s * KSTEP + kq;
+      const u32x4 am = (a_row && kk < kend) ? av[x][s] : u32x4{0, 0, 0, 0};
+      const int cc = s * 4 + (lane >> 4);
+      const int n = lane & 15;
+      const int hn = n & 1;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const u32x4 bv = *reinterpret_cast<const u32x4*>(lds + (j * 8 + (n >> 1)) * PAIR + hn * 512 +
+                                                         ((cc ^ (hn << 3)) << 4));
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(am), as_bf16x8(bv), acc[j], 0, 0, 0);
+      }
+    }
+  };
+  // batch b: stage its weights (loaded during the previous batch), start
+  // batch b+1's loads, run batch b's MFMAs from LDS
+  load_w(0);
+  load_a(0, 0);
+  int b = 0;
+  for (; b + 2 < nbatch; b += 2) {
+    stage();
+    load_w(b + 1);
+    load_a(1, b + 1);
+    compute(0, b);
+    stage();
+    load_w(b + 2);
+    load_a(0, b + 2);
+    compute(1, b + 1);
+  }
+  stage();
+  if (b + 1 < nbatch) {
+    load_w(b + 1);
+    load_a(1, b + 1);
+    compute(0, b);
+    stage();
+    compute(1, b + 1);
+  } else {
+    compute(0, b);
+  }
+}
+
 template <int PHASE, bool FP8>
 __global__ __launch_bounds__(WAVES * 64) void stream_kernel(FfnArgs f, int list_begin_idx, int list_end_idx) {
-  constexpr int NB = PHASE == 1 ? 2 : 4;  // 16-column B blocks per item (gate+up, or 4 down blocks)
+  constexpr int NB = 2;  // gate+up, or 2 down blocks
+  __shared__ __attribute__((aligned(16))) char stage[FP8 ? 16 : WAVES * NB * 8 * PAIR];
   const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int gw = blockIdx.x * WAVES + (threadIdx.x >> 6);
   const int nw = gridDim.x * WAVES;
   const int sb_begin = list_begin_idx < 0 ? 0 : f.plan[list_begin_idx];
   const int sb_end = f.plan[list_end_idx];
   const int wide = PHASE == 1 ? (f.I > f.Is ? f.I : f.Is) : f.H;
-  const int cols_per_item = PHASE == 1 ? 16 : 64;
+  const int cols_per_item = PHASE == 1 ? 16 : 32;
   const int n_slabs = (wide + cols_per_item - 1) / cols_per_item;
   const int total = (sb_end - sb_begin) * n_slabs;
-  const int m = lane & 15;       // A row / B column within a 16-block
+  const int m = lane & 15;         // A row / B column within a 16-block
   const int kq = (lane >> 4) * 8;  // K offset of this lane inside a 32-wide K step
 
   for (int item = gw; item < total; item += nw) {
@@ -43,15 +215,9 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(FfnArgs f, int list_
     const int slab = item % n_slabs;
     const int g = f.sb_group[sb];
     const int r0 = f.sb_row0[sb];
+    const int base = f.sb_base[sb];
+    const int nrows = f.sb_nrows[sb];
     const bool shared = g >= f.E;
-    int base = 0, nrows;
-    if (!shared) {
-      base = f.offsets[g];
-      nrows = f.offsets[g + 1] - base - r0;
-    } else {
-      nrows = f.T - r0;
-    }
-    nrows = nrows < 16 ? nrows : 16;
     const int K = PHASE == 1 ? f.H : (shared ? f.Is : f.I);
     const int Ncols = PHASE == 1 ? (shared ? f.Is : f.I) : f.H;
     const int c0 = slab * cols_per_item;
@@ -63,9 +229,7 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(FfnArgs f, int list_
     if (m < nrows) {
       const int gr = base + r0 + m;
       if (PHASE == 1) {
-        int tok = shared ? gr : f.sorted[gr] / f.k;
-        tok = tok < f.T ? tok : f.T - 1;
-        a_row = reinterpret_cast<const bf16*>(f.x) + (int64_t)tok * f.H;
+        a_row = reinterpret_cast<const bf16*>(f.x) + (int64_t)f.sb_tok[sb * kStreamBM + m] * f.H;
       } else {
         a_row = shared ? reinterpret_cast<const bf16*>(f.h_sh) + (int64_t)gr * f.Is
                        : reinterpret_cast<const bf16*>(f.h) + (int64_t)gr * f.I;
@@ -108,33 +272,32 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(FfnArgs f, int list_
     f32x4 acc[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int nsteps = (K + KSTEP - 1) / KSTEP;
-    for (int s0 = 0; s0 < nsteps; s0 += UNROLL) {
-      u32x4 av[UNROLL];
-      u32x4 bv[UNROLL][NB];
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const int kk = (s0 + u) * KSTEP + kq;
-        const bool in = kk < K;
-        av[u] = (in && a_row) ? ld16(a_row + kk) : u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          if (!in) {
-            bv[u][j] = u32x4{0, 0, 0, 0};
-          } else if (fp8) {
-            const u32x2 c = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(b_row[j]) + kk);
-            bv[u][j] = fp8x8_to_bf16x8(c, s_row[j][kk / 128]);
-          } else {
-            bv[u][j] = ld16(reinterpret_cast<const bf16*>(b_row[j]) + kk);
-          }
-        }
+    if constexpr (FP8) {
+      if (fp8) {
+        stream_dot<NB, true>(a_row, b_row, s_row, 0, K, kq, acc);
+      } else {
+        stream_dot<NB, false>(a_row, b_row, s_row, 0, K, kq, acc);
       }
+    } else {
+      // first row and valid-row count of each 16-row weight block
+      const bf16* w0[NB];
+      int nv[NB];
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u]), as_bf16x8(bv[u][j]), acc[j], 0, 0, 0);
+      for (int j = 0; j < NB; ++j) {
+        int first = PHASE == 1 ? c0 : c0 + j * 16;
+        first = first < Ncols ? first : Ncols - 1;
+        nv[j] = Ncols - first;
+        const bf16* mat;
+        if (PHASE == 1) {
+          mat = shared ? reinterpret_cast<const bf16*>(j ? f.shu : f.shg)
+                       : reinterpret_cast<const bf16*>(j ? f.wu : f.wg) + (int64_t)g * (j ? f.su : f.sg);
+        } else {
+          mat = shared ? reinterpret_cast<const bf16*>(f.shd) : reinterpret_cast<const bf16*>(f.wd) + (int64_t)g * f.sd;
+        }
+        w0[j] = mat + (int64_t)first * K;
+      }
+      const bf16* a_any = reinterpret_cast<const bf16*>(PHASE == 1 ? f.x : (shared ? f.h_sh : f.h));
+      stream_dot_lds<NB>(a_row, a_any, w0, nv, K, 0, K, lane, stage + wave * NB * 8 * PAIR, acc);
     }
 
     // C fragment: lane holds column (lane & 15), rows 4*(lane>>4) + i.
@@ -163,6 +326,48 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(FfnArgs f, int list_
   }
 }
 
+// Router for T <= 16 (a GEMV bound by reading W_r): one workgroup of RW
+// waves per 16 router rows (the shared-gate row counted as row E); wave w
+// covers K chunk w, and the RW partial 16x16 blocks are added through LDS in
+// wave order, so the logits are complete and deterministic.
+constexpr int RW = 8;
+
+__global__ __launch_bounds__(RW * 64) void router_stream_kernel(const bf16* __restrict__ x,
+                                                                const bf16* __restrict__ wr,
+                                                                const bf16* __restrict__ wsg,
+                                                                float* __restrict__ logits, int T, int H, int E,
+                                                                int N, int kchunk) {
+  __shared__ f32x4 part[RW][64];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int slab = blockIdx.x;
+  const int m = lane & 15, kq = (lane >> 4) * 8;
+  const int kbeg = w * kchunk;
+  const int kend = kbeg + kchunk < H ? kbeg + kchunk : H;
+  f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+  if (kbeg < kend) {
+    const bf16* a_row = m < T ? x + (int64_t)m * H : nullptr;
+    int n = slab * 16 + m;
+    n = n < N ? n : N - 1;
+    const void* b_row[1] = {n < E ? wr + (int64_t)n * H : wsg};
+    const float* s_row[1] = {nullptr};
+    stream_dot<1, false>(a_row, b_row, s_row, kbeg, kend, kq, acc);
+  }
+  part[w][lane] = acc[0];
+  __syncthreads();
+  if (w == 0) {
+    f32x4 t = part[0][lane];
+#pragma unroll
+    for (int i = 1; i < RW; ++i) t += part[i][lane];
+    const int col = slab * 16 + m;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = 4 * (lane >> 4) + i;
+      if (tok < T && col < N) logits[(int64_t)tok * N + col] = t[i];
+    }
+  }
+}
+
 int stream_grid() {
   static int g = 0;
   if (!g) {
@@ -176,6 +381,18 @@ int stream_grid() {
 }
 
 }  // namespace
+
+hipError_t launch_router_stream(const void* x, const void* w_router, const void* w_sg, float* logits, int T, int H,
+                                int E, hipStream_t s) {
+  const int N = E + (w_sg ? 1 : 0);
+  int kchunk = (H + RW - 1) / RW;
+  kchunk = (kchunk + KSTEP - 1) / KSTEP * KSTEP;
+  router_stream_kernel<<<(N + 15) / 16, RW * 64, 0, s>>>(reinterpret_cast<const bf16*>(x),
+                                                         reinterpret_cast<const bf16*>(w_router),
+                                                         reinterpret_cast<const bf16*>(w_sg), logits, T, H, E, N,
+                                                         kchunk);
+  return hipGetLastError();
+}
 
 hipError_t launch_ffn_stream(const FfnArgs& a, int phase, hipStream_t s) {
   const int grid = stream_grid();

@@ -70,8 +70,12 @@ OK = _lib.MOE_OK
     (dict(wdt="fp8", scale_block=64), _lib.MOE_ERR_UNSUPPORTED),
     (dict(wdt="fp8"), OK),
     (dict(flags=3), _lib.MOE_ERR_UNSUPPORTED),
-    (dict(flags=8), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(flags=12), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(flags=5), OK),
+    (dict(flags=10), OK),
+    (dict(flags=16), _lib.MOE_ERR_UNSUPPORTED),
     (dict(T=2 ** 31 // 4), _lib.MOE_ERR_SHAPE),
+    (dict(T=2 ** 24, H=256), _lib.MOE_ERR_UNSUPPORTED),  # T*k*H elements >= 2^31
 ])
 def test_validate(kw, status):
     base = dict(T=64, H=256, E=16, k=4, I=128, I_shared=0, act="bf16", wdt="bf16", scale_block=128, flags=0)

@@ -157,6 +157,14 @@ def test_paths_multi_tile_groups(flags):
     check(p, run_stages(p, flags))
 
 
+@pytest.mark.parametrize("tile", [lib.MOE_FLAG_GEMM_TILE_128, lib.MOE_FLAG_GEMM_TILE_256])
+def test_gemm_tile_kernels(tile):
+    # experts with several 256-row tiles plus ragged remainders (partial M-blocks)
+    cfg = CONFIGS["flash_prefill"].with_(name="tiles", T=900, H=512, E=4, k=2, I=384, I_shared=128)
+    p = gpu_problem(cfg, 12)
+    check(p, run_stages(p, lib.MOE_FLAG_FORCE_GEMM | tile))
+
+
 def test_one_expert_takes_every_token():
     # a steep per-expert bias: the rank-1 expert wins every token (k = 1)
     cfg = CONFIGS["max_prefill"].with_(name="all_to_one", T=300, H=256, E=8, k=1, I=128, I_shared=64, zipf_s=8.0)
