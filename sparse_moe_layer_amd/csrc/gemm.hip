@@ -68,7 +68,15 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(FfnArgs f, RouterArgs ra, i
   const int nsplit = MODE == M_ROUTER ? ra.nsplit : 1;
   const int total = (mt_end - mt_begin) * n_tiles_n * nsplit;
 
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+  // Workgroup i runs on XCD i % 8: deal consecutive tile indices to one XCD
+  // (n-tiles and K chunks of an m-tile vary fastest), so the gathered A rows
+  // of an m-tile are fetched into one XCD's L2 and reused from there.
+  const int G8 = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const bool remap = (gridDim.x & 7) == 0;
+  for (int it = 0;; ++it) {
+    const int tile = remap ? it * gridDim.x + xcd * G8 + slot : it * gridDim.x + blockIdx.x;
+    if (tile >= total) break;
     const int mt = mt_begin + tile / (n_tiles_n * nsplit);
     const int rem = tile % (n_tiles_n * nsplit);
     const int nt = rem % n_tiles_n;
@@ -474,7 +482,7 @@ hipError_t launch_router_logits_bf16(const void* x, const void* w_router, const 
                 reinterpret_cast<const bf16*>(w_sg), logits, T, H, E, E + (w_sg ? 1 : 0), nsplit, kchunk};
   const int ntn = (ra.N + BN - 1) / BN;
   const int tiles = ((T + BM - 1) / BM) * ntn * nsplit;
-  const int grid = tiles < num_cus() * 2 ? tiles : num_cus() * 2;
+  const int grid = tiles < num_cus() * 2 ? (tiles + 7) / 8 * 8 : num_cus() * 2;
   FfnArgs none{};
   gemm_kernel<M_ROUTER, false><<<grid, NT, 0, s>>>(none, ra, ntn, -1, 0);
   return hipGetLastError();
@@ -487,7 +495,7 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s) {
   const int wide = a.I > a.Is ? a.I : a.Is;
   const int ntn = phase == 1 ? (wide + 63) / 64 : (a.H + BN - 1) / BN;
   const int64_t tiles = (int64_t)mm * ntn;
-  const int grid = (int)(tiles < num_cus() * 2 ? tiles : num_cus() * 2);
+  const int grid = (int)(tiles < num_cus() * 2 ? (tiles + 7) / 8 * 8 : num_cus() * 2);
   RouterArgs none{};
   if (a.fp8) {
     // routed tiles [0, plan[2]) decode fp8; the shared expert stays bf16
