@@ -63,7 +63,7 @@ def copy_calibration():
 
 def kernel_source_sha():
     h = hashlib.sha256()
-    for f in ("gemm.hip", "gemm_big.hip", "stream.hip", "common.hpp"):
+    for f in ("gemm.hip", "gemm_dma.hip", "stream.hip", "common.hpp"):
         h.update(open(os.path.join(ROOT, "sparse_moe_layer_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

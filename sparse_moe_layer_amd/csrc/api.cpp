@@ -212,13 +212,17 @@ FfnArgs ffn_args(const moe_problem* p, const moe_weights* w, const void* x, cons
   return a;
 }
 
-// Tile height of the MFMA GEMM path: 256-row tiles pay off once experts hold
-// hundreds of rows; the caller can pin either kernel for A/B runs.
+// MFMA GEMM kernel of the grouped GEMM path: the pipelined direct-load
+// kernel with 256-row tiles once experts average 128 rows or more (the MFMA
+// rate bounds them), else the register-staged kernel with 128-row tiles
+// (about a hundred rows per expert: weight streaming bounds them).  The
+// 256-row kernel takes bf16 weights with H, I and I_shared multiples of 32.
+// The caller can pin either kernel for A/B runs.
 bool use_big_tiles(const moe_problem* p, const FfnArgs& a) {
-  if (!moe::ffn_big_supported(a)) return false;
+  if (!moe::ffn_dma_supported(a)) return false;
   if (p->flags & MOE_FLAG_GEMM_TILE_128) return false;
   if (p->flags & MOE_FLAG_GEMM_TILE_256) return true;
-  return p->T * p->k >= 256 * p->E;  // average rows per expert >= 256
+  return p->T * p->k >= 128 * p->E;
 }
 
 // phases: bit 0 gate/up, bit 1 down.  The plan kernel runs first (bf16/fp8).
@@ -239,7 +243,7 @@ moe_status run_ffn(const moe_problem* p, FfnArgs& a, int phases, void* plan_ws, 
   for (int phase = 1; phase <= 2; ++phase) {
     if (!(phases & phase)) continue;
     if (any_gemm) {
-      const hipError_t e = big ? moe::launch_ffn_gemm_big(a, phase, s) : moe::launch_ffn_gemm(a, phase, s);
+      const hipError_t e = big ? moe::launch_ffn_gemm_dma(a, phase, s) : moe::launch_ffn_gemm(a, phase, s);
       if (e != hipSuccess) return MOE_ERR_HIP;
     }
     if (any_stream && moe::launch_ffn_stream(a, phase, s) != hipSuccess) return MOE_ERR_HIP;

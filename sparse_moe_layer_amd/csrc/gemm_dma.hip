@@ -1,0 +1,340 @@
+// Pipelined direct-load grouped expert GEMM for groups of hundreds of rows
+// (MFMA-bound), gfx950: the gate/up and down contractions of eq. expert(x)
+// in the Qwen3.8-Flash-Next study's MoE section (SwiGLU expert; "Per-expert
+// FFN" in the pipeline figure), on v_mfma_f32_32x32x16_bf16.
+//
+// Tile 256 x 256, K step 32, 512 threads = 8 waves (two per SIMD, so one
+// wave's MFMAs cover the other's LDS waits), each wave 128 x 64 (4 x 2 blocks
+// of 32 x 32).  The kernel is a template over the tiling (tile size, wave
+// grid, stages, workgroups per CU); a wave owns M-blocks {wm, wm + WM, ...}
+// (interleaved, so a partial tile keeps every wave busy) and NJ consecutive
+// N-blocks.  For gate/up the first half of a wave's N-blocks are gate rows
+// and the second half the up rows of the same hidden columns, so SiLU(g) * u
+// is formed in registers.
+//
+// Operands move HBM/L2 -> LDS with gfx950's direct loads (global_load_lds,
+// 16 bytes per lane, no VGPR staging) into statically separate stage buffers
+// (A rows, then B rows), four stages, loads three K steps ahead; waits are
+// explicit s_waitcnt vmcnt + s_barrier.  A stage holds a 32-wide K slice,
+// [row][4 chunks of 16 B], chunk c of row r at position c ^ ((r >> 2) & 3):
+// a half-wave's 16-byte fragment reads cover 16 rows and 64 banks span four
+// 64-byte rows, so the XOR spreads them over all banks.  Each lane's direct
+// load fetches the global chunk that belongs at its LDS position, so global
+// reads stay whole 64-byte row segments.
+//
+// Work: (group, 256-row m-tile) entries from the device plan; tiles are
+// ordered in supertiles of 8 m-tiles x all n-tiles and dealt to the
+// persistent grid so that consecutive tiles land on one XCD (workgroup i runs
+// on XCD i mod 8), sharing A slices and weight slices in that XCD's L2.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int BK = 32;     // K per pipeline stage (64-byte rows)
+constexpr int SUPER = 8;   // m-tiles per supertile
+
+template <int BM_, int BN_, int WM_, int WN_, int S_, int WG_PER_CU_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_;
+  static constexpr int NW = WM * WN, NT = 64 * NW;
+  static constexpr int WAVES_PER_EU = NW * WG_PER_CU_ / 4;
+  static constexpr int WG_PER_CU = WG_PER_CU_;
+  static constexpr int MI = BM / (32 * WM);  // M-blocks per wave
+  static constexpr int NJ = BN / (32 * WN);  // N-blocks per wave
+  static constexpr int CW = NJ * 32;         // B tile rows per wave column
+  static constexpr int LA = BM / (16 * NW);  // A direct loads per lane per stage
+  static constexpr int LB = BN / (16 * NW);  // B direct loads per lane per stage
+  static constexpr int L = LA + LB;
+  static constexpr int STAGE = (BM + BN) * BK;  // elements per stage buffer
+  static_assert(MI >= 1 && NJ >= 2 && NJ % 2 == 0 && LA >= 1 && LB >= 1, "tiling");
+  static_assert(S >= 2 && S <= 6 && L * (S - 2) < 64, "pipeline depth");
+  static_assert(S * STAGE * 2 * WG_PER_CU_ <= 160 * 1024, "LDS");
+};
+using BigCfg = Cfg<256, 256, 2, 4, 4, 1>;
+
+constexpr int vmcnt_imm(int n) { return 0xF70 | (n & 15) | (((n >> 4) & 3) << 14); }
+
+__device__ __forceinline__ void dma16(const void* g, bf16* l) { __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0); }
+
+// Compiler-level fence around the raw s_barrier (the barrier builtin itself
+// does not order memory operations for the compiler).
+__device__ __forceinline__ void block_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ int lds_pos(int r, int c) { return r * BK + ((c ^ ((r >> 2) & 3)) << 3); }
+
+// The direct loads of one K step into one stage buffer: load i of wave w
+// fills 16 rows (NW*i + w)*16 .. +16 (1 KB) of the A part, then of the B part.
+template <class C>
+__device__ __forceinline__ void issue_stage(bf16* st, const bf16* abase, const uint32_t* aoff,
+                                            const bf16* const* bbase, const uint32_t* boff, uint32_t k0, int wave) {
+#pragma unroll
+  for (int i = 0; i < C::LA; ++i) dma16(abase + (aoff[i] + k0), st + (C::NW * i + wave) * 512);
+#pragma unroll
+  for (int i = 0; i < C::LB; ++i) dma16(bbase[i] + (boff[i] + k0), st + C::BM * BK + (C::NW * i + wave) * 512);
+}
+
+template <class C, int NB>
+__device__ __forceinline__ void load_frags(const bf16* st, int ks, int wm, int wn, int lane, bf16x8* af,
+                                           bf16x8* bfr) {
+  const int c = ks * 2 + (lane >> 5);
+#pragma unroll
+  for (int ii = 0; ii < NB; ++ii)
+    af[ii] = *reinterpret_cast<const bf16x8*>(st + lds_pos((wm + C::WM * ii) * 32 + (lane & 31), c));
+#pragma unroll
+  for (int jj = 0; jj < C::NJ; ++jj)
+    bfr[jj] = *reinterpret_cast<const bf16x8*>(st + lds_pos(C::BM + wn * C::CW + jj * 32 + (lane & 31), c));
+}
+
+// MFMAs of one stage: 2 K sub-steps of 16, fragments of both loaded first.
+template <class C, int NB>
+__device__ __forceinline__ void compute_stage(f32x16 (&acc)[C::MI][C::NJ], const bf16* st, int wm, int wn,
+                                              int lane) {
+  bf16x8 af[2][NB], bfr[2][C::NJ];
+  load_frags<C, NB>(st, 0, wm, wn, lane, af[0], bfr[0]);
+  load_frags<C, NB>(st, 1, wm, wn, lane, af[1], bfr[1]);
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks)
+#pragma unroll
+    for (int ii = 0; ii < NB; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < C::NJ; ++jj)
+        acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][ii], bfr[ks][jj], acc[ii][jj], 0, 0, 0);
+}
+
+// One K step s held in buffer b: wait until this wave's loads of step s have
+// landed (the S-2 younger stages may stay in flight), one barrier (every
+// wave's loads landed, every wave done with buffer b-1), refill buffer b-1
+// with step s+S-1 (past the end: the last step again, never read), MFMAs.
+template <class C, int NB, int B>
+__device__ __forceinline__ void step(f32x16 (&acc)[C::MI][C::NJ], bf16* const* stg, const bf16* abase,
+                                     const uint32_t* aoff, const bf16* const* bbase, const uint32_t* boff, int s,
+                                     uint32_t klast, int wave, int wm, int wn, int lane) {
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((C::S - 2) * C::L));
+  block_sync();
+  const uint32_t kn = (uint32_t)(s + C::S - 1) * BK;
+  issue_stage<C>(stg[(B + C::S - 1) % C::S], abase, aoff, bbase, boff, kn < klast ? kn : klast, wave);
+  compute_stage<C, NB>(acc, stg[B], wm, wn, lane);
+}
+
+// The K loop of one tile over nk steps, nk % S == R: step s uses buffer s % S.
+template <class C, int NB, int R>
+__device__ __forceinline__ void mainloop(f32x16 (&acc)[C::MI][C::NJ], bf16* const* stg, const bf16* abase,
+                                         const uint32_t* aoff, const bf16* const* bbase, const uint32_t* boff,
+                                         int nk, int wave, int wm, int wn, int lane) {
+  const uint32_t klast = (uint32_t)(nk - 1) * BK;
+  // every wave's loads (vmcnt(0) before the call) and LDS reads of the
+  // previous tile are finished before its buffers are refilled
+  block_sync();
+#pragma unroll
+  for (int st = 0; st < C::S - 1; ++st) {
+    const uint32_t k0 = (uint32_t)st * BK;
+    issue_stage<C>(stg[st], abase, aoff, bbase, boff, k0 < klast ? k0 : klast, wave);
+  }
+  const int nfull = nk - R;
+  for (int kt = 0; kt < nfull; kt += C::S) {
+    step<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, kt + 0, klast, wave, wm, wn, lane);
+    step<C, NB, 1>(acc, stg, abase, aoff, bbase, boff, kt + 1, klast, wave, wm, wn, lane);
+    if constexpr (C::S > 2) step<C, NB, 2>(acc, stg, abase, aoff, bbase, boff, kt + 2, klast, wave, wm, wn, lane);
+    if constexpr (C::S > 3) step<C, NB, 3>(acc, stg, abase, aoff, bbase, boff, kt + 3, klast, wave, wm, wn, lane);
+    if constexpr (C::S > 4) step<C, NB, 4>(acc, stg, abase, aoff, bbase, boff, kt + 4, klast, wave, wm, wn, lane);
+    if constexpr (C::S > 5) step<C, NB, 5>(acc, stg, abase, aoff, bbase, boff, kt + 5, klast, wave, wm, wn, lane);
+  }
+  if constexpr (R > 0) step<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, nfull + 0, klast, wave, wm, wn, lane);
+  if constexpr (R > 1) step<C, NB, 1>(acc, stg, abase, aoff, bbase, boff, nfull + 1, klast, wave, wm, wn, lane);
+  if constexpr (R > 2) step<C, NB, 2>(acc, stg, abase, aoff, bbase, boff, nfull + 2, klast, wave, wm, wn, lane);
+  if constexpr (R > 3) step<C, NB, 3>(acc, stg, abase, aoff, bbase, boff, nfull + 3, klast, wave, wm, wn, lane);
+  if constexpr (R > 4) step<C, NB, 4>(acc, stg, abase, aoff, bbase, boff, nfull + 4, klast, wave, wm, wn, lane);
+}
+
+template <class C, int NB>
+__device__ __forceinline__ void mainloop_r(f32x16 (&acc)[C::MI][C::NJ], bf16* const* stg, const bf16* abase,
+                                           const uint32_t* aoff, const bf16* const* bbase, const uint32_t* boff,
+                                           int nk, int wave, int wm, int wn, int lane) {
+  const int r = nk % C::S;
+  if (r == 0) mainloop<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
+  else if (C::S > 1 && r == 1) mainloop<C, NB, 1 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
+  else if (C::S > 2 && r == 2) mainloop<C, NB, 2 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
+  else if (C::S > 3 && r == 3) mainloop<C, NB, 3 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
+  else if (C::S > 4 && r == 4) mainloop<C, NB, 4 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
+  else mainloop<C, NB, 5 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
+}
+
+template <class C, int MODE>
+__global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArgs f, int n_tiles_n) {
+  __shared__ __attribute__((aligned(1024))) bf16 s0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16 s1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16 s2[C::S > 2 ? C::STAGE : 8];
+  __shared__ __attribute__((aligned(1024))) bf16 s3[C::S > 3 ? C::STAGE : 8];
+  __shared__ __attribute__((aligned(1024))) bf16 s4[C::S > 4 ? C::STAGE : 8];
+  __shared__ __attribute__((aligned(1024))) bf16 s5[C::S > 5 ? C::STAGE : 8];
+  bf16* const stg[6] = {s0, s1, s2, s3, s4, s5};
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+
+  const int MT = f.plan[0];  // m-tiles: routed groups, then the shared expert
+  const int total = MT * n_tiles_n;
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+
+  for (int it = 0;; ++it) {
+    const int t = it * G + xcd * (G >> 3) + slot;
+    if (t >= total) break;
+    // supertile order: SUPER m-tiles x all n-tiles, m fastest
+    const int sbase = (t / (SUPER * n_tiles_n)) * SUPER;
+    const int grp = MT - sbase < SUPER ? MT - sbase : SUPER;
+    const int r = t - sbase * n_tiles_n;
+    const int nt = r / grp;
+    const int mt = sbase + r % grp;
+
+    const int g = f.mt_group[mt];
+    const int r0 = f.mt_row0[mt];
+    const bool shared = g >= f.E;
+    int base = 0, nrows;
+    if (!shared) {
+      base = f.offsets[g];
+      nrows = f.offsets[g + 1] - base - r0;
+    } else {
+      nrows = f.T - r0;
+    }
+    nrows = nrows < C::BM ? nrows : C::BM;
+    const int K = MODE == 1 ? f.H : (shared ? f.Is : f.I);
+    const int Ncols = MODE == 1 ? (shared ? f.Is : f.I) : f.H;
+    const int ncov = MODE == 1 ? C::BN / 2 : C::BN;
+    if (nt * ncov >= Ncols) continue;
+
+    // ---- sources of the direct loads of each K step ----
+    // lane l of a load fills row +l/4 of its 16-row group at position l%4,
+    // so it fetches global chunk (l%4) ^ ((row>>2)&3) = (l%4) ^ ((l>>4)&3).
+    // Bases are wave-uniform (SGPRs); lanes carry 32-bit element offsets.
+    const int lrow = lane >> 2;
+    const int gchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    const bf16* abase;
+    if (MODE == 1) abase = reinterpret_cast<const bf16*>(f.x);
+    else abase = shared ? reinterpret_cast<const bf16*>(f.h_sh) : reinterpret_cast<const bf16*>(f.h);
+    uint32_t aoff[C::LA], boff[C::LB];
+    const bf16* bbase[C::LB];
+#pragma unroll
+    for (int i = 0; i < C::LA; ++i) {
+      int rr = (C::NW * i + wave) * 16 + lrow;
+      rr = rr < nrows ? rr : nrows - 1;
+      const int gr = base + r0 + rr;
+      if (MODE == 1) {
+        int tok = shared ? gr : f.sorted[gr] / f.k;
+        tok = tok < f.T ? tok : f.T - 1;
+        aoff[i] = (uint32_t)tok * (uint32_t)f.H + gchunk * 8;
+      } else {
+        aoff[i] = (uint32_t)gr * (uint32_t)K + gchunk * 8;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::LB; ++i) {
+      const int grp16 = (C::NW * i + wave) * 16;  // wave-uniform first row of the load
+      const int n = grp16 + lrow;                 // B tile row
+      int col;
+      if (MODE == 1) {
+        // wave column wc (CW rows) holds CW/2 gate rows, then the up rows of
+        // the same CW/2 hidden columns
+        const bool up = (grp16 % C::CW) >= C::CW / 2;
+        col = nt * (C::BN / 2) + (n / C::CW) * (C::CW / 2) + (n % (C::CW / 2));
+        bbase[i] = shared ? reinterpret_cast<const bf16*>(up ? f.shu : f.shg)
+                          : reinterpret_cast<const bf16*>(up ? f.wu : f.wg) + (int64_t)g * (up ? f.su : f.sg);
+      } else {
+        col = nt * C::BN + n;
+        bbase[i] = shared ? reinterpret_cast<const bf16*>(f.shd) : reinterpret_cast<const bf16*>(f.wd) + (int64_t)g * f.sd;
+      }
+      col = col < Ncols ? col : Ncols - 1;
+      boff[i] = (uint32_t)col * (uint32_t)K + gchunk * 8;
+    }
+
+    f32x16 acc[C::MI][C::NJ];
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    // M-blocks of 32 rows this wave computes (blocks wm, wm+WM, ... below nrows)
+    const int nblk_tile = (nrows + 31) / 32;
+    const int nb = (nblk_tile - wm + C::WM - 1) / C::WM;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // previous tile's loads and stores settled
+    const int nk = K / BK;
+    if constexpr (C::MI >= 4) {
+      if (nb >= 4) mainloop_r<C, 4>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
+      else if (nb == 3) mainloop_r<C, 3>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
+      else if (nb == 2) mainloop_r<C, 2>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
+      else mainloop_r<C, 1>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
+    } else {
+      if (nb >= 2) mainloop_r<C, 2>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
+      else mainloop_r<C, 1>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
+    }
+
+    // ---- epilogue: C lane layout col = lane%32, row 8*(v/4) + 4*(lane/32) + v%4 ----
+#pragma unroll
+    for (int ii = 0; ii < C::MI; ++ii) {
+      const int mb = wm + C::WM * ii;
+      if (mb * 32 >= nrows) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rl = mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (rl >= nrows) continue;
+        const int64_t gr = base + r0 + rl;
+        if (MODE == 1) {
+          bf16* dst = shared ? reinterpret_cast<bf16*>(f.h_sh) + gr * f.Is : reinterpret_cast<bf16*>(f.h) + gr * f.I;
+#pragma unroll
+          for (int jj = 0; jj < C::NJ / 2; ++jj) {
+            const int col = nt * (C::BN / 2) + wn * (C::CW / 2) + jj * 32 + (lane & 31);
+            if (col < Ncols) dst[col] = f2bf(silu(acc[ii][jj][v]) * acc[ii][jj + C::NJ / 2][v]);
+          }
+        } else {
+          bf16* dst = shared ? reinterpret_cast<bf16*>(f.y_sh) : reinterpret_cast<bf16*>(f.y);
+#pragma unroll
+          for (int jj = 0; jj < C::NJ; ++jj) {
+            const int col = nt * C::BN + wn * C::CW + jj * 32 + (lane & 31);
+            if (col < Ncols) dst[gr * f.H + col] = f2bf(acc[ii][jj][v]);
+          }
+        }
+      }
+    }
+  }
+}
+
+int cu_count() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus = n;
+  }
+  return cus;
+}
+
+template <class C>
+hipError_t launch(const FfnArgs& a, int phase, hipStream_t s) {
+  const int wide = a.I > a.Is ? a.I : a.Is;
+  const int ntn = phase == 1 ? (wide + C::BN / 2 - 1) / (C::BN / 2) : (a.H + C::BN - 1) / C::BN;
+  const int grid = (cu_count() * C::WG_PER_CU + 7) / 8 * 8;  // resident workgroups, a multiple of 8 XCDs
+  if (phase == 1) dma_gemm_kernel<C, 1><<<grid, C::NT, 0, s>>>(a, ntn);
+  else dma_gemm_kernel<C, 2><<<grid, C::NT, 0, s>>>(a, ntn);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool ffn_dma_supported(const FfnArgs& a) {
+  return !a.fp8 && a.H % BK == 0 && a.I % BK == 0 && (a.Is == 0 || a.Is % BK == 0);
+}
+
+hipError_t launch_ffn_gemm_dma(const FfnArgs& a, int phase, hipStream_t s) { return launch<BigCfg>(a, phase, s); }
+
+}  // namespace moe

@@ -6,7 +6,7 @@
 
 namespace moe {
 
-// Rows per MFMA GEMM m-tile (LDS-tiled kernel / big-tile kernel) and per
+// Rows per MFMA GEMM m-tile (128-row kernels / big-tile kernel) and per
 // streaming m-block.
 constexpr int kGemmBM = 128;
 constexpr int kGemmBigBM = 256;
@@ -61,8 +61,10 @@ hipError_t launch_ffn_plan(const int32_t* offsets, const int32_t* sorted, int T,
                            uint32_t flags, int bm, int32_t* plan_ws, hipStream_t s);
 void ffn_bind_plan(FfnArgs& a, int32_t* plan_ws);
 hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s);    // phase 1 gate/up, 2 down
-bool ffn_big_supported(const FfnArgs& a);
-hipError_t launch_ffn_gemm_big(const FfnArgs& a, int phase, hipStream_t s);
+// Pipelined direct-load MFMA GEMM with 256-row tiles (bf16 weights, H, I,
+// I_shared multiples of 32).
+bool ffn_dma_supported(const FfnArgs& a);
+hipError_t launch_ffn_gemm_dma(const FfnArgs& a, int phase, hipStream_t s);
 hipError_t launch_ffn_stream(const FfnArgs& a, int phase, hipStream_t s);  // phase 1 gate/up, 2 down
 hipError_t launch_ffn_f32(const FfnArgs& a, int phases, hipStream_t s);  // bit 0 gate/up, bit 1 down
 hipError_t launch_combine(const void* y, const int32_t* pos, const float* w, const void* y_sh,
