@@ -5,10 +5,11 @@
 
 One step is one pass of the whole layer over one batch of synthetic input
 resident in HBM: router + top-k, dispatch, grouped gate/up GEMM, grouped down
-GEMM, weighted combine with the gated shared expert, each through its C-ABI
-entry point on the current stream, with HIP events between the stages (the
-same kernels moe_layer_forward launches).  K steps are timed back to back
-between two device synchronisations; stage durations come from the events.
+GEMM, weighted combine with the gated shared expert, as one moe_layer_forward
+call on the current stream.  K steps are timed back to back between two device
+synchronisations.  The same layer is then run K more times stage by stage,
+each stage through its own C-ABI entry point with HIP events between them;
+those events give the per-stage durations.
 
 Prints one JSON line: tokens/s for the whole step, the roofline of the
 dominant kernel (algorithmic bytes or FLOPs per launch over its event-timed
@@ -161,30 +162,30 @@ def main():
         lib.moe_combine(P, y, pos, tw, y_sh, sl, out, stream)
         ev[5].record(stream)
 
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    # the timed steps: the whole layer, one moe_layer_forward call per step
     for _ in range(args.warmup):
-        step(mk())
-    torch.cuda.synchronize()
-    evs = [mk() for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    names = ["route", "dispatch", "gate_up", "down", "combine"]
-    stage_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, n in enumerate(names)}
-
-    # the whole layer in one call, same buffers (reported beside the staged step)
-    for _ in range(2):
         lib.moe_layer_forward(P, W, prob.x, out, None, None, ws, stream)
     torch.cuda.synchronize()
-    t2 = time.perf_counter()
+    t0 = time.perf_counter()
     for _ in range(args.steps):
         lib.moe_layer_forward(P, W, prob.x, out, None, None, ws, stream)
     torch.cuda.synchronize()
-    layer_ms = (time.perf_counter() - t2) * 1e3 / args.steps
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # the same layer stage by stage, HIP events on the launch stream between the
+    # entry points: per-stage durations for the roofline of the dominant kernel
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for _ in range(max(1, args.warmup)):
+        step(mk())
+    torch.cuda.synchronize()
+    evs = [mk() for _ in range(args.steps)]
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    staged_ms = (time.perf_counter() - t2) * 1e3 / args.steps
+    names = ["route", "dispatch", "gate_up", "down", "combine"]
+    stage_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, n in enumerate(names)}
 
     counts = torch.diff(offs).cpu()
     touched = int((counts > 0).sum())
@@ -226,7 +227,7 @@ def main():
         "layer": {"tflops": round(work.flops / t_s / 1e12, 2), "hbm_gbps": round(work.bytes / t_s / 1e9, 1),
                   "mfma_frac": round(work.flops / t_s / 1e12 / mfma_peak, 4),
                   "hbm_frac": round(work.bytes / t_s / 1e9 / acc.PEAK_HBM_GBPS, 4),
-                  "single_call_ms": round(layer_ms, 4), "single_call_tokens_per_s": round(T / layer_ms * 1e3, 1)},
+                  "staged_ms": round(staged_ms, 4)},
         "stages_ms": {n: round(v, 4) for n, v in stage_ms.items()},
         "roofline": roof,
     }
