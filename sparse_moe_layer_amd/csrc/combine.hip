@@ -1,9 +1,9 @@
 // Weighted combine + gated shared expert (Qwen3.8-Flash-Next study, MoE
 // section: the last stage of the pipeline figure and eq. MoE(x)):
 //   out[t] = sum_{j<k} w[t,j] * y[pos[t*k+j]] + sigmoid(s_t) * y_shared[t]
-// One workgroup per token, 16-byte loads of y rows (8 bf16 or 4 fp32 per
-// thread), fp32 accumulation with j ascending, one rounding to the output
-// dtype.  HBM-bound: reads k+1 rows of H and writes one.
+// 16-byte loads of y rows (8 bf16 or 4 fp32 per thread), fp32 accumulation
+// with j ascending, one rounding to the output dtype.  HBM-bound: reads k+1
+// rows of H and writes one.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -24,6 +24,10 @@ __device__ __forceinline__ void accumulate(float* acc, float wgt, u32x4 v) {
   }
 }
 
+// Workgroup (t, blockIdx.y) covers 16-byte chunks blockIdx.y*256 + tid of
+// token t.  The token's k row positions and weights are staged in LDS once;
+// a thread then issues the y loads of up to 8 assignments before adding them
+// (j ascending), so the k+1 row reads overlap instead of forming a chain.
 template <bool F32>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y, const int32_t* __restrict__ pos,
                                                       const float* __restrict__ w, const void* __restrict__ y_sh,
@@ -31,33 +35,44 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                                                       int k) {
   constexpr int VEC = F32 ? 4 : 8;
   constexpr int ESZ = F32 ? 4 : 2;
+  constexpr int BATCH = 8;
+  __shared__ int64_t s_row[64];
+  __shared__ float s_w[64];
   const int t = blockIdx.x;
-  const float gamma = y_sh ? sigmoid(sl[t]) : 0.f;
-  const int nchunk = H / VEC;
-  for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
-    float acc[VEC];
+  if ((int)threadIdx.x < k) {
+    const int64_t a = (int64_t)t * k + threadIdx.x;
+    s_row[threadIdx.x] = (int64_t)pos[a] * H;
+    s_w[threadIdx.x] = w[a];
+  }
+  __syncthreads();
+  const int c = blockIdx.y * blockDim.x + threadIdx.x;
+  if (c >= H / VEC) return;
+  const int64_t col = (int64_t)c * VEC;
+  const char* yb = reinterpret_cast<const char*>(y);
+  float acc[VEC];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int64_t a = (int64_t)t * k + j;
-      const float wj = w[a];
-      const int64_t p = pos[a];
-      const u32x4 v = ld16(reinterpret_cast<const char*>(y) + (p * H + (int64_t)c * VEC) * ESZ);
-      accumulate<F32>(acc, wj, v);
-    }
-    if (y_sh) {
-      const u32x4 v = ld16(reinterpret_cast<const char*>(y_sh) + ((int64_t)t * H + (int64_t)c * VEC) * ESZ);
-      accumulate<F32>(acc, gamma, v);
-    }
-    char* dst = reinterpret_cast<char*>(out) + ((int64_t)t * H + (int64_t)c * VEC) * ESZ;
-    if constexpr (F32) {
-      st16(dst, __builtin_bit_cast(u32x4, f32x4{acc[0], acc[1], acc[2], acc[3]}));
-    } else {
-      bf16x8 o;
+  for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+  for (int j0 = 0; j0 < k; j0 += BATCH) {
+    u32x4 v[BATCH];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = f2bf(acc[i]);
-      st16(dst, __builtin_bit_cast(u32x4, o));
-    }
+    for (int b = 0; b < BATCH; ++b)
+      if (j0 + b < k) v[b] = ld16(yb + (s_row[j0 + b] + col) * ESZ);
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b)
+      if (j0 + b < k) accumulate<F32>(acc, s_w[j0 + b], v[b]);
+  }
+  if (y_sh) {
+    const u32x4 v = ld16(reinterpret_cast<const char*>(y_sh) + ((int64_t)t * H + col) * ESZ);
+    accumulate<F32>(acc, sigmoid(sl[t]), v);
+  }
+  char* dst = reinterpret_cast<char*>(out) + ((int64_t)t * H + col) * ESZ;
+  if constexpr (F32) {
+    st16(dst, __builtin_bit_cast(u32x4, f32x4{acc[0], acc[1], acc[2], acc[3]}));
+  } else {
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = f2bf(acc[i]);
+    st16(dst, __builtin_bit_cast(u32x4, o));
   }
 }
 
@@ -65,8 +80,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 
 hipError_t launch_combine(const void* y, const int32_t* pos, const float* w, const void* y_sh,
                           const float* shared_logit, void* out, int T, int H, int k, int f32, hipStream_t s) {
-  if (f32) combine_kernel<true><<<T, 256, 0, s>>>(y, pos, w, y_sh, shared_logit, out, H, k);
-  else combine_kernel<false><<<T, 256, 0, s>>>(y, pos, w, y_sh, shared_logit, out, H, k);
+  const int vec = f32 ? 4 : 8;
+  const dim3 grid(T, (H / vec + 255) / 256);
+  if (f32) combine_kernel<true><<<grid, 256, 0, s>>>(y, pos, w, y_sh, shared_logit, out, H, k);
+  else combine_kernel<false><<<grid, 256, 0, s>>>(y, pos, w, y_sh, shared_logit, out, H, k);
   return hipGetLastError();
 }
 

@@ -3,20 +3,56 @@
 // (Qwen3.8-Flash-Next study, MoE section: "Top 10 + normalize" in the
 // pipeline figure; "Selected router probabilities are normalized").
 //
-// Each lane holds E/64 fp32 logits in registers.  k rounds of a wave-wide
-// argmax (64-lane xor butterfly on (value, id), larger value wins, equal
-// values go to the lower id) pick the experts in descending order; lane j
-// keeps round j's winner.  The renormalised weight of the j-th pick is
-// exp(l_j - l_0) / sum_{j'<k} exp(l_j' - l_0), which equals the selected
-// softmax probabilities divided by their sum (the full softmax's
+// Each lane holds E/64 logits as 64-bit keys: an order-preserving image of
+// the fp32 value in the high word, the complement of the expert id in the low
+// word, so one unsigned maximum ranks by value and sends equal values to the
+// lower id.  k rounds of a wave-wide maximum (DPP within each 16-lane row,
+// then the four row results through readlane) pick the experts in descending
+// order; lane j keeps round j's winner.  The renormalised weight of the j-th
+// pick is exp(l_j - l_0) / sum_{j'<k} exp(l_j' - l_0), which equals the
+// selected softmax probabilities divided by their sum (the full softmax's
 // normaliser cancels).  Also the fp32 SIMT router used for fp32 layers.
-#include <float.h>
-
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 namespace {
+
+// Monotone map fp32 -> u32 (a < b as floats <=> ord(a) < ord(b) unsigned),
+// with -0 folded onto +0 so that equal values compare equal.  Every real
+// logit maps above 0, which marks padding and taken entries.
+__device__ __forceinline__ uint32_t ord(float v) {
+  const uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
+  return (u >> 31) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unord(uint32_t m) { return __uint_as_float((m >> 31) ? (m & 0x7fffffffu) : ~m); }
+
+__device__ __forceinline__ void key_max(uint32_t& hi, uint32_t& lo, uint32_t ohi, uint32_t olo) {
+  const bool gt = ohi > hi || (ohi == hi && olo > lo);
+  hi = gt ? ohi : hi;
+  lo = gt ? olo : lo;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void dpp_max(uint32_t& hi, uint32_t& lo) {
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, 0xf, 0xf, false);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, 0xf, 0xf, false);
+  key_max(hi, lo, ohi, olo);
+}
+
+// Maximum key over the 64 lanes, returned in every lane.
+__device__ __forceinline__ void wave_key_max(uint32_t& hi, uint32_t& lo) {
+  dpp_max<0xb1>(hi, lo);   // quad_perm [1,0,3,2]
+  dpp_max<0x4e>(hi, lo);   // quad_perm [2,3,0,1]: quad maximum in every lane
+  dpp_max<0x141>(hi, lo);  // row_half_mirror: 8-lane maximum
+  dpp_max<0x140>(hi, lo);  // row_mirror: 16-lane (row) maximum
+  uint32_t bh = __builtin_amdgcn_readlane(hi, 0), bl = __builtin_amdgcn_readlane(lo, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r)
+    key_max(bh, bl, __builtin_amdgcn_readlane(hi, 16 * r), __builtin_amdgcn_readlane(lo, 16 * r));
+  hi = bh;
+  lo = bl;
+}
 
 template <int PER_LANE>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ partial, int nsplit, int ldl, int T,
@@ -28,49 +64,36 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
   // logits = sum of the K-chunk partials, chunk order fixed
   const int64_t cstride = (int64_t)T * ldl;
   const float* row = partial + (int64_t)t * ldl;
-  float v[PER_LANE];
+  uint32_t khi[PER_LANE], klo[PER_LANE];
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
     const int e = lane + 64 * i;
     float a = 0.f;
     if (e < E)
       for (int c = 0; c < nsplit; ++c) a += row[c * cstride + e];
-    v[i] = e < E ? a : -FLT_MAX;
+    khi[i] = e < E ? ord(a) : 0u;
+    klo[i] = ~(uint32_t)e;
   }
-  uint32_t taken = 0;
-  float sel_v = 0.f;
-  int sel_e = 0;
+  uint32_t sel_hi = 0, sel_lo = 0;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
+    uint32_t bh = khi[0], bl = klo[0];
 #pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < be))) {
-        bv = v[i];
-        be = e;
-      }
-    }
+    for (int i = 1; i < PER_LANE; ++i) key_max(bh, bl, khi[i], klo[i]);
+    wave_key_max(bh, bl);
+    const int e = (int)~bl;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oe = __shfl_xor(be, o, 64);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    for (int i = 0; i < PER_LANE; ++i)
+      if (lane + 64 * i == e) khi[i] = 0u;  // taken
     if (lane == j) {
-      sel_v = bv;
-      sel_e = be;
+      sel_hi = bh;
+      sel_lo = bl;
     }
   }
-  const float top = __shfl(sel_v, 0, 64);
-  const float ex = lane < k ? expf(sel_v - top) : 0.f;
+  const float top = unord(__builtin_amdgcn_readlane(sel_hi, 0));
+  const float ex = lane < k ? expf(unord(sel_hi) - top) : 0.f;
   const float sum = wave_sum(ex);
   if (lane < k) {
-    ids[(int64_t)t * k + lane] = sel_e;
+    ids[(int64_t)t * k + lane] = (int32_t)~sel_lo;
     w[(int64_t)t * k + lane] = ex / sum;
   }
   if (has_sg && lane == 0) {
