@@ -23,7 +23,7 @@
 // reads stay whole 64-byte row segments.
 //
 // Work: (group, 256-row m-tile) entries from the device plan; tiles are
-// ordered in supertiles of 8 m-tiles x all n-tiles and dealt to the
+// ordered in supertiles of a few m-tiles x all n-tiles and dealt to the
 // persistent grid so that consecutive tiles land on one XCD (workgroup i runs
 // on XCD i mod 8), sharing A slices and weight slices in that XCD's L2.
 #include "common.hpp"
@@ -33,7 +33,6 @@ namespace moe {
 namespace {
 
 constexpr int BK = 32;     // K per pipeline stage (64-byte rows)
-constexpr int SUPER = 8;   // m-tiles per supertile
 
 template <int BM_, int BN_, int WM_, int WN_, int S_, int WG_PER_CU_>
 struct Cfg {
@@ -79,32 +78,63 @@ __device__ __forceinline__ void issue_stage(bf16* st, const bf16* abase, const u
   for (int i = 0; i < C::LB; ++i) dma16(bbase[i] + (boff[i] + k0), st + C::BM * BK + (C::NW * i + wave) * 512);
 }
 
+// Element offsets of this lane's fragment reads inside a stage for K sub-step
+// ks: row (lane % 32) of the wave's first A / B block, chunk 2*ks + lane/32,
+// swizzled.  Block ii / jj adds a whole number of 32-row blocks, so every
+// fragment read is one of these plus a compile-time offset.
+struct FragOff {
+  int a[2], b[2];
+};
+
+template <class C>
+__device__ __forceinline__ FragOff frag_offsets(int wm, int wn, int lane) {
+  FragOff o;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int c = ks * 2 + (lane >> 5);
+    o.a[ks] = lds_pos(wm * 32 + (lane & 31), c);
+    o.b[ks] = lds_pos(C::BM + wn * C::CW + (lane & 31), c);
+  }
+  return o;
+}
+
 template <class C, int NB>
-__device__ __forceinline__ void load_frags(const bf16* st, int ks, int wm, int wn, int lane, bf16x8* af,
-                                           bf16x8* bfr) {
-  const int c = ks * 2 + (lane >> 5);
+__device__ __forceinline__ void load_frags(const bf16* st, int ks, const FragOff& o, bf16x8* af, bf16x8* bfr) {
 #pragma unroll
   for (int ii = 0; ii < NB; ++ii)
-    af[ii] = *reinterpret_cast<const bf16x8*>(st + lds_pos((wm + C::WM * ii) * 32 + (lane & 31), c));
+    af[ii] = *reinterpret_cast<const bf16x8*>(st + o.a[ks] + ii * C::WM * 32 * BK);
 #pragma unroll
   for (int jj = 0; jj < C::NJ; ++jj)
-    bfr[jj] = *reinterpret_cast<const bf16x8*>(st + lds_pos(C::BM + wn * C::CW + jj * 32 + (lane & 31), c));
+    bfr[jj] = *reinterpret_cast<const bf16x8*>(st + o.b[ks] + jj * 32 * BK);
 }
 
 // MFMAs of one stage: 2 K sub-steps of 16, fragments of both loaded first.
 template <class C, int NB>
-__device__ __forceinline__ void compute_stage(f32x16 (&acc)[C::MI][C::NJ], const bf16* st, int wm, int wn,
-                                              int lane) {
-  bf16x8 af[2][NB], bfr[2][C::NJ];
-  load_frags<C, NB>(st, 0, wm, wn, lane, af[0], bfr[0]);
-  load_frags<C, NB>(st, 1, wm, wn, lane, af[1], bfr[1]);
+__device__ __forceinline__ void compute_stage(f32x16 (&acc)[C::MI][C::NJ], const bf16* st, const FragOff& o) {
+  if constexpr (C::MI * C::NJ > 8) {
+    // 128 x 128 wave tiles: one K sub-step of fragments at a time
 #pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks)
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 af[NB], bfr[C::NJ];
+      load_frags<C, NB>(st, ks, o, af, bfr);
 #pragma unroll
-    for (int ii = 0; ii < NB; ++ii)
+      for (int ii = 0; ii < NB; ++ii)
 #pragma unroll
-      for (int jj = 0; jj < C::NJ; ++jj)
-        acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][ii], bfr[ks][jj], acc[ii][jj], 0, 0, 0);
+        for (int jj = 0; jj < C::NJ; ++jj)
+          acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ii], bfr[jj], acc[ii][jj], 0, 0, 0);
+    }
+  } else {
+    bf16x8 af[2][NB], bfr[2][C::NJ];
+    load_frags<C, NB>(st, 0, o, af[0], bfr[0]);
+    load_frags<C, NB>(st, 1, o, af[1], bfr[1]);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks)
+#pragma unroll
+      for (int ii = 0; ii < NB; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < C::NJ; ++jj)
+          acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][ii], bfr[ks][jj], acc[ii][jj], 0, 0, 0);
+  }
 }
 
 // One K step s held in buffer b: wait until this wave's loads of step s have
@@ -114,19 +144,19 @@ __device__ __forceinline__ void compute_stage(f32x16 (&acc)[C::MI][C::NJ], const
 template <class C, int NB, int B>
 __device__ __forceinline__ void step(f32x16 (&acc)[C::MI][C::NJ], bf16* const* stg, const bf16* abase,
                                      const uint32_t* aoff, const bf16* const* bbase, const uint32_t* boff, int s,
-                                     uint32_t klast, int wave, int wm, int wn, int lane) {
+                                     uint32_t klast, int wave, const FragOff& o) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((C::S - 2) * C::L));
   block_sync();
   const uint32_t kn = (uint32_t)(s + C::S - 1) * BK;
   issue_stage<C>(stg[(B + C::S - 1) % C::S], abase, aoff, bbase, boff, kn < klast ? kn : klast, wave);
-  compute_stage<C, NB>(acc, stg[B], wm, wn, lane);
+  compute_stage<C, NB>(acc, stg[B], o);
 }
 
 // The K loop of one tile over nk steps, nk % S == R: step s uses buffer s % S.
 template <class C, int NB, int R>
 __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::MI][C::NJ], bf16* const* stg, const bf16* abase,
                                          const uint32_t* aoff, const bf16* const* bbase, const uint32_t* boff,
-                                         int nk, int wave, int wm, int wn, int lane) {
+                                         int nk, int wave, const FragOff& o) {
   const uint32_t klast = (uint32_t)(nk - 1) * BK;
   // every wave's loads (vmcnt(0) before the call) and LDS reads of the
   // previous tile are finished before its buffers are refilled
@@ -138,35 +168,35 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::MI][C::NJ], bf16* cons
   }
   const int nfull = nk - R;
   for (int kt = 0; kt < nfull; kt += C::S) {
-    step<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, kt + 0, klast, wave, wm, wn, lane);
-    step<C, NB, 1>(acc, stg, abase, aoff, bbase, boff, kt + 1, klast, wave, wm, wn, lane);
-    if constexpr (C::S > 2) step<C, NB, 2>(acc, stg, abase, aoff, bbase, boff, kt + 2, klast, wave, wm, wn, lane);
-    if constexpr (C::S > 3) step<C, NB, 3>(acc, stg, abase, aoff, bbase, boff, kt + 3, klast, wave, wm, wn, lane);
-    if constexpr (C::S > 4) step<C, NB, 4>(acc, stg, abase, aoff, bbase, boff, kt + 4, klast, wave, wm, wn, lane);
-    if constexpr (C::S > 5) step<C, NB, 5>(acc, stg, abase, aoff, bbase, boff, kt + 5, klast, wave, wm, wn, lane);
+    step<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, kt + 0, klast, wave, o);
+    step<C, NB, 1>(acc, stg, abase, aoff, bbase, boff, kt + 1, klast, wave, o);
+    if constexpr (C::S > 2) step<C, NB, 2>(acc, stg, abase, aoff, bbase, boff, kt + 2, klast, wave, o);
+    if constexpr (C::S > 3) step<C, NB, 3>(acc, stg, abase, aoff, bbase, boff, kt + 3, klast, wave, o);
+    if constexpr (C::S > 4) step<C, NB, 4>(acc, stg, abase, aoff, bbase, boff, kt + 4, klast, wave, o);
+    if constexpr (C::S > 5) step<C, NB, 5>(acc, stg, abase, aoff, bbase, boff, kt + 5, klast, wave, o);
   }
-  if constexpr (R > 0) step<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, nfull + 0, klast, wave, wm, wn, lane);
-  if constexpr (R > 1) step<C, NB, 1>(acc, stg, abase, aoff, bbase, boff, nfull + 1, klast, wave, wm, wn, lane);
-  if constexpr (R > 2) step<C, NB, 2>(acc, stg, abase, aoff, bbase, boff, nfull + 2, klast, wave, wm, wn, lane);
-  if constexpr (R > 3) step<C, NB, 3>(acc, stg, abase, aoff, bbase, boff, nfull + 3, klast, wave, wm, wn, lane);
-  if constexpr (R > 4) step<C, NB, 4>(acc, stg, abase, aoff, bbase, boff, nfull + 4, klast, wave, wm, wn, lane);
+  if constexpr (R > 0) step<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, nfull + 0, klast, wave, o);
+  if constexpr (R > 1) step<C, NB, 1>(acc, stg, abase, aoff, bbase, boff, nfull + 1, klast, wave, o);
+  if constexpr (R > 2) step<C, NB, 2>(acc, stg, abase, aoff, bbase, boff, nfull + 2, klast, wave, o);
+  if constexpr (R > 3) step<C, NB, 3>(acc, stg, abase, aoff, bbase, boff, nfull + 3, klast, wave, o);
+  if constexpr (R > 4) step<C, NB, 4>(acc, stg, abase, aoff, bbase, boff, nfull + 4, klast, wave, o);
 }
 
 template <class C, int NB>
 __device__ __forceinline__ void mainloop_r(f32x16 (&acc)[C::MI][C::NJ], bf16* const* stg, const bf16* abase,
                                            const uint32_t* aoff, const bf16* const* bbase, const uint32_t* boff,
-                                           int nk, int wave, int wm, int wn, int lane) {
+                                           int nk, int wave, const FragOff& o) {
   const int r = nk % C::S;
-  if (r == 0) mainloop<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
-  else if (C::S > 1 && r == 1) mainloop<C, NB, 1 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
-  else if (C::S > 2 && r == 2) mainloop<C, NB, 2 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
-  else if (C::S > 3 && r == 3) mainloop<C, NB, 3 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
-  else if (C::S > 4 && r == 4) mainloop<C, NB, 4 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
-  else mainloop<C, NB, 5 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
+  if (r == 0) mainloop<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, nk, wave, o);
+  else if (C::S > 1 && r == 1) mainloop<C, NB, 1 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, o);
+  else if (C::S > 2 && r == 2) mainloop<C, NB, 2 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, o);
+  else if (C::S > 3 && r == 3) mainloop<C, NB, 3 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, o);
+  else if (C::S > 4 && r == 4) mainloop<C, NB, 4 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, o);
+  else mainloop<C, NB, 5 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, o);
 }
 
 template <class C, int MODE>
-__global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArgs f, int n_tiles_n) {
+__global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArgs f, int n_tiles_n, int super) {
   __shared__ __attribute__((aligned(1024))) bf16 s0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) bf16 s1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) bf16 s2[C::S > 2 ? C::STAGE : 8];
@@ -178,6 +208,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArg
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
+  const FragOff fo = frag_offsets<C>(wm, wn, lane);
 
   const int MT = f.plan[0];  // m-tiles: routed groups, then the shared expert
   const int total = MT * n_tiles_n;
@@ -187,9 +218,9 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArg
   for (int it = 0;; ++it) {
     const int t = it * G + xcd * (G >> 3) + slot;
     if (t >= total) break;
-    // supertile order: SUPER m-tiles x all n-tiles, m fastest
-    const int sbase = (t / (SUPER * n_tiles_n)) * SUPER;
-    const int grp = MT - sbase < SUPER ? MT - sbase : SUPER;
+    // supertile order: `super` m-tiles x all n-tiles, m fastest
+    const int sbase = (t / (super * n_tiles_n)) * super;
+    const int grp = MT - sbase < super ? MT - sbase : super;
     const int r = t - sbase * n_tiles_n;
     const int nt = r / grp;
     const int mt = sbase + r % grp;
@@ -268,40 +299,65 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArg
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // previous tile's loads and stores settled
     const int nk = K / BK;
     if constexpr (C::MI >= 4) {
-      if (nb >= 4) mainloop_r<C, 4>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
-      else if (nb == 3) mainloop_r<C, 3>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
-      else if (nb == 2) mainloop_r<C, 2>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
-      else mainloop_r<C, 1>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
+      if (nb >= 4) mainloop_r<C, 4>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo);
+      else if (nb == 3) mainloop_r<C, 3>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo);
+      else if (nb == 2) mainloop_r<C, 2>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo);
+      else mainloop_r<C, 1>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo);
     } else {
-      if (nb >= 2) mainloop_r<C, 2>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
-      else mainloop_r<C, 1>(acc, stg, abase, aoff, bbase, boff, nk, wave, wm, wn, lane);
+      if (nb >= 2) mainloop_r<C, 2>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo);
+      else mainloop_r<C, 1>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo);
     }
 
-    // ---- epilogue: C lane layout col = lane%32, row 8*(v/4) + 4*(lane/32) + v%4 ----
+    // ---- epilogue through LDS ----
+    // The tile leaves in M bands of WM*32 rows: band ii (M-blocks WM*ii ..
+    // WM*ii + WM-1) goes, as bf16 (gate/up: SiLU(g)*u), into stage buffer ii,
+    // then every thread stores whole 16-byte row chunks.  C lane layout of a
+    // 32x32 block: col = lane%32, row 8*(v/4) + 4*(lane/32) + v%4.  Chunk c of
+    // band row r sits at c ^ (4 * ((r >> 2) & 1)), so the two half-waves'
+    // rows (4 apart) write different banks.
+    constexpr int CCOLS = MODE == 1 ? C::BN / 2 : C::BN;  // output columns of the tile
+    constexpr int CPR = CCOLS / 8;                        // 16-byte chunks per row
+    constexpr int BAND = C::WM * 32;
+    static_assert(C::MI <= C::S && BAND * CCOLS <= C::STAGE && CPR >= 8, "epilogue staging");
+    auto cpos = [&](int r, int col) { return r * CCOLS + ((((col >> 3) ^ (((r >> 2) & 1) << 2))) << 3) + (col & 7); };
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // trailing (redundant) direct loads have landed
+    block_sync();                              // every wave is done reading the stage buffers
 #pragma unroll
     for (int ii = 0; ii < C::MI; ++ii) {
-      const int mb = wm + C::WM * ii;
-      if (mb * 32 >= nrows) continue;
+      bf16* ct = stg[ii];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int rl = mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (rl >= nrows) continue;
-        const int64_t gr = base + r0 + rl;
-        if (MODE == 1) {
-          bf16* dst = shared ? reinterpret_cast<bf16*>(f.h_sh) + gr * f.Is : reinterpret_cast<bf16*>(f.h) + gr * f.I;
+        const int r = wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if constexpr (MODE == 1) {
 #pragma unroll
-          for (int jj = 0; jj < C::NJ / 2; ++jj) {
-            const int col = nt * (C::BN / 2) + wn * (C::CW / 2) + jj * 32 + (lane & 31);
-            if (col < Ncols) dst[col] = f2bf(silu(acc[ii][jj][v]) * acc[ii][jj + C::NJ / 2][v]);
-          }
+          for (int jj = 0; jj < C::NJ / 2; ++jj)
+            ct[cpos(r, wn * (C::CW / 2) + jj * 32 + (lane & 31))] =
+                f2bf(silu(acc[ii][jj][v]) * acc[ii][jj + C::NJ / 2][v]);
         } else {
-          bf16* dst = shared ? reinterpret_cast<bf16*>(f.y_sh) : reinterpret_cast<bf16*>(f.y);
 #pragma unroll
-          for (int jj = 0; jj < C::NJ; ++jj) {
-            const int col = nt * C::BN + wn * C::CW + jj * 32 + (lane & 31);
-            if (col < Ncols) dst[gr * f.H + col] = f2bf(acc[ii][jj][v]);
-          }
+          for (int jj = 0; jj < C::NJ; ++jj) ct[cpos(r, wn * C::CW + jj * 32 + (lane & 31))] = f2bf(acc[ii][jj][v]);
         }
+      }
+    }
+    block_sync();
+    bf16* obase;
+    int ld;
+    if (MODE == 1) {
+      obase = shared ? reinterpret_cast<bf16*>(f.h_sh) : reinterpret_cast<bf16*>(f.h);
+      ld = shared ? f.Is : f.I;
+    } else {
+      obase = shared ? reinterpret_cast<bf16*>(f.y_sh) : reinterpret_cast<bf16*>(f.y);
+      ld = f.H;
+    }
+#pragma unroll
+    for (int ii = 0; ii < C::MI; ++ii) {
+      const bf16* ct = stg[ii];
+      for (int q = tid; q < BAND * CPR; q += C::NT) {
+        const int r = q / CPR, c = q % CPR;
+        const int trow = ii * BAND + r;  // band ii holds tile rows ii*BAND ..
+        const int col = nt * CCOLS + c * 8;
+        if (trow < nrows && col < Ncols)
+          st16(obase + (int64_t)(base + r0 + trow) * ld + col, ld16(ct + cpos(r, c * 8)));
       }
     }
   }
@@ -324,8 +380,13 @@ hipError_t launch(const FfnArgs& a, int phase, hipStream_t s) {
   const int wide = a.I > a.Is ? a.I : a.Is;
   const int ntn = phase == 1 ? (wide + C::BN / 2 - 1) / (C::BN / 2) : (a.H + C::BN - 1) / C::BN;
   const int grid = (cu_count() * C::WG_PER_CU + 7) / 8 * 8;  // resident workgroups, a multiple of 8 XCDs
-  if (phase == 1) dma_gemm_kernel<C, 1><<<grid, C::NT, 0, s>>>(a, ntn);
-  else dma_gemm_kernel<C, 2><<<grid, C::NT, 0, s>>>(a, ntn);
+  // Each XCD takes grid/8 consecutive tiles: supertiles of 8 m-tiles, so an
+  // expert's weight slice serves up to 8 of its m-tiles from L2.  (Two
+  // m-tiles x all n-tiles per XCD, which fetches each A slice once, measured
+  // slower on the 8192-token skewed layer.)
+  const int super = 8;
+  if (phase == 1) dma_gemm_kernel<C, 1><<<grid, C::NT, 0, s>>>(a, ntn, super);
+  else dma_gemm_kernel<C, 2><<<grid, C::NT, 0, s>>>(a, ntn, super);
   return hipGetLastError();
 }
 

@@ -12,8 +12,9 @@
 // runs (each 16-byte-per-lane load covers 2 rows x 512 B), one batch of 256 K
 // values ahead in registers, and re-laid into MFMA fragments through a
 // wave-private LDS stage (no barriers).
-// fp8 codes stream through registers in batches of U K steps instead.  The
-// (at most 16) activation rows come from L2.
+// fp8 codes stream the same way in 256-byte runs (4 rows per load) and are
+// decoded with their block scale as fragments leave LDS.  The (at most 16)
+// activation rows come from L2.
 //   gate/up item: 16 hidden columns (16 gate rows + 16 up rows), SiLU*mul in registers
 //   down item   : 32 output columns (2 blocks of 16 W_down rows)
 //   router item : 16 router rows (the shared-gate row last) over one K chunk,
@@ -30,30 +31,17 @@ constexpr int KSTEP = 32;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Raw storage of one lane's 8 B-operand values: 16 bytes of bf16, or 8 bytes
-// of e4m3fn codes (decoded with the block scale right before the MFMA so the
-// load stays asynchronous).
-template <bool FP8>
-struct BRaw;
-template <>
-struct BRaw<false> {
-  u32x4 v;
-};
-template <>
-struct BRaw<true> {
-  u32x2 v;
-  float s;
-};
-
-// acc[j] += A[16 rows, kbeg..kend) x B_j[16 rows, kbeg..kend)^T for NB weight
-// blocks.  a_row: this lane's A row (row lane%16) or null (zero row);
-// b_row[j]: this lane's row of weight block j; s_row[j]: its fp8 scale row.
-// kq = 8*(lane/16) is the lane's K offset inside a 32-wide step.
-template <int NB, bool FP8>
-__device__ __forceinline__ void stream_dot(const bf16* a_row, const void* const* b_row, const float* const* s_row,
-                                           int kbeg, int kend, int kq, f32x4* acc) {
+// acc[j] += A[16 rows, kbeg..kend) x B_j[16 rows, kbeg..kend)^T for NB bf16
+// weight blocks, operands loaded straight into MFMA fragments (the small-batch
+// router).  a_row: this lane's A row (row lane%16) or null (zero row);
+// b_row[j]: this lane's row of weight block j.  kq = 8*(lane/16) is the
+// lane's K offset inside a 32-wide K step.  U K steps per batch, two batches
+// in flight.
+template <int NB>
+__device__ __forceinline__ void stream_dot(const bf16* a_row, const bf16* const* b_row, int kbeg, int kend, int kq,
+                                           f32x4* acc) {
   u32x4 av[2][U];
-  BRaw<FP8> bv[2][U][NB];
+  u32x4 bv[2][U][NB];
   const int nsteps = (kend - kbeg + KSTEP - 1) / KSTEP;
   auto load = [&](int buf, int s0) {
 #pragma unroll
@@ -62,27 +50,16 @@ __device__ __forceinline__ void stream_dot(const bf16* a_row, const void* const*
       const bool in = kk < kend;
       av[buf][u] = (in && a_row) ? ld16(a_row + kk) : u32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        if constexpr (FP8) {
-          bv[buf][u][j].v = in ? *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(b_row[j]) + kk)
-                               : u32x2{0, 0};
-          bv[buf][u][j].s = in ? s_row[j][kk / 128] : 0.f;
-        } else {
-          bv[buf][u][j].v = in ? ld16(reinterpret_cast<const bf16*>(b_row[j]) + kk) : u32x4{0, 0, 0, 0};
-        }
-      }
+      for (int j = 0; j < NB; ++j) bv[buf][u][j] = in ? ld16(b_row[j] + kk) : u32x4{0, 0, 0, 0};
     }
   };
   auto mma = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        u32x4 b;
-        if constexpr (FP8) b = fp8x8_to_bf16x8(bv[buf][u][j].v, bv[buf][u][j].s);
-        else b = bv[buf][u][j].v;
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[buf][u]), as_bf16x8(b), acc[j], 0, 0, 0);
-      }
+      for (int j = 0; j < NB; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[buf][u]), as_bf16x8(bv[buf][u][j]), acc[j],
+                                                         0, 0, 0);
   };
   load(0, 0);
   for (int s0 = 0; s0 < nsteps; s0 += 2 * U) {
@@ -193,10 +170,113 @@ __device__ __forceinline__ void stream_dot_lds(const bf16* a_row, const bf16* a_
   }
 }
 
+// ---- LDS-staged fp8 streaming ----------------------------------------------
+// Same scheme for e4m3fn codes: a batch holds SB8 = 256 K values (256 B) of
+// NB*16 weight rows; rows 2i and 2i+1 sit in 512 B at i * 528 B, odd rows
+// store chunk c at c ^ 8.  Each 16-byte-per-lane load covers 4 rows x 256
+// contiguous bytes.  Fragments are decoded when read from LDS: 8 codes times
+// the row's 128 x 128 block scale (s_row[j]: this lane's fragment row's scale
+// row, indexed by k / 128) to eight bf16.
+constexpr int SB8 = 256;
+constexpr int PAIR8 = 528;
+
+template <int NB>
+__device__ __forceinline__ void stream_dot_lds8(const bf16* a_row, const bf16* a_any, const uint8_t* const* wrow0,
+                                                const int* nvalid, int ldw, const float* const* s_row, int kbeg,
+                                                int kend, int lane, char* lds, f32x4* acc) {
+  constexpr int NL = NB * 4;       // weight loads per batch (4 rows each)
+  constexpr int NA = SB8 / KSTEP;  // activation loads per batch
+  const int kq = (lane >> 4) * 8;
+  const int q4 = lane >> 4;        // row of the quad this lane loads
+  const int c = lane & 15;         // its 16-byte chunk of the 256-byte run
+  const int nbatch = (kend - kbeg + SB8 - 1) / SB8;
+  const bf16* arow = a_row ? a_row : a_any;
+  u32x4 wb[NL];
+  u32x4 av[2][NA];
+  float sc[2][NB][2];  // block scales of this lane's fragment row, two 128-wide K blocks per batch
+  auto load_w = [&](int b) {
+    int k = kbeg + b * SB8 + c * 16;
+    k = k < kend ? k : kend - 16;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + q4 < nvalid[j] ? 4 * i + q4 : nvalid[j] - 1;
+        wb[j * 4 + i] = ld16(wrow0[j] + (uint32_t)(r * ldw + k));
+      }
+  };
+  auto load_a = [&](int x, int b) {
+#pragma unroll
+    for (int s = 0; s < NA; ++s) {
+      const int kk = kbeg + b * SB8 + s * KSTEP + kq;
+      av[x][s] = ld16(arow + (kk < kend ? kk : kend - 8));
+    }
+    const int kb = (kbeg + b * SB8) / 128;
+    const int kbl = (kend - 1) / 128;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      sc[x][j][0] = s_row[j][kb < kbl ? kb : kbl];
+      sc[x][j][1] = s_row[j][kb + 1 < kbl ? kb + 1 : kbl];
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + q4;
+        *reinterpret_cast<u32x4*>(lds + (j * 8 + (r >> 1)) * PAIR8 + (r & 1) * 256 + ((c ^ ((r & 1) << 3)) << 4)) =
+            wb[j * 4 + i];
+      }
+  };
+  auto compute = [&](int x, int b) {
+    const int n = lane & 15;
+    const int hn = n & 1;
+#pragma unroll
+    for (int s = 0; s < NA; ++s) {
+      const int kk = kbeg + b * SB8 + s * KSTEP + kq;
+      const u32x4 am = (a_row && kk < kend) ? av[x][s] : u32x4{0, 0, 0, 0};
+      const int byte = s * KSTEP + kq;  // offset in the 256-byte row run
+      const int cc = byte >> 4;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const u32x2 codes = *reinterpret_cast<const u32x2*>(lds + (j * 8 + (n >> 1)) * PAIR8 + hn * 256 +
+                                                            ((cc ^ (hn << 3)) << 4) + (byte & 15));
+        const u32x4 bv = fp8x8_to_bf16x8(codes, sc[x][j][s >= NA / 2 ? 1 : 0]);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(am), as_bf16x8(bv), acc[j], 0, 0, 0);
+      }
+    }
+  };
+  load_w(0);
+  load_a(0, 0);
+  int b = 0;
+  for (; b + 2 < nbatch; b += 2) {
+    stage();
+    load_w(b + 1);
+    load_a(1, b + 1);
+    compute(0, b);
+    stage();
+    load_w(b + 2);
+    load_a(0, b + 2);
+    compute(1, b + 1);
+  }
+  stage();
+  if (b + 1 < nbatch) {
+    load_w(b + 1);
+    load_a(1, b + 1);
+    compute(0, b);
+    stage();
+    compute(1, b + 1);
+  } else {
+    compute(0, b);
+  }
+}
+
 template <int PHASE, bool FP8>
-__global__ __launch_bounds__(WAVES * 64) void stream_kernel(FfnArgs f, int list_begin_idx, int list_end_idx) {
+__global__ __launch_bounds__(WAVES * 64, 2) void stream_kernel(FfnArgs f, int list_begin_idx, int list_end_idx) {
   constexpr int NB = 2;  // gate+up, or 2 down blocks
-  __shared__ __attribute__((aligned(16))) char stage[FP8 ? 16 : WAVES * NB * 8 * PAIR];
+  constexpr int STAGE_BYTES = NB * 8 * (FP8 ? PAIR8 : PAIR);  // per wave
+  __shared__ __attribute__((aligned(16))) char stage[WAVES * STAGE_BYTES];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int gw = blockIdx.x * WAVES + (threadIdx.x >> 6);
@@ -208,7 +288,6 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(FfnArgs f, int list_
   const int n_slabs = (wide + cols_per_item - 1) / cols_per_item;
   const int total = (sb_end - sb_begin) * n_slabs;
   const int m = lane & 15;         // A row / B column within a 16-block
-  const int kq = (lane >> 4) * 8;  // K offset of this lane inside a 32-wide K step
 
   for (int item = gw; item < total; item += nw) {
     const int sb = sb_begin + item / n_slabs;
@@ -222,7 +301,6 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(FfnArgs f, int list_
     const int Ncols = PHASE == 1 ? (shared ? f.Is : f.I) : f.H;
     const int c0 = slab * cols_per_item;
     if (c0 >= Ncols) continue;
-    const bool fp8 = FP8 && !shared;
 
     // A row of this lane (zero when past the group's rows)
     const bf16* a_row = nullptr;
@@ -235,36 +313,20 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(FfnArgs f, int list_
                        : reinterpret_cast<const bf16*>(f.h) + (int64_t)gr * f.I;
       }
     }
-    // B rows of this lane, one per 16-column block
-    const void* b_row[NB];
+    // fp8: this lane's fragment row's block-scale row, one per 16-column block
     const float* s_row[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      int col = PHASE == 1 ? c0 + m : c0 + j * 16 + m;
-      col = col < Ncols ? col : Ncols - 1;
       s_row[j] = nullptr;
-      if (PHASE == 1) {
-        const bool up = j == 1;
-        if (shared) {
-          b_row[j] = reinterpret_cast<const bf16*>(up ? f.shu : f.shg) + (int64_t)col * f.H;
-        } else if (fp8) {
-          b_row[j] = reinterpret_cast<const uint8_t*>(up ? f.wu : f.wg) + (int64_t)g * (up ? f.su : f.sg) +
-                     (int64_t)col * f.H;
+      if (FP8) {
+        int col = PHASE == 1 ? c0 + m : c0 + j * 16 + m;
+        col = col < Ncols ? col : Ncols - 1;
+        if (PHASE == 1) {
           const int kb = f.H / 128;
-          s_row[j] = (up ? f.scu : f.scg) + (int64_t)g * (f.I / 128) * kb + (col / 128) * kb;
+          s_row[j] = (j ? f.scu : f.scg) + (int64_t)g * (f.I / 128) * kb + (col / 128) * kb;
         } else {
-          b_row[j] = reinterpret_cast<const bf16*>(up ? f.wu : f.wg) + (int64_t)g * (up ? f.su : f.sg) +
-                     (int64_t)col * f.H;
-        }
-      } else {
-        if (shared) {
-          b_row[j] = reinterpret_cast<const bf16*>(f.shd) + (int64_t)col * f.Is;
-        } else if (fp8) {
-          b_row[j] = reinterpret_cast<const uint8_t*>(f.wd) + (int64_t)g * f.sd + (int64_t)col * f.I;
           const int kb = f.I / 128;
           s_row[j] = f.scd + (int64_t)g * (f.H / 128) * kb + (col / 128) * kb;
-        } else {
-          b_row[j] = reinterpret_cast<const bf16*>(f.wd) + (int64_t)g * f.sd + (int64_t)col * f.I;
         }
       }
     }
@@ -273,11 +335,24 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(FfnArgs f, int list_
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (FP8) {
-      if (fp8) {
-        stream_dot<NB, true>(a_row, b_row, s_row, 0, K, kq, acc);
-      } else {
-        stream_dot<NB, false>(a_row, b_row, s_row, 0, K, kq, acc);
+      // (an fp8 launch covers the routed groups only; the shared expert's
+      // bf16 weights go through the bf16 launch)
+      // first row and valid-row count of each 16-row weight block, and this
+      // lane's fragment row's scale row
+      const uint8_t* w0[NB];
+      int nv[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        int first = PHASE == 1 ? c0 : c0 + j * 16;
+        first = first < Ncols ? first : Ncols - 1;
+        nv[j] = Ncols - first;
+        const uint8_t* mat = PHASE == 1
+                                 ? reinterpret_cast<const uint8_t*>(j ? f.wu : f.wg) + (int64_t)g * (j ? f.su : f.sg)
+                                 : reinterpret_cast<const uint8_t*>(f.wd) + (int64_t)g * f.sd;
+        w0[j] = mat + (int64_t)first * K;
       }
+      const bf16* a_any = reinterpret_cast<const bf16*>(PHASE == 1 ? f.x : f.h);
+      stream_dot_lds8<NB>(a_row, a_any, w0, nv, K, s_row, 0, K, lane, stage + wave * STAGE_BYTES, acc);
     } else {
       // first row and valid-row count of each 16-row weight block
       const bf16* w0[NB];
@@ -297,7 +372,7 @@ __global__ __launch_bounds__(WAVES * 64) void stream_kernel(FfnArgs f, int list_
         w0[j] = mat + (int64_t)first * K;
       }
       const bf16* a_any = reinterpret_cast<const bf16*>(PHASE == 1 ? f.x : (shared ? f.h_sh : f.h));
-      stream_dot_lds<NB>(a_row, a_any, w0, nv, K, 0, K, lane, stage + wave * NB * 8 * PAIR, acc);
+      stream_dot_lds<NB>(a_row, a_any, w0, nv, K, 0, K, lane, stage + wave * STAGE_BYTES, acc);
     }
 
     // C fragment: lane holds column (lane & 15), rows 4*(lane>>4) + i.
@@ -349,9 +424,8 @@ __global__ __launch_bounds__(RW * 64) void router_stream_kernel(const bf16* __re
     const bf16* a_row = m < T ? x + (int64_t)m * H : nullptr;
     int n = slab * 16 + m;
     n = n < N ? n : N - 1;
-    const void* b_row[1] = {n < E ? wr + (int64_t)n * H : wsg};
-    const float* s_row[1] = {nullptr};
-    stream_dot<1, false>(a_row, b_row, s_row, kbeg, kend, kq, acc);
+    const bf16* b_row[1] = {n < E ? wr + (int64_t)n * H : wsg};
+    stream_dot<1>(a_row, b_row, kbeg, kend, kq, acc);
   }
   part[w][lane] = acc[0];
   __syncthreads();

@@ -212,6 +212,15 @@ def test_fp8_small_with_and_without_shared(shared):
         check(p, run_stages(p, flags))
 
 
+@pytest.mark.parametrize("flags", [0, lib.MOE_FLAG_FORCE_STREAM])
+def test_fp8_streaming_several_batches(flags):
+    # H = 1024: four 256-wide K batches and eight 128-wide scale blocks per
+    # gate/up row; I = 384: the down rows end in half a batch
+    cfg = CONFIGS["max_fp8"].with_(name="fp8_stream", T=24, H=1024, E=6, k=2, I=384, I_shared=128)
+    p = gpu_problem(cfg, 10)
+    check(p, run_stages(p, flags))
+
+
 def test_fused_gate_up_strides():
     cfg = CONFIGS["flash_prefill"].with_(name="fused", T=64, H=128, E=6, k=2, I=64, I_shared=0)
     p = gpu_problem(cfg, 8)
