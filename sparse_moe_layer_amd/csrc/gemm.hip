@@ -17,6 +17,8 @@
 // m-tile x n-tile indices, so no host sync is needed to size it.
 // fp8 routed weights are decoded (OCP e4m3fn x fp32 block scale -> bf16) on
 // their way into LDS.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -194,66 +196,70 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(FfnArgs f, RouterArgs ra, i
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    u32x4 ra_reg[4], rb_reg[4];
-    float rs_reg[2];
+    // fp8 weights: two register stages, the loads of K step kt+2 are issued
+    // while step kt computes from LDS and step kt+1's registers are decoded
+    // into LDS, so two steps' loads are in flight per workgroup (past the last
+    // step the loads repeat it, never stored).  bf16: one register stage.
+    u32x4 ra_reg[2][4], rb_reg[2][4];
+    float rs_reg[2][2];
     const int kcol = tid & 7;
     const int nk = (K - kbeg + BK - 1) / BK;
 
-    auto gload = [&](int kt) {
+    auto gload = [&](int kt, int rb) {
+      kt = kt < nk ? kt : nk - 1;
       const int k0 = kbeg + kt * BK;
+      // loads are unconditional (address clamped into the row, value zeroed
+      // past K) so that no branch splits the load stream
+      const int kk = k0 + kcol * 8;
+      const bool kin = kk < K;
+      const int kc = kin ? kk : K - 8;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int kk = k0 + kcol * 8;
-        ra_reg[i] = kk < K ? ld16(a_ptr[i] + kk) : u32x4{0, 0, 0, 0};
+        const u32x4 v = ld16(a_ptr[i] + kc);
+        ra_reg[rb][i] = kin ? v : u32x4{0, 0, 0, 0};
       }
       if (fp8_tile) {
         const int kk = k0 + (tid & 3) * 16;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          rb_reg[i] = ld16(reinterpret_cast<const uint8_t*>(b_ptr[i]) + kk);
-          rs_reg[i] = s_ptr[i][k0 / 128];
+          rb_reg[rb][i] = ld16(reinterpret_cast<const uint8_t*>(b_ptr[i]) + kk);
+          rs_reg[rb][i] = s_ptr[i][k0 / 128];
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int kk = k0 + kcol * 8;
-          rb_reg[i] = kk < K ? ld16(reinterpret_cast<const bf16*>(b_ptr[i]) + kk) : u32x4{0, 0, 0, 0};
+          const u32x4 v = ld16(reinterpret_cast<const bf16*>(b_ptr[i]) + kc);
+          rb_reg[rb][i] = kin ? v : u32x4{0, 0, 0, 0};
         }
       }
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](int buf, int rb) {
       bf16* a = sA + buf * BM * BK;
       bf16* b = sB + buf * BN * BK;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = (tid >> 3) + 32 * i;
-        *reinterpret_cast<u32x4*>(a + lds_off(r, kcol)) = ra_reg[i];
+        *reinterpret_cast<u32x4*>(a + lds_off(r, kcol)) = ra_reg[rb][i];
       }
       if (fp8_tile) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int r = (tid >> 2) + 64 * i;
           const int c = (tid & 3) * 2;
-          u32x2 lo = {rb_reg[i][0], rb_reg[i][1]};
-          u32x2 hi = {rb_reg[i][2], rb_reg[i][3]};
-          *reinterpret_cast<u32x4*>(b + lds_off(r, c)) = fp8x8_to_bf16x8(lo, rs_reg[i]);
-          *reinterpret_cast<u32x4*>(b + lds_off(r, c + 1)) = fp8x8_to_bf16x8(hi, rs_reg[i]);
+          u32x2 lo = {rb_reg[rb][i][0], rb_reg[rb][i][1]};
+          u32x2 hi = {rb_reg[rb][i][2], rb_reg[rb][i][3]};
+          *reinterpret_cast<u32x4*>(b + lds_off(r, c)) = fp8x8_to_bf16x8(lo, rs_reg[rb][i]);
+          *reinterpret_cast<u32x4*>(b + lds_off(r, c + 1)) = fp8x8_to_bf16x8(hi, rs_reg[rb][i]);
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = (tid >> 3) + 32 * i;
-          *reinterpret_cast<u32x4*>(b + lds_off(r, kcol)) = rb_reg[i];
+          *reinterpret_cast<u32x4*>(b + lds_off(r, kcol)) = rb_reg[rb][i];
         }
       }
     };
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nk) gload(kt + 1);
+    auto compute = [&](int buf) {
       const bf16* a = sA + buf * BM * BK;
       const bf16* b = sB + buf * BN * BK;
 #pragma unroll
@@ -276,8 +282,52 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(FfnArgs f, RouterArgs ra, i
           for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
-      if (kt + 1 < nk) lstore(buf ^ 1);
+    };
+    // step kt computes from LDS buffer kt%2 == P, refills register stage P
+    // with step kt+2 and moves register stage 1-P (step kt+1) into LDS.
+    auto step = [&](int kt, auto P) {
+      constexpr int p = decltype(P)::value;
+      gload(kt + 2, p);
+      compute(p);
+      if (kt + 1 < nk) lstore(1 - p, 1 - p);
       __syncthreads();
+    };
+
+    if constexpr (FP8) {
+      gload(0, 0);
+      gload(1, 1);
+      lstore(0, 0);
+      __syncthreads();
+      for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, std::integral_constant<int, 0>{});
+        if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
+      }
+    } else {
+      // bf16 weights: one register stage with loads guarded per lane (both
+      // measured faster for ~100-row groups than two stages or clamped loads)
+      auto gload1 = [&](int kt) {
+        const int k0 = kbeg + kt * BK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = k0 + kcol * 8;
+          ra_reg[0][i] = kk < K ? ld16(a_ptr[i] + kk) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = k0 + kcol * 8;
+          rb_reg[0][i] = kk < K ? ld16(reinterpret_cast<const bf16*>(b_ptr[i]) + kk) : u32x4{0, 0, 0, 0};
+        }
+      };
+      gload1(0);
+      lstore(0, 0);
+      __syncthreads();
+      for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) gload1(kt + 1);
+        compute(buf);
+        if (kt + 1 < nk) lstore(buf ^ 1, 0);
+        __syncthreads();
+      }
     }
 
     // ---------------- epilogue ----------------
