@@ -18,7 +18,8 @@
 // explicit s_waitcnt vmcnt + s_barrier.  A stage holds a 32-wide K slice,
 // [row][4 chunks of 16 B], chunk c of row r at position c ^ ((r >> 2) & 3):
 // a half-wave's 16-byte fragment reads cover 16 rows and 64 banks span four
-// 64-byte rows, so the XOR spreads them over all banks.  Each lane's direct
+// 64-byte rows, so the XOR spreads them over all banks.  (The template also
+// takes a 64-wide K step: 8 chunks per 128-byte row, XOR (r >> 1) & 7.)  Each lane's direct
 // load fetches the global chunk that belongs at its LDS position, so global
 // reads stay whole 64-byte row segments.
 //
@@ -32,21 +33,22 @@
 namespace moe {
 namespace {
 
-constexpr int BK = 32;     // K per pipeline stage (64-byte rows)
 
-template <int BM_, int BN_, int WM_, int WN_, int S_, int WG_PER_CU_>
+template <int BM_, int BN_, int WM_, int WN_, int S_, int WG_PER_CU_, int BK_ = 32>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_, BK = BK_;
+  static constexpr int RPL = 512 / BK;  // rows one 1 KB direct load fills
   static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int WAVES_PER_EU = NW * WG_PER_CU_ / 4;
   static constexpr int WG_PER_CU = WG_PER_CU_;
   static constexpr int MI = BM / (32 * WM);  // M-blocks per wave
   static constexpr int NJ = BN / (32 * WN);  // N-blocks per wave
   static constexpr int CW = NJ * 32;         // B tile rows per wave column
-  static constexpr int LA = BM / (16 * NW);  // A direct loads per lane per stage
-  static constexpr int LB = BN / (16 * NW);  // B direct loads per lane per stage
+  static constexpr int LA = BM / (RPL * NW);  // A direct loads per lane per stage
+  static constexpr int LB = BN / (RPL * NW);  // B direct loads per lane per stage
   static constexpr int L = LA + LB;
   static constexpr int STAGE = (BM + BN) * BK;  // elements per stage buffer
+  static_assert(BK == 32 || BK == 64, "K step");
   static_assert(MI >= 1 && NJ >= 2 && NJ % 2 == 0 && LA >= 1 && LB >= 1, "tiling");
   static_assert(S >= 2 && S <= 6 && L * (S - 2) < 64, "pipeline depth");
   static_assert(S * STAGE * 2 * WG_PER_CU_ <= 160 * 1024, "LDS");
@@ -65,7 +67,12 @@ __device__ __forceinline__ void block_sync() {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ int lds_pos(int r, int c) { return r * BK + ((c ^ ((r >> 2) & 3)) << 3); }
+// Chunk c of row r: 4 chunks per 64-byte row XOR (r >> 2) & 3, or 8 per
+// 128-byte row XOR (r >> 1) & 7 (16 rows of one chunk hit 16 bank groups).
+template <int BK>
+__device__ __forceinline__ int swz(int r) { return BK == 32 ? (r >> 2) & 3 : (r >> 1) & 7; }
+template <int BK>
+__device__ __forceinline__ int lds_pos(int r, int c) { return r * BK + ((c ^ swz<BK>(r)) << 3); }
 
 // The direct loads of one K step into one stage buffer: load i of wave w
 // fills 16 rows (NW*i + w)*16 .. +16 (1 KB) of the A part, then of the B part.
@@ -75,7 +82,7 @@ __device__ __forceinline__ void issue_stage(bf16* st, const bf16* abase, const u
 #pragma unroll
   for (int i = 0; i < C::LA; ++i) dma16(abase + (aoff[i] + k0), st + (C::NW * i + wave) * 512);
 #pragma unroll
-  for (int i = 0; i < C::LB; ++i) dma16(bbase[i] + (boff[i] + k0), st + C::BM * BK + (C::NW * i + wave) * 512);
+  for (int i = 0; i < C::LB; ++i) dma16(bbase[i] + (boff[i] + k0), st + C::BM * C::BK + (C::NW * i + wave) * 512);
 }
 
 // Element offsets of this lane's fragment reads inside a stage for K sub-step
@@ -83,17 +90,17 @@ __device__ __forceinline__ void issue_stage(bf16* st, const bf16* abase, const u
 // swizzled.  Block ii / jj adds a whole number of 32-row blocks, so every
 // fragment read is one of these plus a compile-time offset.
 struct FragOff {
-  int a[2], b[2];
+  int a[4], b[4];  // per 16-wide K sub-step of a stage
 };
 
 template <class C>
 __device__ __forceinline__ FragOff frag_offsets(int wm, int wn, int lane) {
   FragOff o;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
+  for (int ks = 0; ks < C::BK / 16; ++ks) {
     const int c = ks * 2 + (lane >> 5);
-    o.a[ks] = lds_pos(wm * 32 + (lane & 31), c);
-    o.b[ks] = lds_pos(C::BM + wn * C::CW + (lane & 31), c);
+    o.a[ks] = lds_pos<C::BK>(wm * 32 + (lane & 31), c);
+    o.b[ks] = lds_pos<C::BK>(C::BM + wn * C::CW + (lane & 31), c);
   }
   return o;
 }
@@ -102,10 +109,10 @@ template <class C, int NB>
 __device__ __forceinline__ void load_frags(const bf16* st, int ks, const FragOff& o, bf16x8* af, bf16x8* bfr) {
 #pragma unroll
   for (int ii = 0; ii < NB; ++ii)
-    af[ii] = *reinterpret_cast<const bf16x8*>(st + o.a[ks] + ii * C::WM * 32 * BK);
+    af[ii] = *reinterpret_cast<const bf16x8*>(st + o.a[ks] + ii * C::WM * 32 * C::BK);
 #pragma unroll
   for (int jj = 0; jj < C::NJ; ++jj)
-    bfr[jj] = *reinterpret_cast<const bf16x8*>(st + o.b[ks] + jj * 32 * BK);
+    bfr[jj] = *reinterpret_cast<const bf16x8*>(st + o.b[ks] + jj * 32 * C::BK);
 }
 
 // MFMAs of one stage: 2 K sub-steps of 16, fragments of both loaded first.
@@ -114,7 +121,7 @@ __device__ __forceinline__ void compute_stage(f32x16 (&acc)[C::MI][C::NJ], const
   if constexpr (C::MI * C::NJ > 8) {
     // 128 x 128 wave tiles: one K sub-step of fragments at a time
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    for (int ks = 0; ks < C::BK / 16; ++ks) {
       bf16x8 af[NB], bfr[C::NJ];
       load_frags<C, NB>(st, ks, o, af, bfr);
 #pragma unroll
@@ -124,11 +131,11 @@ __device__ __forceinline__ void compute_stage(f32x16 (&acc)[C::MI][C::NJ], const
           acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ii], bfr[jj], acc[ii][jj], 0, 0, 0);
     }
   } else {
-    bf16x8 af[2][NB], bfr[2][C::NJ];
-    load_frags<C, NB>(st, 0, o, af[0], bfr[0]);
-    load_frags<C, NB>(st, 1, o, af[1], bfr[1]);
+    bf16x8 af[C::BK / 16][NB], bfr[C::BK / 16][C::NJ];
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks)
+    for (int ks = 0; ks < C::BK / 16; ++ks) load_frags<C, NB>(st, ks, o, af[ks], bfr[ks]);
+#pragma unroll
+    for (int ks = 0; ks < C::BK / 16; ++ks)
 #pragma unroll
       for (int ii = 0; ii < NB; ++ii)
 #pragma unroll
@@ -147,7 +154,7 @@ __device__ __forceinline__ void step(f32x16 (&acc)[C::MI][C::NJ], bf16* const* s
                                      uint32_t klast, int wave, const FragOff& o) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((C::S - 2) * C::L));
   block_sync();
-  const uint32_t kn = (uint32_t)(s + C::S - 1) * BK;
+  const uint32_t kn = (uint32_t)(s + C::S - 1) * C::BK;
   issue_stage<C>(stg[(B + C::S - 1) % C::S], abase, aoff, bbase, boff, kn < klast ? kn : klast, wave);
   compute_stage<C, NB>(acc, stg[B], o);
 }
@@ -157,13 +164,13 @@ template <class C, int NB, int R>
 __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::MI][C::NJ], bf16* const* stg, const bf16* abase,
                                          const uint32_t* aoff, const bf16* const* bbase, const uint32_t* boff,
                                          int nk, int wave, const FragOff& o) {
-  const uint32_t klast = (uint32_t)(nk - 1) * BK;
+  const uint32_t klast = (uint32_t)(nk - 1) * C::BK;
   // every wave's loads (vmcnt(0) before the call) and LDS reads of the
   // previous tile are finished before its buffers are refilled
   block_sync();
 #pragma unroll
   for (int st = 0; st < C::S - 1; ++st) {
-    const uint32_t k0 = (uint32_t)st * BK;
+    const uint32_t k0 = (uint32_t)st * C::BK;
     issue_stage<C>(stg[st], abase, aoff, bbase, boff, k0 < klast ? k0 : klast, wave);
   }
   const int nfull = nk - R;
@@ -242,11 +249,13 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArg
     if (nt * ncov >= Ncols) continue;
 
     // ---- sources of the direct loads of each K step ----
-    // lane l of a load fills row +l/4 of its 16-row group at position l%4,
-    // so it fetches global chunk (l%4) ^ ((row>>2)&3) = (l%4) ^ ((l>>4)&3).
-    // Bases are wave-uniform (SGPRs); lanes carry 32-bit element offsets.
-    const int lrow = lane >> 2;
-    const int gchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    // load i of wave w fills rows (NW*i + w)*RPL .. +RPL of its part; lane l
+    // lands at row +l/(BK/8), position l%(BK/8), so it fetches the global
+    // chunk that belongs there: position ^ swz(row).  Bases are wave-uniform
+    // (SGPRs); lanes carry 32-bit element offsets.
+    constexpr int LPR = C::BK / 8;  // lanes per row
+    const int lrow = lane / LPR;
+    const int lpos = lane % LPR;
     const bf16* abase;
     if (MODE == 1) abase = reinterpret_cast<const bf16*>(f.x);
     else abase = shared ? reinterpret_cast<const bf16*>(f.h_sh) : reinterpret_cast<const bf16*>(f.h);
@@ -254,8 +263,9 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArg
     const bf16* bbase[C::LB];
 #pragma unroll
     for (int i = 0; i < C::LA; ++i) {
-      int rr = (C::NW * i + wave) * 16 + lrow;
-      rr = rr < nrows ? rr : nrows - 1;
+      const int row = (C::NW * i + wave) * C::RPL + lrow;
+      const int gchunk = lpos ^ swz<C::BK>(row);
+      const int rr = row < nrows ? row : nrows - 1;
       const int gr = base + r0 + rr;
       if (MODE == 1) {
         int tok = shared ? gr : f.sorted[gr] / f.k;
@@ -267,13 +277,14 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArg
     }
 #pragma unroll
     for (int i = 0; i < C::LB; ++i) {
-      const int grp16 = (C::NW * i + wave) * 16;  // wave-uniform first row of the load
-      const int n = grp16 + lrow;                 // B tile row
+      const int grow0 = (C::NW * i + wave) * C::RPL;  // wave-uniform first row of the load
+      const int n = grow0 + lrow;                       // B tile row
+      const int gchunk = lpos ^ swz<C::BK>(n);
       int col;
       if (MODE == 1) {
         // wave column wc (CW rows) holds CW/2 gate rows, then the up rows of
         // the same CW/2 hidden columns
-        const bool up = (grp16 % C::CW) >= C::CW / 2;
+        const bool up = (grow0 % C::CW) >= C::CW / 2;
         col = nt * (C::BN / 2) + (n / C::CW) * (C::CW / 2) + (n % (C::CW / 2));
         bbase[i] = shared ? reinterpret_cast<const bf16*>(up ? f.shu : f.shg)
                           : reinterpret_cast<const bf16*>(up ? f.wu : f.wg) + (int64_t)g * (up ? f.su : f.sg);
@@ -297,7 +308,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArg
     const int nblk_tile = (nrows + 31) / 32;
     const int nb = (nblk_tile - wm + C::WM - 1) / C::WM;
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // previous tile's loads and stores settled
-    const int nk = K / BK;
+    const int nk = K / C::BK;
     if constexpr (C::MI >= 4) {
       if (nb >= 4) mainloop_r<C, 4>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo);
       else if (nb == 3) mainloop_r<C, 3>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo);
@@ -393,7 +404,8 @@ hipError_t launch(const FfnArgs& a, int phase, hipStream_t s) {
 }  // namespace
 
 bool ffn_dma_supported(const FfnArgs& a) {
-  return !a.fp8 && a.H % BK == 0 && a.I % BK == 0 && (a.Is == 0 || a.Is % BK == 0);
+  constexpr int k = BigCfg::BK;
+  return !a.fp8 && a.H % k == 0 && a.I % k == 0 && (a.Is == 0 || a.Is % k == 0);
 }
 
 hipError_t launch_ffn_gemm_dma(const FfnArgs& a, int phase, hipStream_t s) { return launch<BigCfg>(a, phase, s); }
