@@ -36,14 +36,14 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="flash_prefill", choices=WORKLOADS)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--gemm-tile", default="auto", choices=["auto", "128", "256"],
                     help="pin the MFMA GEMM kernel (A/B runs); default picks by rows per expert")
     ap.add_argument("--path", default="auto", choices=["auto", "gemm", "stream"],
                     help="pin every expert to one path (A/B runs); default picks per expert by rows")
-    ap.add_argument("--cpu-tokens", type=int, default=192,
+    ap.add_argument("--cpu-tokens", type=int, default=1024,
                     help="tokens of the same workload the CPU oracle runs on (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scale factor for HBM byte counters)")

@@ -321,21 +321,23 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArg
 
     // ---- epilogue through LDS ----
     // The tile leaves in M bands of WM*32 rows: band ii (M-blocks WM*ii ..
-    // WM*ii + WM-1) goes, as bf16 (gate/up: SiLU(g)*u), into stage buffer ii,
-    // then every thread stores whole 16-byte row chunks.  C lane layout of a
+    // WM*ii + WM-1) goes, as bf16 (gate/up: SiLU(g)*u), into the stage
+    // buffers (BPS bands each), then every thread stores whole 16-byte row
+    // chunks.  C lane layout of a
     // 32x32 block: col = lane%32, row 8*(v/4) + 4*(lane/32) + v%4.  Chunk c of
     // band row r sits at c ^ (4 * ((r >> 2) & 1)), so the two half-waves'
     // rows (4 apart) write different banks.
     constexpr int CCOLS = MODE == 1 ? C::BN / 2 : C::BN;  // output columns of the tile
     constexpr int CPR = CCOLS / 8;                        // 16-byte chunks per row
     constexpr int BAND = C::WM * 32;
-    static_assert(C::MI <= C::S && BAND * CCOLS <= C::STAGE && CPR >= 8, "epilogue staging");
+    constexpr int BPS = C::STAGE / (BAND * CCOLS);        // bands per stage buffer
+    static_assert(BPS >= 1 && C::MI <= C::S * BPS && CPR >= 8, "epilogue staging");
     auto cpos = [&](int r, int col) { return r * CCOLS + ((((col >> 3) ^ (((r >> 2) & 1) << 2))) << 3) + (col & 7); };
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // trailing (redundant) direct loads have landed
     block_sync();                              // every wave is done reading the stage buffers
 #pragma unroll
     for (int ii = 0; ii < C::MI; ++ii) {
-      bf16* ct = stg[ii];
+      bf16* ct = stg[ii / BPS] + (ii % BPS) * BAND * CCOLS;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
@@ -362,7 +364,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArg
     }
 #pragma unroll
     for (int ii = 0; ii < C::MI; ++ii) {
-      const bf16* ct = stg[ii];
+      const bf16* ct = stg[ii / BPS] + (ii % BPS) * BAND * CCOLS;
       for (int q = tid; q < BAND * CPR; q += C::NT) {
         const int r = q / CPR, c = q % CPR;
         const int trow = ii * BAND + r;  // band ii holds tile rows ii*BAND ..
