@@ -44,10 +44,17 @@ def expert_weights_fn(problem):
     return get
 
 
-def ensure_margin(problem, min_margin: float = 1e-3, adjacent: bool = True, max_attempts: int = 64):
-    """Redraw token rows of x until every token's sorted fp32 logits have gaps
-    >= min_margin between consecutive ranks 1..k+1 (adjacent=True) or between
-    ranks k and k+1.  Uses the oracle's router; returns the number of redraws."""
+def ensure_margin(problem, min_margin: float = 1e-3, adjacent: bool = True, max_attempts: int = 64,
+                  page: bool = False, min_midpoint: float = 1e-4):
+    """Redraw token rows of x until every token's routing is decided with room
+    to spare against the GPU's own fp32 logit rounding (~1e-6):
+
+    page=False: the sorted fp32 logits have gaps >= min_margin between
+    consecutive ranks 1..k+1 (adjacent=True) or between ranks k and k+1;
+    page=True : the fp32 logits of the experts that can decide the bf16-rounded
+    top-k lie >= min_midpoint from every bf16 rounding boundary.
+
+    Uses the oracle's router; returns the number of redraws."""
     c = problem.cfg
     wr = _dec(problem, problem.w_router, c.act)
     redraws = 0
@@ -55,7 +62,10 @@ def ensure_margin(problem, min_margin: float = 1e-3, adjacent: bool = True, max_
     for _ in range(max_attempts + 1):
         x = moe.decode(problem.host_raw(problem.x[rows] if len(rows) < c.T else problem.x), c.act)
         l32 = moe.to_fp32(moe.router_logits(x, wr))
-        bad = rows[moe.margins(l32, c.k, adjacent) < min_margin]
+        if page:
+            bad = rows[moe.bf16_midpoint_distance(l32, c.k) < min_midpoint]
+        else:
+            bad = rows[moe.margins(l32, c.k, adjacent) < min_margin]
         if bad.size == 0:
             return redraws
         attempts = [problem.x_attempts.get(int(t), 0) + 1 for t in bad]
@@ -67,8 +77,10 @@ def ensure_margin(problem, min_margin: float = 1e-3, adjacent: bool = True, max_
     raise RuntimeError("margin fix-up did not converge")
 
 
-def forward(problem, tokens=None):
-    """Oracle forward pass of the problem; see moe.moe_forward."""
+def forward(problem, tokens=None, page: bool = False):
+    """Oracle forward pass of the problem; see moe.moe_forward.  page: the
+    section's bf16 routing numerics (a no-op for fp32 layers, whose activation
+    dtype is fp32)."""
     x, wr, shared, sg = dense_inputs(problem)
     return moe.moe_forward(x, wr, problem.cfg.k, expert_weights_fn(problem), problem.cfg.E,
-                           shared, sg, tokens)
+                           shared, sg, tokens, page=page and problem.cfg.act == "bf16")

@@ -119,6 +119,15 @@ def to_fp32(a: np.ndarray) -> np.ndarray:
     return np.asarray(a, np.float64).astype(np.float32).astype(np.float64)
 
 
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """Round to bfloat16 (the activation dtype), back in fp64: the value is
+    first taken to fp32, then its low 16 bits are rounded away to nearest,
+    ties to even (add 0x7FFF plus the lowest kept bit, truncate)."""
+    u = np.asarray(a, np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def softmax(logits: np.ndarray) -> np.ndarray:
     """p[t, e] = exp(l[t,e] - max_e l) / sum_e exp(l[t,e] - max_e l) over all E."""
     m = logits.max(axis=1, keepdims=True)
@@ -145,12 +154,22 @@ def renormalised_weights(probs: np.ndarray, ids: np.ndarray) -> np.ndarray:
     return sel / sel.sum(axis=1, keepdims=True)
 
 
-def route(x: np.ndarray, w_router: np.ndarray, k: int):
-    """Router -> top-k + normalise.  Returns (fp32-rounded logits, ids, w)."""
-    l32 = to_fp32(router_logits(x, w_router))
-    ids = topk_ids(l32, k)
-    w = renormalised_weights(softmax(l32), ids)
-    return l32, ids, w
+def route(x: np.ndarray, w_router: np.ndarray, k: int, page: bool = False):
+    """Router -> top-k + normalise.  Returns (logits the selection used, ids, w).
+
+    page=False: fp32 logits, full-precision mixing weights.
+    page=True : the section's stated numerics for a bf16 model: the softmax
+    runs on the logits rounded to the activation dtype, and the mixing
+    weights are cast to the activation dtype.  Rounded logits tie often;
+    ties go to the lower expert id."""
+    l = to_fp32(router_logits(x, w_router))
+    if page:
+        l = round_bf16(l)
+    ids = topk_ids(l, k)
+    w = renormalised_weights(softmax(l), ids)
+    if page:
+        w = round_bf16(w)
+    return l, ids, w
 
 
 def margins(l32: np.ndarray, k: int, adjacent: bool = True) -> np.ndarray:
@@ -164,6 +183,28 @@ def margins(l32: np.ndarray, k: int, adjacent: bool = True) -> np.ndarray:
     if adjacent:
         return gaps.min(axis=1)
     return gaps[:, -1] if kk == k + 1 else np.full(l32.shape[0], np.inf)
+
+
+def bf16_midpoint_distance(l32: np.ndarray, k: int) -> np.ndarray:
+    """Per token, the smallest distance from an fp32 logit to a bf16 rounding
+    boundary, over the experts that can decide the page-numerics top-k: every
+    expert whose rounded logit is within 2^-7 (relative; at least one bf16
+    step) of the (k+1)-th largest rounded logit, or above it.  Two fp32
+    evaluations of a logit that differ by less than this distance round to
+    the same bf16 value.  The boundaries around a bf16 value are the fp32
+    numbers whose bit patterns are its own plus and minus 0x8000 (half a bf16
+    step; this holds across binade edges too)."""
+    T, E = l32.shape
+    r = round_bf16(l32)
+    out = np.full(T, np.inf)
+    for t in range(T):
+        v = -np.sort(-r[t])[min(k, E - 1)]
+        crit = np.nonzero(r[t] >= v - max(abs(v), 2.0 ** -126) * 2.0 ** -7)[0]
+        u = r[t, crit].astype(np.float32).view(np.uint32).astype(np.int64)
+        mids = np.concatenate([(u + 0x8000), (u - 0x8000)]).astype(np.uint32).view(np.float32).astype(np.float64)
+        vals = np.concatenate([l32[t, crit], l32[t, crit]])
+        out[t] = np.abs(vals - mids).min()
+    return out
 
 
 # ----------------------------------------------------------------------------
@@ -241,16 +282,19 @@ def combine(y: np.ndarray, w: np.ndarray, y_shared: Optional[np.ndarray] = None,
 
 def moe_forward(x: np.ndarray, w_router: np.ndarray, k: int, expert_weights: ExpertFn,
                 E: Optional[int] = None, shared: Optional[Tuple[np.ndarray, np.ndarray, np.ndarray]] = None,
-                sh_gate_w: Optional[np.ndarray] = None, tokens: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                sh_gate_w: Optional[np.ndarray] = None, tokens: Optional[np.ndarray] = None,
+                page: bool = False) -> Dict[str, np.ndarray]:
     """The whole layer on fp64 inputs.  Routing and dispatch cover all T tokens;
     the expert math and combine cover `tokens` (default: all).
 
-    Returns logits (fp32-rounded), ids, w, counts, offsets, sorted_assign,
+    page: the routing numerics of `route(page=True)`.
+
+    Returns logits (as the selection used them), ids, w, counts, offsets, sorted_assign,
     assign_pos, shared_logit, gamma, y (routed outputs [T',k,H]),
     y_shared [T',H] and out [T',H] for the rows in `tokens`."""
     x = np.asarray(x, np.float64)
     E = w_router.shape[0] if E is None else E
-    l32, ids, w = route(x, w_router, k)
+    l32, ids, w = route(x, w_router, k, page)
     counts, offsets, sorted_assign, assign_pos = dispatch(ids, E)
     if tokens is None:
         tokens = np.arange(x.shape[0])

@@ -327,3 +327,50 @@ def test_zero_gate_row_zeroes_hidden_column():
     wd_masked = wd.copy()
     wd_masked[:, 1] = 123.0  # whatever column 1 of W_down holds cannot matter
     assert np.allclose(moe.swiglu(x, wg, wu, wd), moe.swiglu(x, wg, wu, wd_masked), rtol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# Page-exact routing numerics (Flash-Next MoE section: fp32 softmax on logits
+# rounded to the activation dtype, mixing weights cast to the activation dtype)
+# ----------------------------------------------------------------------------
+def test_round_bf16_matches_torch_and_ties_to_even():
+    rng = np.random.default_rng(5)
+    v = np.concatenate([rng.normal(size=100000) * 10.0 ** rng.integers(-8, 8, size=100000),
+                        rng.standard_cauchy(size=100000)]).astype(np.float32).astype(np.float64)
+    ref = torch.tensor(v, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(moe.round_bf16(v), ref)
+    # halfway cases go to the even neighbour: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7
+    assert moe.round_bf16(1 + 2.0 ** -8) == 1.0
+    assert moe.round_bf16(1 + 3 * 2.0 ** -8) == 1 + 2.0 ** -6
+    assert moe.round_bf16(-(1 + 2.0 ** -8)) == -1.0
+
+
+def test_page_routing_ties_and_rounded_weights():
+    # W_r = identity, so the logits are x itself (4 experts, k = 2)
+    x = np.array([[1.0, 1.0 + 2.0 ** -10, 0.25, -1.0]])
+    wr = np.eye(4)
+    _, ids, w = moe.route(x, wr, 2)
+    assert ids.tolist() == [[1, 0]]            # fp32 logits: 1 + 2^-10 ranks first
+    l, ids_p, w_p = moe.route(x, wr, 2, page=True)
+    assert l[0, 1] == 1.0                       # 1 + 2^-10 rounds to 1 in bf16: a tie
+    assert ids_p.tolist() == [[0, 1]]           # the tie goes to the lower id
+    assert w_p.tolist() == [[0.5, 0.5]]
+    # rounded logits one apart: weights sigmoid(1) and 1 - sigmoid(1), each
+    # rounded to bf16 (8 significant bits: steps 2^-8 in [0.5, 1), 2^-9 in [0.25, 0.5))
+    x2 = np.array([[2.0, 1.0, -3.0]])
+    _, ids2, w2 = moe.route(x2, np.eye(3), 2, page=True)
+    assert ids2.tolist() == [[0, 1]]
+    s = 1.0 / (1.0 + np.exp(-1.0))
+    assert w2[0, 0] == np.round(s / 2.0 ** -8) * 2.0 ** -8 == 0.73046875
+    assert w2[0, 1] == np.round((1 - s) / 2.0 ** -9) * 2.0 ** -9 == 0.26953125
+
+
+def test_bf16_midpoint_distance():
+    # logit 1 + 2^-8 + 1e-5 sits 1e-5 above the boundary between 1 and 1 + 2^-7
+    l = np.array([[1.0 + 2.0 ** -8 + 1e-5, -2.0, -3.0]])
+    d = moe.bf16_midpoint_distance(moe.to_fp32(l), 1)
+    assert abs(d[0] - 1e-5) < 1e-7
+    # a bf16 value itself: half a step to either side; below 1 the step is
+    # 2^-8, so the nearest boundary is 1 - 2^-9
+    d2 = moe.bf16_midpoint_distance(np.array([[1.0, -2.0, -3.0]]), 1)
+    assert d2[0] == 2.0 ** -9
