@@ -100,6 +100,13 @@ typedef struct {
  * otherwise the 128-row kernel runs whatever the flag says.  For A/B tests. */
 #define MOE_FLAG_GEMM_TILE_128 (1u << 2)
 #define MOE_FLAG_GEMM_TILE_256 (1u << 3)
+/* Routing numerics of the Qwen3.8-Flash-Next study, MoE section, for bf16
+ * layers: the softmax and top-k run on the router logits rounded to bf16
+ * (equal rounded logits go to the lower expert id), and the renormalised
+ * mixing weights are rounded to bf16 (returned in the fp32 topk_w).  Without
+ * the flag the logits and weights stay fp32.  No effect on fp32 layers (their
+ * activation dtype is fp32) or on the shared expert's gate logit. */
+#define MOE_FLAG_PAGE_ROUTING (1u << 4)
 
 /* Weights.  Layouts follow PyTorch Linear (out x in), which matches the GGUF
  * shapes on the Qwen3.8-2.4T-A95B hub discussion's zero-fraction table

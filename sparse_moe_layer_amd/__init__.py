@@ -13,7 +13,7 @@ from typing import Optional
 import torch
 
 from ._lib import (LIB, MOE_BF16, MOE_F32, MOE_FLAG_FORCE_GEMM, MOE_FLAG_FORCE_STREAM,  # noqa: F401
-                   MOE_FLAG_GEMM_TILE_128, MOE_FLAG_GEMM_TILE_256, MOE_FP8_E4M3FN, MOE_OK, EXPORTS, moe_problem, moe_weights)
+                   MOE_FLAG_GEMM_TILE_128, MOE_FLAG_GEMM_TILE_256, MOE_FLAG_PAGE_ROUTING, MOE_FP8_E4M3FN, MOE_OK, EXPORTS, moe_problem, moe_weights)
 
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3FN}
 

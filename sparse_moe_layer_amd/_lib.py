@@ -20,6 +20,7 @@ MOE_FLAG_FORCE_GEMM = 1
 MOE_FLAG_FORCE_STREAM = 2
 MOE_FLAG_GEMM_TILE_128 = 4
 MOE_FLAG_GEMM_TILE_256 = 8
+MOE_FLAG_PAGE_ROUTING = 16
 
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_validate", "moe_workspace_bytes", "moe_route",
            "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",

@@ -120,7 +120,8 @@ moe_status check_problem(const moe_problem* p) {
   const int64_t q = f32 ? 4 : 8;  // 16-byte vectors along every K-contiguous row
   if (p->H % q || p->I % q || p->I_shared % q) return MOE_ERR_UNSUPPORTED;
   if (fp8 && (p->scale_block != 128 || p->H % 128 || p->I % 128)) return MOE_ERR_UNSUPPORTED;
-  const uint32_t known = MOE_FLAG_FORCE_GEMM | MOE_FLAG_FORCE_STREAM | MOE_FLAG_GEMM_TILE_128 | MOE_FLAG_GEMM_TILE_256;
+  const uint32_t known = MOE_FLAG_FORCE_GEMM | MOE_FLAG_FORCE_STREAM | MOE_FLAG_GEMM_TILE_128 | MOE_FLAG_GEMM_TILE_256 |
+                         MOE_FLAG_PAGE_ROUTING;
   if (p->flags & ~known) return MOE_ERR_UNSUPPORTED;
   if ((p->flags & MOE_FLAG_FORCE_GEMM) && (p->flags & MOE_FLAG_FORCE_STREAM)) return MOE_ERR_UNSUPPORTED;
   if ((p->flags & MOE_FLAG_GEMM_TILE_128) && (p->flags & MOE_FLAG_GEMM_TILE_256)) return MOE_ERR_UNSUPPORTED;
@@ -181,7 +182,8 @@ moe_status do_route(const moe_problem* p, const void* x, const void* w_router, c
     e = moe::launch_router_logits_bf16(x, w_router, wsg, partial, T, H, E, rp.nsplit, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(
-      moe::launch_topk(partial, rp.nsplit, E + (wsg ? 1 : 0), T, E, k, wsg ? 1 : 0, ids, w, sl, s));
+      moe::launch_topk(partial, rp.nsplit, E + (wsg ? 1 : 0), T, E, k, wsg ? 1 : 0,
+                       p->act_dtype == MOE_BF16 && (p->flags & MOE_FLAG_PAGE_ROUTING), ids, w, sl, s));
 }
 
 FfnArgs ffn_args(const moe_problem* p, const moe_weights* w, const void* x, const int32_t* offsets,

@@ -52,7 +52,9 @@ hipError_t launch_router_stream(const void* x, const void* w_router, const void*
                                 int H, int E, hipStream_t s);
 hipError_t launch_router_logits_f32(const float* x, const float* w_router, const float* w_sg,
                                     float* logits, int T, int H, int E, hipStream_t s);
-hipError_t launch_topk(const float* partial, int nsplit, int ldl, int T, int E, int k, int has_sg,
+// page: round the logits to bf16 before the top-k and the mixing weights to
+// bf16 after renormalising (the page's routing numerics for bf16 layers).
+hipError_t launch_topk(const float* partial, int nsplit, int ldl, int T, int E, int k, int has_sg, bool page,
                        int32_t* ids, float* w, float* shared_logit, hipStream_t s);
 size_t dispatch_ws_ints(int64_t T, int64_t E);
 hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* offsets,

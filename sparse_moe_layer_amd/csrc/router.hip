@@ -11,7 +11,9 @@
 // order; lane j keeps round j's winner.  The renormalised weight of the j-th
 // pick is exp(l_j - l_0) / sum_{j'<k} exp(l_j' - l_0), which equals the
 // selected softmax probabilities divided by their sum (the full softmax's
-// normaliser cancels).  Also the fp32 SIMT router used for fp32 layers.
+// normaliser cancels).  With the section's routing numerics for bf16 layers
+// the logits are rounded to bf16 first (ties become common) and the weights
+// are rounded to bf16 last.  Also the fp32 SIMT router used for fp32 layers.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -56,7 +58,7 @@ __device__ __forceinline__ void wave_key_max(uint32_t& hi, uint32_t& lo) {
 
 template <int PER_LANE>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ partial, int nsplit, int ldl, int T,
-                                                   int E, int k, int has_sg, int32_t* __restrict__ ids,
+                                                   int E, int k, int has_sg, int page, int32_t* __restrict__ ids,
                                                    float* __restrict__ w, float* __restrict__ shared_logit) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -71,6 +73,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
     float a = 0.f;
     if (e < E)
       for (int c = 0; c < nsplit; ++c) a += row[c * cstride + e];
+    if (page) a = bf2f(f2bf(a));  // logits in the activation dtype (round to nearest even)
     khi[i] = e < E ? ord(a) : 0u;
     klo[i] = ~(uint32_t)e;
   }
@@ -93,8 +96,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
   const float ex = lane < k ? expf(unord(sel_hi) - top) : 0.f;
   const float sum = wave_sum(ex);
   if (lane < k) {
+    const float wj = ex / sum;
     ids[(int64_t)t * k + lane] = (int32_t)~sel_lo;
-    w[(int64_t)t * k + lane] = ex / sum;
+    w[(int64_t)t * k + lane] = page ? bf2f(f2bf(wj)) : wj;  // mixing weight in the activation dtype
   }
   if (has_sg && lane == 0) {
     float a = 0.f;
@@ -119,11 +123,12 @@ __global__ void router_f32_kernel(const float* __restrict__ x, const float* __re
 
 }  // namespace
 
-hipError_t launch_topk(const float* partial, int nsplit, int ldl, int T, int E, int k, int has_sg, int32_t* ids,
-                       float* w, float* shared_logit, hipStream_t s) {
+hipError_t launch_topk(const float* partial, int nsplit, int ldl, int T, int E, int k, int has_sg, bool page,
+                       int32_t* ids, float* w, float* shared_logit, hipStream_t s) {
   const int grid = (T + 3) / 4;
   const int per = (E + 63) / 64;
-#define MOE_TOPK(P) topk_kernel<P><<<grid, 256, 0, s>>>(partial, nsplit, ldl, T, E, k, has_sg, ids, w, shared_logit)
+#define MOE_TOPK(P) \
+  topk_kernel<P><<<grid, 256, 0, s>>>(partial, nsplit, ldl, T, E, k, has_sg, page ? 1 : 0, ids, w, shared_logit)
   if (per <= 1) MOE_TOPK(1);
   else if (per <= 2) MOE_TOPK(2);
   else if (per <= 4) MOE_TOPK(4);

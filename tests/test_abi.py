@@ -73,7 +73,9 @@ OK = _lib.MOE_OK
     (dict(flags=12), _lib.MOE_ERR_UNSUPPORTED),
     (dict(flags=5), OK),
     (dict(flags=10), OK),
-    (dict(flags=16), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(flags=16), OK),
+    (dict(flags=21), OK),
+    (dict(flags=32), _lib.MOE_ERR_UNSUPPORTED),
     (dict(T=2 ** 31 // 4), _lib.MOE_ERR_SHAPE),
     (dict(T=2 ** 24, H=256), _lib.MOE_ERR_UNSUPPORTED),  # T*k*H elements >= 2^31
 ])
