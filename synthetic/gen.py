@@ -348,3 +348,42 @@ def make_problem(cfg, seed: int = 0, device="cpu", **kw) -> Problem:
     if isinstance(cfg, str):
         cfg = CONFIGS[cfg]
     return Problem(cfg, seed, device, **kw)
+
+
+# ----------------------------------------------------------------------------
+# Gated residual around a sublayer (Qwen3.8-Flash-Next study, "Gated residual:
+# four streams, one sublayer input"): four residual streams of width H, a
+# per-stream RMSNorm gain, a rank-r read-gate bottleneck and four write gates.
+# ----------------------------------------------------------------------------
+T_GR_R, T_GR_NW, T_GR_RD, T_GR_UP, T_GR_F = 13, 14, 15, 16, 17
+
+
+class GRProblem:
+    """resid  [T, 4, H] act   the four residual streams
+    norm_w [4, H]     act   RMSNorm gain of each stream (1 + 0.1 N(0,1))
+    w_read [r+4, 4H]  act   rows 0..r-1: the read bottleneck's down projection,
+                            rows r..r+3: the four write-gate projections
+    w_up   [4H, r]    act   the read bottleneck's up projection
+    f      [T, H]     act   a sublayer output to write back
+    Weights ~ N(0, 0.02), streams and f ~ N(0, 1); eps is the model config's
+    rms_norm_eps (1e-6, model-atlas page, raw config)."""
+
+    def __init__(self, T: int, H: int, rank: int = 320, seed: int = 0, device="cpu", act: str = "bf16"):
+        self.T, self.H, self.rank, self.seed, self.act = T, H, rank, seed, act
+        self.eps = 1e-6
+        self.device = torch.device(device)
+        dev = self.device
+        self.resid = to_storage(normals([stream_key(seed, T_GR_R, t) for t in range(T)], 4 * H, dev), act).reshape(T, 4, H)
+        self.norm_w = to_storage(1.0 + 0.1 * normals([stream_key(seed, T_GR_NW)], 4 * H, dev).reshape(4, H), act)
+        self.w_read = to_storage(normals([stream_key(seed, T_GR_RD)], (rank + 4) * 4 * H, dev).reshape(rank + 4, 4 * H)
+                                 * 0.02, act)
+        self.w_up = to_storage(normals([stream_key(seed, T_GR_UP)], 4 * H * rank, dev).reshape(4 * H, rank) * 0.02, act)
+        self.f = to_storage(normals([stream_key(seed, T_GR_F, t) for t in range(T)], H, dev), act)
+
+    def host(self, t: torch.Tensor) -> np.ndarray:
+        """Host fp64 copy of a stored tensor (exact: bf16 and fp32 convert exactly)."""
+        return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def make_gr_problem(T: int, H: int, rank: int = 320, seed: int = 0, device="cpu", act: str = "bf16") -> GRProblem:
+    return GRProblem(T, H, rank, seed, device, act)
