@@ -219,6 +219,42 @@ moe_status moe_layer_forward(const moe_problem* p, const moe_weights* w, const v
                              void* out, int32_t* topk_ids, float* topk_w,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Gated residual around the layer (Qwen3.8-Flash-Next study, "Gated residual:
+ * four streams, one sublayer input"): the persistent residual is four
+ * streams of width H; the layer reads one gated mean of them and writes its
+ * output back into each stream with a scalar gate.
+ *   Rhat_i = GroupRMSNorm(R_i)           (stream i alone: R_i / sqrt(mean R_i^2 + eps) * norm_w[i])
+ *   G      = sigmoid(W_up SiLU(W_down vec(Rhat) / 4))
+ *   x      = mean_i (G_i * Rhat_i),   s = 2 sigmoid(W_write vec(Rhat) / 4)
+ *   R'_i   = R_i + s_i F(x)              (F = the layer, e.g. moe_layer_forward)
+ * bf16 activations only (MOE_ERR_UNSUPPORTED otherwise); H a multiple of 32,
+ * rank a multiple of 16.  Uses p->T, p->H and p->act_dtype of the layer's
+ * problem.  All pointers device memory, 16-byte aligned, caller-owned.
+ * --------------------------------------------------------------------------- */
+typedef struct {
+  const void* norm_w; /* [4, H] bf16: RMSNorm gain of each stream                              */
+  const void* w_read; /* [rank + 4, 4H] bf16: rows 0..rank-1 W_down, rows rank..rank+3 W_write */
+  const void* w_up;   /* [4H, rank] bf16: the read gate's up projection                        */
+  int64_t rank;       /* read bottleneck width (320 in the study)                             */
+  float eps;          /* RMSNorm epsilon (rms_norm_eps 1e-6 in the model config)               */
+} moe_gr_weights;
+
+/* Scratch bytes moe_gr_read needs: Rhat [T, 4H] bf16, split-K partials of
+ * the read projection, the bottleneck activations [T, rank] bf16. */
+size_t moe_gr_workspace_bytes(const moe_problem* p, int64_t rank);
+
+/* resid [T, 4, H] bf16 (stream i at columns iH .. iH+H-1 of a token) ->
+ * x [T, H] bf16 (the layer's input) and s [T, 4] fp32 (write gates).
+ * Errors as moe_route (shapes, alignment, workspace) before any launch. */
+moe_status moe_gr_read(const moe_problem* p, const moe_gr_weights* g, const void* resid, void* x, float* s,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* resid_out [T, 4, H] = resid + s[:, i] * f (f [T, H] bf16, the layer's
+ * output); resid_out may alias resid. */
+moe_status moe_gr_write(const moe_problem* p, const void* resid, const float* s, const void* f, void* resid_out,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,7 +13,7 @@ from typing import Optional
 import torch
 
 from ._lib import (LIB, MOE_BF16, MOE_F32, MOE_FLAG_FORCE_GEMM, MOE_FLAG_FORCE_STREAM,  # noqa: F401
-                   MOE_FLAG_GEMM_TILE_128, MOE_FLAG_GEMM_TILE_256, MOE_FLAG_PAGE_ROUTING, MOE_FP8_E4M3FN, MOE_OK, EXPORTS, moe_problem, moe_weights)
+                   MOE_FLAG_GEMM_TILE_128, MOE_FLAG_GEMM_TILE_256, MOE_FLAG_PAGE_ROUTING, MOE_FP8_E4M3FN, MOE_OK, EXPORTS, moe_gr_weights, moe_problem, moe_weights)
 
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3FN}
 
@@ -108,3 +108,30 @@ def moe_combine(p, y, assign_pos, topk_w, y_shared, shared_logit, out, stream=No
 def moe_layer_forward(p, w: moe_weights, x, out, topk_ids, topk_w, ws, stream=None):
     _check(LIB.moe_layer_forward(ctypes.byref(p), ctypes.byref(w), _ptr(x), _ptr(out), _ptr(topk_ids),
                                  _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream)), "moe_layer_forward")
+
+
+def gr_weights(norm_w, w_read, w_up, rank: int, eps: float = 1e-6) -> moe_gr_weights:
+    return moe_gr_weights(_ptr(norm_w), _ptr(w_read), _ptr(w_up), rank, eps)
+
+
+def moe_gr_workspace_bytes(p: moe_problem, rank: int) -> int:
+    return LIB.moe_gr_workspace_bytes(ctypes.byref(p), rank)
+
+
+def gr_workspace(p: moe_problem, rank: int, device="cuda") -> torch.Tensor:
+    """A device buffer of moe_gr_workspace_bytes(p, rank) bytes."""
+    n = moe_gr_workspace_bytes(p, rank)
+    if n == 0:
+        st = LIB.moe_validate(ctypes.byref(p))
+        raise MoEError(st if st != MOE_OK else 6, "moe_gr_workspace_bytes")  # 6: MOE_ERR_UNSUPPORTED
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_gr_read(p, g: moe_gr_weights, resid, x, s, ws, stream=None):
+    _check(LIB.moe_gr_read(ctypes.byref(p), ctypes.byref(g), _ptr(resid), _ptr(x), _ptr(s), _ptr(ws), ws.numel(),
+                           _stream(stream)), "moe_gr_read")
+
+
+def moe_gr_write(p, resid, s, f, resid_out, stream=None):
+    _check(LIB.moe_gr_write(ctypes.byref(p), _ptr(resid), _ptr(s), _ptr(f), _ptr(resid_out), _stream(stream)),
+           "moe_gr_write")

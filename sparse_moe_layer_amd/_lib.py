@@ -24,7 +24,7 @@ MOE_FLAG_PAGE_ROUTING = 16
 
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_validate", "moe_workspace_bytes", "moe_route",
            "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",
-           "moe_layer_forward"]
+           "moe_layer_forward", "moe_gr_workspace_bytes", "moe_gr_read", "moe_gr_write"]
 
 
 class moe_problem(ctypes.Structure):
@@ -41,12 +41,18 @@ class moe_weights(ctypes.Structure):
                 ("sh_down", ctypes.c_void_p), ("sh_gate_w", ctypes.c_void_p)]
 
 
+class moe_gr_weights(ctypes.Structure):
+    _fields_ = [("norm_w", ctypes.c_void_p), ("w_read", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
+                ("rank", ctypes.c_int64), ("eps", ctypes.c_float)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python sparse_moe_layer_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(moe_problem)
     W = ctypes.POINTER(moe_weights)
+    G = ctypes.POINTER(moe_gr_weights)
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     sig = {
         "moe_abi_version": (i32, []),
@@ -60,6 +66,9 @@ def _load():
         "moe_expert_down": (i32, [P, W, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moe_combine": (i32, [P, vp, vp, vp, vp, vp, vp, vp]),
         "moe_layer_forward": (i32, [P, W, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_gr_workspace_bytes": (sz, [P, ctypes.c_int64]),
+        "moe_gr_read": (i32, [P, G, vp, vp, vp, vp, sz, vp]),
+        "moe_gr_write": (i32, [P, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -401,4 +401,49 @@ moe_status moe_layer_forward(const moe_problem* p, const moe_weights* w, const v
                                         (int)p->H, (int)p->k, p->act_dtype == MOE_F32 ? 1 : 0, s));
 }
 
+
+// ---------------------------------------------------------------------------
+// gated residual
+// ---------------------------------------------------------------------------
+static moe_status check_gr(const moe_problem* p, int64_t rank) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (p->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (p->H % 32 || rank < 16 || rank % 16 || rank > (1 << 16)) return MOE_ERR_UNSUPPORTED;
+  const int64_t lim = (int64_t)1 << 31;
+  if (p->T * 4 * p->H >= lim || (rank + 4) * 4 * p->H >= lim || p->T * (rank + 4) >= lim) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+size_t moe_gr_workspace_bytes(const moe_problem* p, int64_t rank) {
+  if (check_gr(p, rank) != MOE_OK) return 0;
+  return moe::gr_workspace_bytes(p->T, p->H, rank);
+}
+
+moe_status moe_gr_read(const moe_problem* p, const moe_gr_weights* g, const void* resid, void* x, float* s,
+                       void* ws, size_t ws_bytes, void* stream) {
+  if (!p || !g) return MOE_ERR_NULL;
+  moe_status st = check_gr(p, g->rank);
+  if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;
+  if (!g->norm_w || !g->w_read || !g->w_up || !resid || !x || !s || !ws) return MOE_ERR_NULL;
+  if (!al16(g->norm_w) || !al16(g->w_read) || !al16(g->w_up) || !al16(resid) || !al16(x) || !al16(s) ||
+      reinterpret_cast<uintptr_t>(ws) % kAlign)
+    return MOE_ERR_ALIGN;
+  if (ws_bytes < moe::gr_workspace_bytes(p->T, p->H, g->rank)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_gr_read(resid, g->norm_w, g->w_read, g->w_up, g->eps, (int)p->T, (int)p->H,
+                                        (int)g->rank, x, s, ws, (hipStream_t)stream));
+}
+
+moe_status moe_gr_write(const moe_problem* p, const void* resid, const float* s, const void* f, void* resid_out,
+                        void* stream) {
+  if (!p) return MOE_ERR_NULL;
+  moe_status st = check_gr(p, 16);
+  if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;
+  if (!resid || !s || !f || !resid_out) return MOE_ERR_NULL;
+  if (!al16(resid) || !al16(f) || !al16(resid_out) || reinterpret_cast<uintptr_t>(s) % 4) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_gr_write(resid, s, f, resid_out, (int)p->T, (int)p->H, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -73,4 +73,10 @@ hipError_t launch_combine(const void* y, const int32_t* pos, const float* w, con
                           const float* shared_logit, void* out, int T, int H, int k, int f32,
                           hipStream_t s);
 
+// Gated residual read / write (bf16).
+size_t gr_workspace_bytes(int64_t T, int64_t H, int64_t rank);
+hipError_t launch_gr_read(const void* resid, const void* norm_w, const void* w_read, const void* w_up, float eps,
+                          int T, int H, int rank, void* x, float* s, void* ws, hipStream_t st);
+hipError_t launch_gr_write(const void* resid, const float* s, const void* f, void* out, int T, int H, hipStream_t st);
+
 }  // namespace moe

@@ -355,7 +355,7 @@ def make_problem(cfg, seed: int = 0, device="cpu", **kw) -> Problem:
 # four streams, one sublayer input"): four residual streams of width H, a
 # per-stream RMSNorm gain, a rank-r read-gate bottleneck and four write gates.
 # ----------------------------------------------------------------------------
-T_GR_R, T_GR_NW, T_GR_RD, T_GR_UP, T_GR_F = 13, 14, 15, 16, 17
+T_GR_R, T_GR_NW, T_GR_RD, T_GR_UP, T_GR_F, T_GR_S = 13, 14, 15, 16, 17, 18
 
 
 class GRProblem:
@@ -365,6 +365,7 @@ class GRProblem:
                             rows r..r+3: the four write-gate projections
     w_up   [4H, r]    act   the read bottleneck's up projection
     f      [T, H]     act   a sublayer output to write back
+    s      [T, 4]     fp32  write gates for the write step alone (1 + 0.25 N(0,1))
     Weights ~ N(0, 0.02), streams and f ~ N(0, 1); eps is the model config's
     rms_norm_eps (1e-6, model-atlas page, raw config)."""
 
@@ -379,6 +380,7 @@ class GRProblem:
                                  * 0.02, act)
         self.w_up = to_storage(normals([stream_key(seed, T_GR_UP)], 4 * H * rank, dev).reshape(4 * H, rank) * 0.02, act)
         self.f = to_storage(normals([stream_key(seed, T_GR_F, t) for t in range(T)], H, dev), act)
+        self.s = 1.0 + 0.25 * normals([stream_key(seed, T_GR_S, t) for t in range(T)], 4, dev)
 
     def host(self, t: torch.Tensor) -> np.ndarray:
         """Host fp64 copy of a stored tensor (exact: bf16 and fp32 convert exactly)."""

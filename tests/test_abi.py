@@ -46,6 +46,8 @@ def test_struct_layout_matches_header():
     # 6 int64 + 3 int32 + 1 uint32 = 64 bytes; weights: 10 pointers + 3 int64 + 1 pointer
     assert ctypes.sizeof(_lib.moe_problem) == 64
     assert ctypes.sizeof(_lib.moe_weights) == 14 * 8
+    # gated residual weights: 3 pointers + int64 + float (+ 4 bytes of padding)
+    assert ctypes.sizeof(_lib.moe_gr_weights) == 40
 
 
 OK = _lib.MOE_OK
@@ -130,3 +132,35 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert L.moe_layer_forward(ctypes.byref(p0), ctypes.byref(
         _lib.moe_weights(fake, fake, fake, fake, 0, 0, 0, None, None, None, None, None, None, None)),
         fake, fake, None, None, fake, lib.moe_workspace_bytes(p0), None) == OK
+
+
+def test_gated_residual_entry_points_validate_before_any_launch():
+    L = _lib.LIB
+    fake = 1 << 20
+    p = lib.problem(64, 2560, 512, 10, 640, 640)
+    P = ctypes.byref(p)
+    wsz = lib.moe_gr_workspace_bytes(p, 320)
+    # Rhat [T, 4H] bf16 alone needs T * 4H * 2 bytes
+    assert wsz >= 64 * 4 * 2560 * 2 and wsz % 256 == 0
+    assert lib.moe_gr_workspace_bytes(lib.problem(4096, 2560, 512, 10, 640, 640), 320) > wsz
+    # unsupported: fp32 activations, H not a multiple of 32, rank not a multiple of 16
+    assert lib.moe_gr_workspace_bytes(lib.problem(64, 256, 16, 4, 128, 0, "f32", "f32"), 32) == 0
+    assert lib.moe_gr_workspace_bytes(lib.problem(64, 272, 16, 4, 128), 32) == 0
+    assert lib.moe_gr_workspace_bytes(p, 24) == 0
+    g = _lib.moe_gr_weights(fake, fake, fake, 320, 1e-6)
+    G = ctypes.byref(g)
+    assert L.moe_gr_read(P, None, fake, fake, fake, fake, wsz, None) == _lib.MOE_ERR_NULL
+    assert L.moe_gr_read(P, G, None, fake, fake, fake, wsz, None) == _lib.MOE_ERR_NULL
+    assert L.moe_gr_read(P, G, fake + 2, fake, fake, fake, wsz, None) == _lib.MOE_ERR_ALIGN
+    assert L.moe_gr_read(P, G, fake, fake, fake, fake + 16, wsz, None) == _lib.MOE_ERR_ALIGN
+    assert L.moe_gr_read(P, G, fake, fake, fake, fake, wsz - 1, None) == _lib.MOE_ERR_WORKSPACE
+    g24 = _lib.moe_gr_weights(fake, fake, fake, 24, 1e-6)
+    assert L.moe_gr_read(P, ctypes.byref(g24), fake, fake, fake, fake, wsz, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_gr_write(P, None, fake, fake, fake, None) == _lib.MOE_ERR_NULL
+    assert L.moe_gr_write(P, fake, fake + 2, fake, fake, None) == _lib.MOE_ERR_ALIGN
+    pf = lib.problem(64, 256, 16, 4, 128, 0, "f32", "f32")
+    assert L.moe_gr_write(ctypes.byref(pf), fake, fake, fake, fake, None) == _lib.MOE_ERR_UNSUPPORTED
+    # empty batch: valid no-op
+    p0 = lib.problem(0, 2560, 512, 10, 640, 640)
+    assert L.moe_gr_read(ctypes.byref(p0), G, None, None, None, None, 0, None) == OK
+    assert L.moe_gr_write(ctypes.byref(p0), None, None, None, None, None) == OK

@@ -14,13 +14,17 @@ def _rand(T=3, H=16, rank=5, seed=0):
 
 
 def test_group_rmsnorm_hand_example():
-    # stream [3, 4]: rms = sqrt((9 + 16) / 2) = sqrt(12.5); other streams zero
+    # stream [3, 4]: rms = sqrt((9 + 16) / 2) = sqrt(12.5); stream [1, -1]: rms 1
     r = np.zeros((1, 4, 2))
     r[0, 1] = [3.0, 4.0]
+    r[0, 0] = r[0, 2] = r[0, 3] = [1.0, -1.0]
     out = gr.group_rmsnorm(r, np.ones((4, 2)), 0.0)
     assert np.allclose(out[0, 1], [3 / np.sqrt(12.5), 4 / np.sqrt(12.5)], rtol=0, atol=1e-15)
+    assert np.array_equal(out[0, 0], [1.0, -1.0])
     # a zero stream stays zero (eps keeps the division finite)
-    assert np.all(gr.group_rmsnorm(r, np.ones((4, 2)), 1e-6)[0, 0] == 0.0)
+    rz = r.copy()
+    rz[0, 0] = 0.0
+    assert np.all(gr.group_rmsnorm(rz, np.ones((4, 2)), 1e-6)[0, 0] == 0.0)
     # the gain multiplies per channel
     g = np.array([[1, 1], [2, -1], [1, 1], [1, 1]], dtype=float)
     assert np.allclose(gr.group_rmsnorm(r, g, 0.0)[0, 1], [6 / np.sqrt(12.5), -4 / np.sqrt(12.5)])
