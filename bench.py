@@ -14,7 +14,9 @@ those events give the per-stage durations.
 Prints one JSON line: tokens/s for the whole step, the roofline of the
 dominant kernel (algorithmic bytes or FLOPs per launch over its event-timed
 duration), and the fp64 CPU oracle timed on a bounded sample of the same
-workload on this host's cores.
+workload on this host's cores.  For bf16 workloads it also reports the
+four-stream gated residual read and write around the layer at the same T and
+H (event-timed, with their own rooflines); they are not part of the step.
 """
 from __future__ import annotations
 
@@ -103,6 +105,43 @@ def cpu_baseline(problem, n_tokens):
             "sample": f"first {n} of {problem.cfg.T} tokens of the same workload, full layer "
                       f"(route, dispatch, every routed and shared expert, combine) in fp64 NumPy; "
                       f"{dt:.1f} s wall"}
+
+
+def gated_residual(lib, acc, args, cfg, dev, stream):
+    """The four-stream gated residual read and write around the layer at the
+    workload's T and H (read bottleneck width 320), each entry point timed
+    over --steps calls with HIP events on the launch stream.  Not part of the
+    step: the layer is the step."""
+    import torch
+    from synthetic import make_gr_problem
+
+    T, H, rank = cfg.T, cfg.H, 320
+    g = make_gr_problem(T, H, rank, seed=args.seed, device=dev)
+    P = lib.problem(T, H, cfg.E, cfg.k, cfg.I, cfg.I_shared, act="bf16", wdt=cfg.wdt)
+    G = lib.gr_weights(g.norm_w, g.w_read, g.w_up, rank, g.eps)
+    ws = lib.gr_workspace(P, rank)
+    x = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    s = torch.empty((T, 4), dtype=torch.float32, device=dev)
+    out = torch.empty_like(g.resid)
+    for _ in range(max(1, args.warmup)):
+        lib.moe_gr_read(P, G, g.resid, x, s, ws, stream)
+        lib.moe_gr_write(P, g.resid, g.s, g.f, out, stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        lib.moe_gr_read(P, G, g.resid, x, s, ws, stream)
+    ev[1].record(stream)
+    for _ in range(args.steps):
+        lib.moe_gr_write(P, g.resid, g.s, g.f, out, stream)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    t_read = ev[0].elapsed_time(ev[1]) / args.steps * 1e-3
+    t_write = ev[1].elapsed_time(ev[2]) / args.steps * 1e-3
+    fr, br = acc.gr_read_work(T, H, rank)
+    fw, bw = acc.gr_write_work(T, H)
+    return {"rank": rank,
+            "read_us": round(t_read * 1e6, 2), "read_roofline": acc.roofline(fr, br, t_read),
+            "write_us": round(t_write * 1e6, 2), "write_roofline": acc.roofline(fw, bw, t_write)}
 
 
 def main():
@@ -207,6 +246,8 @@ def main():
             "traffic": load_traffic(args.workload, kname), "kernel": kname,
             "algorithmic": {"flops": f_dom, "bytes": b_dom}}
 
+    gr = gated_residual(lib, acc, args, cfg, dev, stream) if cfg.act == "bf16" else None
+
     t_s = ms_step * 1e-3
     res = {
         "metric": METRIC,
@@ -230,6 +271,7 @@ def main():
                   "staged_ms": round(staged_ms, 4)},
         "stages_ms": {n: round(v, 4) for n, v in stage_ms.items()},
         "roofline": roof,
+        "gated_residual": gr,
     }
     if args.cpu_tokens > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

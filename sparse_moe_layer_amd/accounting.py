@@ -69,3 +69,31 @@ def layer_work(T, H, E, k, I, I_shared, act="bf16", wdt="bf16", touched=None, sc
     b_layer = w_gu + w_dn + sh_gu + sh_dn + E * H * a + (H * a if sh else 0) + x_b + 1.0 * T * H * a
     return Work(flops=f_router + f_gu + f_dn, bytes=b_layer, flops_gate_up=f_gu, bytes_gate_up=b_gu,
                 flops_down=f_dn, bytes_down=b_dn)
+
+
+def gr_read_work(T: int, H: int, rank: int):
+    """Gated residual read (Qwen3.8-Flash-Next study, "Gated residual: four
+    streams, one sublayer input"): FLOPs of the two projections
+    (vec(Rhat) [T, 4H] times [W_down; W_write]^T, then z [T, rank] times
+    W_up^T) and the bytes that must cross HBM (the four bf16 streams, the
+    gains, both weight matrices, x [T, H] bf16 and s [T, 4] fp32)."""
+    flops = 2.0 * T * 4 * H * (rank + 4) + 2.0 * T * rank * 4 * H
+    byts = 2.0 * (T * 4 * H + 4 * H + (rank + 4) * 4 * H + 4 * H * rank + T * H) + 4.0 * T * 4
+    return flops, byts
+
+
+def gr_write_work(T: int, H: int):
+    """Gated residual write R'_i = R_i + s_i F(x): read the four bf16 streams,
+    F(x) and s, write the four streams (the update has 2 FLOPs per element)."""
+    return 2.0 * T * 4 * H, 2.0 * (2 * T * 4 * H + T * H) + 4.0 * T * 4
+
+
+def roofline(flops: float, byts: float, seconds: float, mfma_peak: float = PEAK_BF16_TFLOPS) -> dict:
+    """Bound from the intensity against the ridge, then achieved / peak."""
+    if flops / byts > mfma_peak * 1e12 / (PEAK_HBM_GBPS * 1e9):
+        ach = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": round(ach / mfma_peak, 4)}
+    ach = byts / seconds / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBPS, 4)}

@@ -21,8 +21,11 @@ constexpr int kWave = 64;
 __device__ __forceinline__ float bf2f(bf16 v) { return (float)v; }
 __device__ __forceinline__ bf16 f2bf(float v) { return (bf16)v; }  // round to nearest even
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
-__device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// 1 / (1 + e^-z) with the hardware reciprocal (v_rcp_f32, about 1 ulp): the
+// argument is >= 1 (or +inf, whose reciprocal is 0), so no scaling is needed,
+// and it replaces the ten-instruction IEEE division in every epilogue.
+__device__ __forceinline__ float sigmoid(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+__device__ __forceinline__ float silu(float z) { return z * sigmoid(z); }
 
 // 16-byte global load / store helpers (addresses must be 16-byte aligned).
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }

@@ -64,6 +64,7 @@ def _check_read(g, x, s, rows):
     (1, 2560, RANK),
     (300, 96, 32),       # ragged token tiles (300 = 2 x 128 + 44), three column blocks
     (129, 2560, 16),     # one token past a tile, smallest bottleneck
+    (3, 8224, 16),       # wider than the 2.4T model (H = 8192)
 ])
 def test_gr_read_matches_oracle(T, H, rank):
     print(f"[gr] read T={T} H={H} rank={rank}", flush=True)
