@@ -389,3 +389,23 @@ class GRProblem:
 
 def make_gr_problem(T: int, H: int, rank: int = 320, seed: int = 0, device="cpu", act: str = "bf16") -> GRProblem:
     return GRProblem(T, H, rank, seed, device, act)
+
+
+T_AUD_W, T_AUD_M = 19, 20
+
+
+def make_audit_tensor(S: int, N: int, seed: int = 0, zero_frac: float = 0.0, std: float = 0.02,
+                      device="cpu") -> torch.Tensor:
+    """bf16 [S, N] weight-like tensor for the expert-weight audit: slice s is
+    drawn from its own stream, N(0, std), with entries set to exactly zero
+    with probability zero_frac (the discussion's table has 71.0% and 84.3%
+    zeros in early gate/up expert tensors)."""
+    out = torch.empty((S, N), dtype=torch.bfloat16, device=device)
+    thresh = int(round(zero_frac * 2 ** 32))
+    for s in range(S):
+        w32 = normals([stream_key(seed, T_AUD_W, s)], N, device).reshape(N) * std
+        if zero_frac > 0:
+            h = uniforms_u32([stream_key(seed, T_AUD_M, s)], N, device).reshape(N)
+            w32 = torch.where(h < thresh, torch.zeros_like(w32), w32)
+        out[s] = w32.to(torch.bfloat16)
+    return out
