@@ -16,7 +16,8 @@ dominant kernel (algorithmic bytes or FLOPs per launch over its event-timed
 duration), and the fp64 CPU oracle timed on a bounded sample of the same
 workload on this host's cores.  For bf16 workloads it also reports the
 four-stream gated residual read and write around the layer at the same T and
-H (event-timed, with their own rooflines); they are not part of the step.
+H, and the expert-weight audit of the layer's gate tensor (event-timed, with
+their own rooflines); they are not part of the step.
 """
 from __future__ import annotations
 
@@ -144,6 +145,36 @@ def gated_residual(lib, acc, args, cfg, dev, stream):
             "write_us": round(t_write * 1e6, 2), "write_roofline": acc.roofline(fw, bw, t_write)}
 
 
+def weight_audit(lib, acc, args, prob, stream):
+    """The expert-weight audit (zero count and sigma_rob per expert and over
+    the tensor) of the workload's own routed gate tensor [E, I, H], timed
+    over --steps calls with HIP events on the launch stream; not part of the
+    step."""
+    import torch
+
+    w = prob.w_gate
+    E = w.shape[0]
+    n = w[0].numel()
+    stats = lib.audit_stats_buffer(E)
+    ws = lib.audit_workspace(E)
+    flat = w.reshape(-1)
+    for _ in range(max(1, args.warmup)):
+        lib.moe_weight_audit(flat, E, n, n, stats, ws, stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        lib.moe_weight_audit(flat, E, n, n, stats, ws, stream)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    t = ev[0].elapsed_time(ev[1]) / args.steps * 1e-3
+    whole = lib.audit_records(stats)[E]
+    byts = acc.audit_work(E * n)
+    return {"tensor": "w_gate", "slices": E, "values_per_slice": n, "us": round(t * 1e6, 2),
+            "roofline": acc.roofline(0.0, byts, t),
+            "whole": {"zero_frac": whole["n_zero"] / whole["n"], "median": whole["median"],
+                      "sigma_rob": whole["sigma_rob"]}}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -247,6 +278,7 @@ def main():
             "algorithmic": {"flops": f_dom, "bytes": b_dom}}
 
     gr = gated_residual(lib, acc, args, cfg, dev, stream) if cfg.act == "bf16" else None
+    audit = weight_audit(lib, acc, args, prob, stream) if cfg.wdt == "bf16" else None
 
     t_s = ms_step * 1e-3
     res = {
@@ -272,6 +304,7 @@ def main():
         "stages_ms": {n: round(v, 4) for n, v in stage_ms.items()},
         "roofline": roof,
         "gated_residual": gr,
+        "weight_audit": audit,
     }
     if args.cpu_tokens > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -255,6 +255,42 @@ moe_status moe_gr_read(const moe_problem* p, const moe_gr_weights* g, const void
 moe_status moe_gr_write(const moe_problem* p, const void* resid, const float* s, const void* f, void* resid_out,
                         void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Expert-weight audit (model-hub discussion "singular matrices in
+ * Qwen3.8-2.4T-A95B"): for a bf16 weight tensor cut into `slices` equal
+ * slices (e.g. one per expert of an [E, I, H] tensor), the number of exact
+ * zeros (the discussion's "zer%" column) and the robust spread
+ *   sigma_rob = 1.4826 * median(|w_i - median(w)|)
+ * of each slice and of the whole tensor.  The median of an even count is the
+ * mean of the two middle values; both signed zeros are zeros; a NaN in a set
+ * (or an empty set) makes its median, mad and sigma_rob NaN.  The statistics
+ * are exact: every value is one of the 65536 bf16 patterns, so the kernels
+ * count patterns and derive the order statistics from the counts, in fp64.
+ * --------------------------------------------------------------------------- */
+typedef struct moe_audit_stats {
+  int64_t n;        /* values in the set                                      */
+  int64_t n_zero;   /* values equal to 0 (+0 or -0)                           */
+  int64_t n_nan;    /* NaN values                                             */
+  double median;    /* median of the values                                   */
+  double mad;       /* median of |w - median|                                 */
+  double sigma_rob; /* 1.4826 * mad                                           */
+} moe_audit_stats;
+
+/* Scratch bytes of moe_weight_audit: one 65536-bin uint32 histogram per
+ * slice and one uint64 histogram of the whole tensor.  0 if slices < 1 or
+ * slices > 65535. */
+size_t moe_audit_workspace_bytes(int64_t slices);
+
+/* w: device, dtype MOE_BF16 (MOE_ERR_UNSUPPORTED otherwise); slice s is the
+ * n contiguous values at w + s * slice_stride (elements; slice_stride >= n).
+ * stats: device, [slices + 1] records, caller-owned: the slices in order,
+ * then the whole tensor.  1 <= slices <= 65535 and n < 2^32 (MOE_ERR_SHAPE
+ * otherwise); w 2-byte aligned, stats 8-byte aligned, ws 256-byte aligned
+ * (MOE_ERR_ALIGN).  n == 0 is valid (every record then has n = 0 and NaN
+ * statistics).  Errors are reported before any launch. */
+moe_status moe_weight_audit(const void* w, int32_t dtype, int64_t slices, int64_t n, int64_t slice_stride,
+                            moe_audit_stats* stats, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -40,8 +40,9 @@ def audit_values(w: np.ndarray) -> dict:
     if n == 0 or n_nan:
         med = mad = np.nan
     else:
-        med = float(np.median(v))
-        mad = float(np.median(np.abs(v - med)))
+        with np.errstate(invalid="ignore"):  # inf - inf where the median is infinite: NaN, as defined
+            med = float(np.median(v))
+            mad = float(np.median(np.abs(v - med)))
     sig = SIGMA_ROB_SCALE * mad
     return {"n": n, "n_zero": n_zero, "n_nan": n_nan, "median": med, "mad": mad, "sigma_rob": sig,
             "zero_frac": n_zero / n if n else np.nan}

@@ -13,7 +13,8 @@ from typing import Optional
 import torch
 
 from ._lib import (LIB, MOE_BF16, MOE_F32, MOE_FLAG_FORCE_GEMM, MOE_FLAG_FORCE_STREAM,  # noqa: F401
-                   MOE_FLAG_GEMM_TILE_128, MOE_FLAG_GEMM_TILE_256, MOE_FLAG_PAGE_ROUTING, MOE_FP8_E4M3FN, MOE_OK, EXPORTS, moe_gr_weights, moe_problem, moe_weights)
+                   MOE_FLAG_GEMM_TILE_128, MOE_FLAG_GEMM_TILE_256, MOE_FLAG_PAGE_ROUTING, MOE_FP8_E4M3FN, MOE_OK, EXPORTS, moe_audit_stats, moe_gr_weights, moe_problem,
+                   moe_weights)
 
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3FN}
 
@@ -135,3 +136,40 @@ def moe_gr_read(p, g: moe_gr_weights, resid, x, s, ws, stream=None):
 def moe_gr_write(p, resid, s, f, resid_out, stream=None):
     _check(LIB.moe_gr_write(ctypes.byref(p), _ptr(resid), _ptr(s), _ptr(f), _ptr(resid_out), _stream(stream)),
            "moe_gr_write")
+
+
+# numpy dtype of one moe_audit_stats record (int64 n, n_zero, n_nan; float64 median, mad, sigma_rob)
+AUDIT_STATS_FIELDS = ("n", "n_zero", "n_nan", "median", "mad", "sigma_rob")
+
+
+def moe_audit_workspace_bytes(slices: int) -> int:
+    return LIB.moe_audit_workspace_bytes(slices)
+
+
+def audit_workspace(slices: int, device="cuda") -> torch.Tensor:
+    n = moe_audit_workspace_bytes(slices)
+    if n == 0:
+        raise MoEError(2, "moe_audit_workspace_bytes")  # 2: MOE_ERR_SHAPE
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def audit_stats_buffer(slices: int, device="cuda") -> torch.Tensor:
+    """Device buffer for slices + 1 records (48 bytes each, 8-byte aligned)."""
+    return torch.empty((slices + 1, 6), dtype=torch.float64, device=device)
+
+
+def moe_weight_audit(w, slices: int, n: int, slice_stride: int, stats, ws, stream=None):
+    """w: bf16 device tensor; stats: audit_stats_buffer(slices)."""
+    if w.dtype != torch.bfloat16:
+        raise MoEError(6, "moe_weight_audit")  # 6: MOE_ERR_UNSUPPORTED
+    _check(LIB.moe_weight_audit(_ptr(w), MOE_BF16, slices, n, slice_stride, _ptr(stats), _ptr(ws), ws.numel(),
+                                _stream(stream)), "moe_weight_audit")
+
+
+def audit_records(stats: torch.Tensor) -> list:
+    """Host dicts of the records in an audit_stats_buffer (after the stream is synchronised)."""
+    host = stats.detach().cpu().contiguous()
+    ints = host.view(torch.int64)
+    return [{"n": int(ints[i, 0]), "n_zero": int(ints[i, 1]), "n_nan": int(ints[i, 2]),
+             "median": float(host[i, 3]), "mad": float(host[i, 4]), "sigma_rob": float(host[i, 5])}
+            for i in range(host.shape[0])]

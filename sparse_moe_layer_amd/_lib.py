@@ -24,7 +24,8 @@ MOE_FLAG_PAGE_ROUTING = 16
 
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_validate", "moe_workspace_bytes", "moe_route",
            "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",
-           "moe_layer_forward", "moe_gr_workspace_bytes", "moe_gr_read", "moe_gr_write"]
+           "moe_layer_forward", "moe_gr_workspace_bytes", "moe_gr_read", "moe_gr_write",
+           "moe_audit_workspace_bytes", "moe_weight_audit"]
 
 
 class moe_problem(ctypes.Structure):
@@ -44,6 +45,11 @@ class moe_weights(ctypes.Structure):
 class moe_gr_weights(ctypes.Structure):
     _fields_ = [("norm_w", ctypes.c_void_p), ("w_read", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
                 ("rank", ctypes.c_int64), ("eps", ctypes.c_float)]
+
+
+class moe_audit_stats(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("n_zero", ctypes.c_int64), ("n_nan", ctypes.c_int64),
+                ("median", ctypes.c_double), ("mad", ctypes.c_double), ("sigma_rob", ctypes.c_double)]
 
 
 def _load():
@@ -69,6 +75,9 @@ def _load():
         "moe_gr_workspace_bytes": (sz, [P, ctypes.c_int64]),
         "moe_gr_read": (i32, [P, G, vp, vp, vp, vp, sz, vp]),
         "moe_gr_write": (i32, [P, vp, vp, vp, vp, vp]),
+        "moe_audit_workspace_bytes": (sz, [ctypes.c_int64]),
+        "moe_weight_audit": (i32, [vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp, vp, sz,
+                                   vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

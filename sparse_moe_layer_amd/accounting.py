@@ -88,6 +88,12 @@ def gr_write_work(T: int, H: int):
     return 2.0 * T * 4 * H, 2.0 * (2 * T * 4 * H + T * H) + 4.0 * T * 4
 
 
+def audit_work(values: int) -> float:
+    """Expert-weight audit: every bf16 value is read once (the histograms it
+    writes are a few hundred KB per slice and are not counted)."""
+    return 2.0 * values
+
+
 def roofline(flops: float, byts: float, seconds: float, mfma_peak: float = PEAK_BF16_TFLOPS) -> dict:
     """Bound from the intensity against the ridge, then achieved / peak."""
     if flops / byts > mfma_peak * 1e12 / (PEAK_HBM_GBPS * 1e9):

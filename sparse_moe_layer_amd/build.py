@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmoe_mi355x.so")
 BUILD = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.cpp", "router.hip", "dispatch.hip", "gemm.hip", "gemm_dma.hip", "stream.hip", "combine.hip", "simt.hip", "gr.hip"]
+SOURCES = ["api.cpp", "router.hip", "dispatch.hip", "gemm.hip", "gemm_dma.hip", "stream.hip", "combine.hip", "simt.hip", "gr.hip", "audit.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]

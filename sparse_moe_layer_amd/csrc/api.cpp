@@ -446,4 +446,21 @@ moe_status moe_gr_write(const moe_problem* p, const void* resid, const float* s,
   return hip_status(moe::launch_gr_write(resid, s, f, resid_out, (int)p->T, (int)p->H, (hipStream_t)stream));
 }
 
+size_t moe_audit_workspace_bytes(int64_t slices) {
+  if (slices < 1 || slices > 65535) return 0;
+  return moe::audit_workspace_bytes(slices);
+}
+
+moe_status moe_weight_audit(const void* w, int32_t dtype, int64_t slices, int64_t n, int64_t slice_stride,
+                            moe_audit_stats* stats, void* ws, size_t ws_bytes, void* stream) {
+  if (dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (slices < 1 || slices > 65535 || n < 0 || n >= ((int64_t)1 << 32) || slice_stride < n) return MOE_ERR_SHAPE;
+  if ((n > 0 && !w) || !stats || !ws) return MOE_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(w) & 1u) || (reinterpret_cast<uintptr_t>(stats) & 7u) ||
+      reinterpret_cast<uintptr_t>(ws) % kAlign)
+    return MOE_ERR_ALIGN;
+  if (ws_bytes < moe::audit_workspace_bytes(slices)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_audit(w, slices, n, slice_stride, stats, ws, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe_mi355x.h"
+
 namespace moe {
 
 // Rows per MFMA GEMM m-tile (128-row kernels / big-tile kernel) and per
@@ -74,6 +76,11 @@ hipError_t launch_combine(const void* y, const int32_t* pos, const float* w, con
                           hipStream_t s);
 
 // Gated residual read / write (bf16).
+// Expert-weight audit (bf16): histograms of the bit patterns per slice and
+// over the tensor, then the exact statistics of each.
+size_t audit_workspace_bytes(int64_t slices);
+hipError_t launch_audit(const void* w, int64_t slices, int64_t n, int64_t stride, moe_audit_stats* stats, void* ws,
+                        hipStream_t st);
 size_t gr_workspace_bytes(int64_t T, int64_t H, int64_t rank);
 hipError_t launch_gr_read(const void* resid, const void* norm_w, const void* w_read, const void* w_up, float eps,
                           int T, int H, int rank, void* x, float* s, void* ws, hipStream_t st);

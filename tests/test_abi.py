@@ -164,3 +164,24 @@ def test_gated_residual_entry_points_validate_before_any_launch():
     p0 = lib.problem(0, 2560, 512, 10, 640, 640)
     assert L.moe_gr_read(ctypes.byref(p0), G, None, None, None, None, 0, None) == OK
     assert L.moe_gr_write(ctypes.byref(p0), None, None, None, None, None) == OK
+
+
+def test_audit_entry_points_validate_before_any_launch():
+    L = _lib.LIB
+    fake = 1 << 20
+    assert ctypes.sizeof(_lib.moe_audit_stats) == 48
+    assert lib.moe_audit_workspace_bytes(512) >= 512 * 65536 * 4 + 65536 * 8
+    assert lib.moe_audit_workspace_bytes(0) == 0 and lib.moe_audit_workspace_bytes(65536) == 0
+    wsz = lib.moe_audit_workspace_bytes(4)
+    A = L.moe_weight_audit
+    bf, f32 = _lib.MOE_BF16, _lib.MOE_F32
+    assert A(fake, f32, 4, 100, 100, fake, fake, wsz, None) == _lib.MOE_ERR_UNSUPPORTED
+    assert A(fake, bf, 0, 100, 100, fake, fake, wsz, None) == _lib.MOE_ERR_SHAPE
+    assert A(fake, bf, 4, 100, 99, fake, fake, wsz, None) == _lib.MOE_ERR_SHAPE      # stride < n
+    assert A(fake, bf, 4, 1 << 32, 1 << 32, fake, fake, wsz, None) == _lib.MOE_ERR_SHAPE
+    assert A(None, bf, 4, 100, 100, fake, fake, wsz, None) == _lib.MOE_ERR_NULL
+    assert A(fake, bf, 4, 100, 100, None, fake, wsz, None) == _lib.MOE_ERR_NULL
+    assert A(fake + 1, bf, 4, 100, 100, fake, fake, wsz, None) == _lib.MOE_ERR_ALIGN
+    assert A(fake, bf, 4, 100, 100, fake + 4, fake, wsz, None) == _lib.MOE_ERR_ALIGN
+    assert A(fake, bf, 4, 100, 100, fake, fake + 16, wsz, None) == _lib.MOE_ERR_ALIGN
+    assert A(fake, bf, 4, 100, 100, fake, fake, wsz - 1, None) == _lib.MOE_ERR_WORKSPACE
