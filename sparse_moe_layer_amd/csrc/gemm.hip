@@ -48,7 +48,9 @@ struct RouterArgs {
 // bank groups.
 __device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ ((r >> 1) & 7)) << 3); }
 
-template <int MODE, bool FP8>
+// USE tells apart launches of the same code for different callers in traces
+// (0: the layer; 1: the gated residual's read projection).
+template <int MODE, bool FP8, int USE = 0>
 __global__ __launch_bounds__(NT, 2) void gemm_kernel(FfnArgs f, RouterArgs ra, int n_tiles_n,
                                                      int list_begin_idx, int list_end_idx) {
   __shared__ __attribute__((aligned(16))) bf16 sA[2 * BM * BK];
@@ -525,7 +527,7 @@ int router_gemm_split(int T, int H, int E) {
 }
 
 hipError_t launch_router_logits_bf16(const void* x, const void* w_router, const void* w_sg, float* logits,
-                                     int T, int H, int E, int nsplit, hipStream_t s) {
+                                     int T, int H, int E, int nsplit, hipStream_t s, bool gated_residual) {
   int kchunk = (H + nsplit - 1) / nsplit;
   kchunk = (kchunk + BK - 1) / BK * BK;
   RouterArgs ra{reinterpret_cast<const bf16*>(x), reinterpret_cast<const bf16*>(w_router),
@@ -534,7 +536,10 @@ hipError_t launch_router_logits_bf16(const void* x, const void* w_router, const 
   const int tiles = ((T + BM - 1) / BM) * ntn * nsplit;
   const int grid = tiles < num_cus() * 2 ? (tiles + 7) / 8 * 8 : num_cus() * 2;
   FfnArgs none{};
-  gemm_kernel<M_ROUTER, false><<<grid, NT, 0, s>>>(none, ra, ntn, -1, 0);
+  if (gated_residual)
+    gemm_kernel<M_ROUTER, false, 1><<<grid, NT, 0, s>>>(none, ra, ntn, -1, 0);
+  else
+    gemm_kernel<M_ROUTER, false><<<grid, NT, 0, s>>>(none, ra, ntn, -1, 0);
   return hipGetLastError();
 }
 

@@ -312,7 +312,7 @@ hipError_t launch_gr_read(const void* resid, const void* norm_w, const void* w_r
                                     H, eps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_router_logits_bf16(rhat, w_read, nullptr, partial, T, STREAMS * H, N, nsplit, st);
+  e = launch_router_logits_bf16(rhat, w_read, nullptr, partial, T, STREAMS * H, N, nsplit, st, true);
   if (e != hipSuccess) return e;
   const int64_t n = (int64_t)T * N;
   gr_gate_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(partial, nsplit, T, rank, z, s);

@@ -48,8 +48,11 @@ size_t ffn_plan_ints(int64_t T, int64_t E, int64_t k, bool shared);
 // kernel adds the chunks in order c = 0..nsplit-1.  The small-batch
 // streaming router writes complete logits (nsplit = 1).
 int router_gemm_split(int T, int H, int E);
+// gated_residual: the same GEMM for the gated residual's read projection
+// (a separately named kernel instance, so traces tell the two apart).
 hipError_t launch_router_logits_bf16(const void* x, const void* w_router, const void* w_sg,
-                                     float* partial, int T, int H, int E, int nsplit, hipStream_t s);
+                                     float* partial, int T, int H, int E, int nsplit, hipStream_t s,
+                                     bool gated_residual = false);
 hipError_t launch_router_stream(const void* x, const void* w_router, const void* w_sg, float* logits, int T,
                                 int H, int E, hipStream_t s);
 hipError_t launch_router_logits_f32(const float* x, const float* w_router, const float* w_sg,
