@@ -13,7 +13,8 @@
 //                         atomics; each workgroup then adds its non-empty
 //                         LDS bins into the slice's histogram and the whole
 //                         tensor's (uint64) in HBM.
-//   audit_finalize_kernel one workgroup per histogram.  Positions o in value
+//   audit_finalize_kernel one workgroup per histogram (the slices' and the
+//                         tensor's in one launch).  Positions o in value
 //                         order (-inf .. -0 | +0 .. +inf, NaN patterns at
 //                         both ends) are dealt 4096 per wave; wave scans and
 //                         a scan of the wave sums turn each histogram, in place,
@@ -150,15 +151,14 @@ __device__ __forceinline__ CT wave_total(CT v) {
 
 __device__ __forceinline__ unsigned long long dbits(double d) { return (unsigned long long)__double_as_longlong(d); }
 
+// Statistics of one histogram h (in place: becomes value-order prefix counts).
 template <typename CT>
-__global__ __launch_bounds__(kFinThreads) void audit_finalize_kernel(CT* __restrict__ hist,
-                                                                     moe_audit_stats* __restrict__ out) {
+__device__ void finalize_one(CT* __restrict__ h, moe_audit_stats* __restrict__ out) {
   __shared__ CT wsum[kFinThreads / 64];
   __shared__ unsigned long long nan_sum;
   __shared__ int ord_k[2];
   __shared__ unsigned long long dmin[2];
   __shared__ unsigned long long zero_cnt;
-  CT* h = hist + (int64_t)blockIdx.x * kBins;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // wave w owns the 4096 positions from 4096 w; in its j-th step lane l takes
   // position 4096 w + 64 j + l, so every load and store is one coalesced run
@@ -293,8 +293,17 @@ __global__ __launch_bounds__(kFinThreads) void audit_finalize_kernel(CT* __restr
     r.median = med;
     r.mad = mad;
     r.sigma_rob = kSigmaRobScale * mad;
-    out[blockIdx.x] = r;
+    *out = r;
   }
+}
+
+// One workgroup per slice histogram (uint32 counts), and the last one for
+// the whole tensor's (uint64), all in one launch.
+__global__ __launch_bounds__(kFinThreads) void audit_finalize_kernel(uint32_t* __restrict__ hist,
+                                                                     unsigned long long* __restrict__ whole,
+                                                                     int slices, moe_audit_stats* __restrict__ out) {
+  if ((int)blockIdx.x < slices) finalize_one<uint32_t>(hist + (int64_t)blockIdx.x * kBins, out + blockIdx.x);
+  else finalize_one<unsigned long long>(whole, out + slices);
 }
 
 int audit_cus() {
@@ -338,10 +347,7 @@ hipError_t launch_audit(const void* w, int64_t slices, int64_t n, int64_t stride
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  audit_finalize_kernel<uint32_t><<<(unsigned)slices, kFinThreads, 0, st>>>(hist, stats);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  audit_finalize_kernel<unsigned long long><<<1, kFinThreads, 0, st>>>(whole, stats + slices);
+  audit_finalize_kernel<<<(unsigned)(slices + 1), kFinThreads, 0, st>>>(hist, whole, (int)slices, stats);
   return hipGetLastError();
 }
 
