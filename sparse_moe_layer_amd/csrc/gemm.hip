@@ -122,9 +122,11 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(FfnArgs f, RouterArgs ra, i
 
     // ---------------- per-thread operand row pointers ----------------
     const bf16* a_ptr[4];
+    bool a_in[4];  // the row is one of the group's (rows past it are never stored)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int r = (tid >> 3) + 32 * i;
+      a_in[i] = r < nrows;
       r = r < nrows ? r : nrows - 1;  // clamp: rows past the group are computed, never stored
       const int gr = base + r0 + r;
       if (MODE == M_ROUTER) {
@@ -211,7 +213,8 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(FfnArgs f, RouterArgs ra, i
       kt = kt < nk ? kt : nk - 1;
       const int k0 = kbeg + kt * BK;
       // loads are unconditional (address clamped into the row, value zeroed
-      // past K) so that no branch splits the load stream
+      // past K) so that no branch splits the load stream; skipping the padded
+      // activation rows here, as the bf16 path does, measured no faster
       const int kk = k0 + kcol * 8;
       const bool kin = kk < K;
       const int kc = kin ? kk : K - 8;
@@ -306,13 +309,15 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(FfnArgs f, RouterArgs ra, i
       }
     } else {
       // bf16 weights: one register stage with loads guarded per lane (both
-      // measured faster for ~100-row groups than two stages or clamped loads)
+      // measured faster for ~100-row groups than two stages or clamped loads).
+      // Activation rows past the group are not loaded at all: in a 128-row
+      // tile over a ~80-row expert they would be a third of the A loads.
       auto gload1 = [&](int kt) {
         const int k0 = kbeg + kt * BK;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int kk = k0 + kcol * 8;
-          ra_reg[0][i] = kk < K ? ld16(a_ptr[i] + kk) : u32x4{0, 0, 0, 0};
+          ra_reg[0][i] = (kk < K && a_in[i]) ? ld16(a_ptr[i] + kk) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
