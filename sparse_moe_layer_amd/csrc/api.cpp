@@ -25,7 +25,8 @@ size_t w_bytes(const moe_problem* p) {
 
 // ---------------------------------------------------------------------------
 // router form: fp32 SIMT (fp32 layers), split-K weight streaming (T <= 16, the
-// router is a GEMV bound by reading W_r), or split-K MFMA GEMM (larger T).
+// router is a GEMV bound by reading W_r; K split so that ~128 K values fall to
+// each wave), or split-K MFMA GEMM (larger T).
 // The logits land as nsplit fp32 partials that the top-k kernel adds.
 // ---------------------------------------------------------------------------
 struct RoutePlan {
@@ -35,7 +36,7 @@ struct RoutePlan {
 
 RoutePlan route_plan(const moe_problem* p) {
   if (p->act_dtype == MOE_F32) return {false, 1};
-  if (p->T <= moe::kStreamMaxRows) return {true, 1};
+  if (p->T <= moe::kStreamMaxRows) return {true, moe::router_stream_split((int)p->H)};
   return {false, moe::router_gemm_split((int)p->T, (int)p->H, (int)p->E)};
 }
 
@@ -177,7 +178,7 @@ moe_status do_route(const moe_problem* p, const void* x, const void* w_router, c
     e = moe::launch_router_logits_f32(static_cast<const float*>(x), static_cast<const float*>(w_router),
                                       static_cast<const float*>(wsg), partial, T, H, E, s);
   else if (rp.stream)
-    e = moe::launch_router_stream(x, w_router, wsg, partial, T, H, E, s);
+    e = moe::launch_router_stream(x, w_router, wsg, partial, T, H, E, rp.nsplit, s);
   else
     e = moe::launch_router_logits_bf16(x, w_router, wsg, partial, T, H, E, rp.nsplit, s);
   if (e != hipSuccess) return MOE_ERR_HIP;

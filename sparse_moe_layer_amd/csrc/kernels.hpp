@@ -53,8 +53,10 @@ int router_gemm_split(int T, int H, int E);
 hipError_t launch_router_logits_bf16(const void* x, const void* w_router, const void* w_sg,
                                      float* partial, int T, int H, int E, int nsplit, hipStream_t s,
                                      bool gated_residual = false);
+// nsplit = router_stream_split(H) K chunks, each its own partial logits.
+int router_stream_split(int H);
 hipError_t launch_router_stream(const void* x, const void* w_router, const void* w_sg, float* logits, int T,
-                                int H, int E, hipStream_t s);
+                                int H, int E, int nsplit, hipStream_t s);
 hipError_t launch_router_logits_f32(const float* x, const float* w_router, const float* w_sg,
                                     float* logits, int T, int H, int E, hipStream_t s);
 // page: round the logits to bf16 before the top-k and the mixing weights to

@@ -67,12 +67,30 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
   const int64_t cstride = (int64_t)T * ldl;
   const float* row = partial + (int64_t)t * ldl;
   uint32_t khi[PER_LANE], klo[PER_LANE];
+  float lg[PER_LANE];
+#pragma unroll
+  for (int i = 0; i < PER_LANE; ++i) lg[i] = 0.f;
+  // four chunks at a time, the loads of all of this lane's logits in flight
+  // together, then added in chunk order
+  for (int c0 = 0; c0 < nsplit; c0 += 4) {
+    float v[4][PER_LANE];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < PER_LANE; ++i) {
+        const int e = lane + 64 * i;
+        v[u][i] = (c0 + u < nsplit && e < E) ? row[(c0 + u) * cstride + e] : 0.f;
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < PER_LANE; ++i)
+        if (c0 + u < nsplit) lg[i] += v[u][i];
+  }
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
     const int e = lane + 64 * i;
-    float a = 0.f;
-    if (e < E)
-      for (int c = 0; c < nsplit; ++c) a += row[c * cstride + e];
+    float a = lg[i];
     if (page) a = bf2f(f2bf(a));  // logits in the activation dtype (round to nearest even)
     khi[i] = e < E ? ord(a) : 0u;
     klo[i] = ~(uint32_t)e;

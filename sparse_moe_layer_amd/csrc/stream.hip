@@ -417,8 +417,11 @@ __global__ __launch_bounds__(RW * 64) void router_stream_kernel(const bf16* __re
   const int w = threadIdx.x >> 6;
   const int slab = blockIdx.x;
   const int m = lane & 15, kq = (lane >> 4) * 8;
-  const int kbeg = w * kchunk;
+  // workgroup blockIdx.y covers K values [y * RW * kchunk, +RW * kchunk) and
+  // writes its own partial logits
+  const int kbeg = (blockIdx.y * RW + w) * kchunk;
   const int kend = kbeg + kchunk < H ? kbeg + kchunk : H;
+  logits += (int64_t)blockIdx.y * T * N;
   f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
   if (kbeg < kend) {
     const bf16* a_row = m < T ? x + (int64_t)m * H : nullptr;
@@ -456,12 +459,19 @@ int stream_grid() {
 
 }  // namespace
 
+int router_stream_split(int H) {
+  // about 128 K values per wave, so that each wave's loads fit in one batch
+  // and the few (E + 1) / 16 row slabs still spread over many CUs
+  const int ks = (H + RW * 128 - 1) / (RW * 128);
+  return ks < 1 ? 1 : (ks > 16 ? 16 : ks);
+}
+
 hipError_t launch_router_stream(const void* x, const void* w_router, const void* w_sg, float* logits, int T, int H,
-                                int E, hipStream_t s) {
+                                int E, int nsplit, hipStream_t s) {
   const int N = E + (w_sg ? 1 : 0);
-  int kchunk = (H + RW - 1) / RW;
+  int kchunk = (H + RW * nsplit - 1) / (RW * nsplit);
   kchunk = (kchunk + KSTEP - 1) / KSTEP * KSTEP;
-  router_stream_kernel<<<(N + 15) / 16, RW * 64, 0, s>>>(reinterpret_cast<const bf16*>(x),
+  router_stream_kernel<<<dim3((N + 15) / 16, nsplit), RW * 64, 0, s>>>(reinterpret_cast<const bf16*>(x),
                                                          reinterpret_cast<const bf16*>(w_router),
                                                          reinterpret_cast<const bf16*>(w_sg), logits, T, H, E, N,
                                                          kchunk);
