@@ -46,8 +46,9 @@ def parse():
                     help="pin the MFMA GEMM kernel (A/B runs); default picks by rows per expert")
     ap.add_argument("--path", default="auto", choices=["auto", "gemm", "stream"],
                     help="pin every expert to one path (A/B runs); default picks per expert by rows")
-    ap.add_argument("--cpu-tokens", type=int, default=1024,
-                    help="tokens of the same workload the CPU oracle runs on (0: skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=-1,
+                    help="tokens of the same workload the CPU oracle runs on (0: skip; -1: as many as fit "
+                         "in about 15 s after a 64-token probe)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scale factor for HBM byte counters)")
     return ap.parse_args()
@@ -85,25 +86,37 @@ def load_traffic(workload, kernel):
 
 
 def cpu_baseline(problem, n_tokens):
-    """The fp64 oracle, as it stands, on the first n_tokens tokens of the workload."""
+    """The fp64 oracle, as it stands, on the first n tokens of the workload.
+    n_tokens < 0 sizes the sample by time: a 64-token probe, then as many
+    tokens as the probe's rate fits in about 15 s (at most the whole batch)."""
     import types
 
     from threadpoolctl import threadpool_info
 
     from oracle import adapter
-    n = min(n_tokens, problem.cfg.T)
-    sub = types.SimpleNamespace(**{k: getattr(problem, k) for k in (
-        "w_router", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "sh_gate", "sh_up", "sh_down",
-        "sh_gate_w")})
-    sub.cfg = problem.cfg.with_(T=n)
-    sub.x = problem.x[:n]
-    sub.host_raw = problem.host_raw
-    t0 = time.perf_counter()
-    adapter.forward(sub)
-    dt = time.perf_counter() - t0
+
+    def run(n):
+        sub = types.SimpleNamespace(**{k: getattr(problem, k) for k in (
+            "w_router", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "sh_gate", "sh_up", "sh_down",
+            "sh_gate_w")})
+        sub.cfg = problem.cfg.with_(T=n)
+        sub.x = problem.x[:n]
+        sub.host_raw = problem.host_raw
+        t0 = time.perf_counter()
+        adapter.forward(sub)
+        return time.perf_counter() - t0
+
+    T = problem.cfg.T
+    if n_tokens < 0:
+        n0 = min(64, T)
+        rate = n0 / run(n0)
+        n = min(T, max(n0, int(15.0 * rate)))
+    else:
+        n = min(n_tokens, T)
+    dt = run(n)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of {problem.cfg.T} tokens of the same workload, full layer "
+            "sample": f"first {n} of {T} tokens of the same workload, full layer "
                       f"(route, dispatch, every routed and shared expert, combine) in fp64 NumPy; "
                       f"{dt:.1f} s wall"}
 
@@ -306,7 +319,7 @@ def main():
         "gated_residual": gr,
         "weight_audit": audit,
     }
-    if args.cpu_tokens > 0:
+    if args.cpu_tokens != 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(prob, args.cpu_tokens)
     else:
