@@ -535,9 +535,11 @@ hipError_t launch_ffn_plan(const int32_t* offsets, const int32_t* sorted, int T,
 }
 
 int router_gemm_split(int T, int H, int E) {
-  // enough (m, n, K-chunk) tiles to cover the chip; chunks of whole 64-wide K steps
+  // as many (m, n, K-chunk) tiles as fit in one round of resident workgroups
+  // (two per CU): a split that spills a few tiles into a second round
+  // doubles the kernel's time.  Chunks are whole 64-wide K steps.
   const int tiles = ((T + BM - 1) / BM) * ((E + 1 + BN - 1) / BN);
-  int ns = (2 * num_cus() + tiles - 1) / tiles;
+  int ns = (2 * num_cus()) / tiles;
   const int maxs = H / (4 * BK) > 0 ? H / (4 * BK) : 1;
   ns = ns < 1 ? 1 : (ns > maxs ? maxs : ns);
   int kchunk = (H + ns - 1) / ns;
