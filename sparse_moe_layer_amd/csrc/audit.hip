@@ -16,7 +16,7 @@
 //   audit_finalize_kernel one workgroup per histogram (the slices' and the
 //                         tensor's in one launch).  Positions o in value
 //                         order (-inf .. -0 | +0 .. +inf, NaN patterns at
-//                         both ends) are dealt 4096 per wave; wave scans and
+//                         both ends) are dealt 8192 per wave; wave scans and
 //                         a scan of the wave sums turn each histogram, in place,
 //                         into inclusive counts in value order (stored at
 //                         each position's own pattern), and the lanes
@@ -40,7 +40,7 @@ namespace {
 constexpr int kBins = 65536;       // bf16 bit patterns
 constexpr int kLdsBins = 32768;    // patterns with exponent field < 128, sign included
 constexpr int kHistThreads = 1024;
-constexpr int kFinThreads = 1024;  // 64 value-order positions per thread
+constexpr int kFinThreads = 512;   // four finalize workgroups fit on a CU
 constexpr int kOrdFirst = 0x7F;    // value-order position of -inf (below it: negative NaNs)
 constexpr int kOrdLast = 0xFF80;   // +inf (above it: positive NaNs)
 constexpr int kOrdZero = 0x8000;   // +0, which holds the count of every zero
@@ -151,18 +151,28 @@ __device__ __forceinline__ CT wave_total(CT v) {
 
 __device__ __forceinline__ unsigned long long dbits(double d) { return (unsigned long long)__double_as_longlong(d); }
 
-// Statistics of one histogram h (in place: becomes value-order prefix counts).
+// Statistics of one histogram h (in place: the occupied groups become
+// value-order prefix counts).  Positions come in 1024 groups of 64; a group
+// with no values is never read again after pass 1, and its prefix count
+// lives in LDS.
 template <typename CT>
 __device__ void finalize_one(CT* __restrict__ h, moe_audit_stats* __restrict__ out) {
-  __shared__ CT wsum[kFinThreads / 64];
+  constexpr int kGroups = kBins / 64;
+  constexpr int kWaves = kFinThreads / 64;
+  constexpr int kGpw = kGroups / kWaves;        // groups per wave
+  constexpr int kGpt = kGroups / kFinThreads;   // groups per thread in the group scan
+  __shared__ CT gsum[kGroups];  // values in each group
+  __shared__ CT gpre[kGroups];  // values in the groups before it
+  __shared__ CT wsum[kWaves];
   __shared__ unsigned long long nan_sum;
   __shared__ int ord_k[2];
   __shared__ unsigned long long dmin[2];
   __shared__ unsigned long long zero_cnt;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // wave w owns the 4096 positions from 4096 w; in its j-th step lane l takes
-  // position 4096 w + 64 j + l, so every load and store is one coalesced run
-  const int wbase = wave * 4096;
+  // wave w owns groups kGpw w .. (positions 64 kGpw w ..); in its j-th step
+  // lane l takes position 64 (kGpw w + j) + l, so every access is one
+  // coalesced run
+  const int g0 = wave * kGpw;
   if (tid == 0) {
     nan_sum = 0ull;
     ord_k[0] = ord_k[1] = -1;
@@ -170,51 +180,74 @@ __device__ void finalize_one(CT* __restrict__ h, moe_audit_stats* __restrict__ o
     zero_cnt = 0ull;
   }
   __syncthreads();
-  // pass 1: the wave's count (NaN patterns are counted apart and take no
+  // pass 1: every group's count (NaN patterns are counted apart and take no
   // place in the order)
-  CT mine = 0;
   unsigned long long nans = 0;
-#pragma unroll 16
-  for (int j = 0; j < 64; ++j) {
-    const int o = wbase + 64 * j + lane;
-    const CT c = h[pat_of_ord(o)];
-    if (o < kOrdFirst || o > kOrdLast) nans += (unsigned long long)c;
-    else mine += c;
+  for (int j0 = 0; j0 < kGpw; j0 += 16) {
+    CT cb[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) cb[j] = h[pat_of_ord(64 * (g0 + j0 + j) + lane)];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int o = 64 * (g0 + j0 + j) + lane;
+      CT c = cb[j];
+      if (o < kOrdFirst || o > kOrdLast) {
+        nans += (unsigned long long)c;
+        c = 0;
+      }
+      const CT gs = __ballot(c != 0) ? wave_total<CT>(c) : (CT)0;
+      if (lane == 0) gsum[g0 + j0 + j] = gs;
+    }
   }
-  mine = wave_total<CT>(mine);
-  if (lane == 0) wsum[wave] = mine;
   if (nans) atomicAdd(&nan_sum, nans);
   __syncthreads();
-  CT before = 0, total = 0;
-  for (int i = 0; i < kFinThreads / 64; ++i) {
-    before += i < wave ? wsum[i] : (CT)0;
-    total += wsum[i];
+  // exclusive prefix of the group counts: thread t holds groups kGpt t ..
+  {
+    CT v[kGpt], sum = 0;
+#pragma unroll
+    for (int i = 0; i < kGpt; ++i) {
+      v[i] = gsum[kGpt * tid + i];
+      sum += v[i];
+    }
+    const CT incl = wave_incl_scan<CT>(sum, lane);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    CT run = incl - sum;
+    for (int i = 0; i < wave; ++i) run += wsum[i];
+#pragma unroll
+    for (int i = 0; i < kGpt; ++i) {
+      gpre[kGpt * tid + i] = run;
+      run += v[i];
+    }
   }
+  __syncthreads();
+  CT total = 0;
+  for (int i = 0; i < kWaves; ++i) total += wsum[i];
   const unsigned long long n = (unsigned long long)total;
   const unsigned long long k1 = n ? (n - 1) / 2 : 0, k2 = n / 2;
-  // pass 2: counts -> inclusive counts in value order, in place (stored at
-  // each position's own pattern); find the positions of ranks k1 and k2
-  CT run = before;
-  for (int j0 = 0; j0 < 64; j0 += 16) {
-    CT cb[16];  // one batch of counts, loaded together
+  // pass 2, occupied groups only, eight groups' loads in flight together:
+  // counts -> inclusive counts in value order, in place (stored at each
+  // position's own pattern); find the positions of ranks k1 and k2
+  for (int j0 = 0; j0 < kGpw; j0 += 8) {
+    CT cb[8];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int o = wbase + 64 * (j0 + j) + lane;
-      cb[j] = (o < kOrdFirst || o > kOrdLast) ? (CT)0 : h[pat_of_ord(o)];
+    for (int j = 0; j < 8; ++j) {
+      const int o = 64 * (g0 + j0 + j) + lane;
+      cb[j] = (gsum[g0 + j0 + j] == 0 || o < kOrdFirst || o > kOrdLast) ? (CT)0 : h[pat_of_ord(o)];
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int o = wbase + 64 * (j0 + j) + lane;
+    for (int j = 0; j < 8; ++j) {
+      const int g = g0 + j0 + j;
+      if (gsum[g] == 0) continue;  // wave-uniform
+      const int o = 64 * g + lane;
       const CT c = cb[j];
-      const CT incl = wave_incl_scan<CT>(c, lane);
-      const CT at = run + incl;  // values at positions <= o
+      const CT at = gpre[g] + wave_incl_scan<CT>(c, lane);  // values at positions <= o
       if (o == kOrdZero) zero_cnt = (unsigned long long)c;
       if (c) {
         if ((unsigned long long)(at - c) <= k1 && k1 < (unsigned long long)at) ord_k[0] = o;
         if ((unsigned long long)(at - c) <= k2 && k2 < (unsigned long long)at) ord_k[1] = o;
       }
       h[pat_of_ord(o)] = at;
-      run += __shfl(incl, 63, 64);
     }
   }
   __syncthreads();
@@ -225,9 +258,13 @@ __device__ void finalize_one(CT* __restrict__ h, moe_audit_stats* __restrict__ o
     med = (val_of_ord(ord_k[0]) + val_of_ord(ord_k[1])) * 0.5;
     if (__builtin_isfinite(med)) {  // an infinite or NaN median (inf - inf) leaves the MAD NaN
       const double m = med;
-      // P(o): values at positions <= o (0 below the first position)
+      // P(o): values at positions <= o (0 below the first position); an
+      // empty group's positions all hold its prefix
       auto P = [&](int o) -> unsigned long long {
-        return o < kOrdFirst ? 0ull : (unsigned long long)h[pat_of_ord(o > kOrdLast ? kOrdLast : o)];
+        if (o < kOrdFirst) return 0ull;
+        o = o > kOrdLast ? kOrdLast : o;
+        const int g = o >> 6;
+        return gsum[g] == 0 ? (unsigned long long)gpre[g] : (unsigned long long)h[pat_of_ord(o)];
       };
       // om: first position with value >= m (values increase with o)
       int lo = kOrdFirst, hi = kOrdLast + 1;
@@ -257,16 +294,18 @@ __device__ void finalize_one(CT* __restrict__ h, moe_audit_stats* __restrict__ o
         }
         return above + (below_all - P(c - 1));
       };
-      // candidates dealt round-robin (position tid + 1024 j), so that the
-      // occupied positions, which cluster around the median, spread over
-      // all threads and the loads of neighbouring threads coalesce
+      // candidates (occupied positions) dealt round-robin, position
+      // tid + kFinThreads j, so that the positions, which cluster around the
+      // median, spread over all threads; sixteen occupancy tests' loads are
+      // in flight together
       unsigned long long best1 = ~0ull, best2 = ~0ull;
-      for (int j0 = 0; j0 < 64; j0 += 16) {
-        uint32_t occ = 0;  // one batch of occupancy tests, loaded together
+      constexpr int kPer = kBins / kFinThreads;
+      for (int j0 = 0; j0 < kPer; j0 += 16) {
+        uint32_t occ = 0;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int o = tid + kFinThreads * (j0 + j);
-          if (o >= kOrdFirst && o <= kOrdLast && P(o) != P(o - 1)) occ |= 1u << j;
+          if (o >= kOrdFirst && o <= kOrdLast && gsum[o >> 6] != 0 && P(o) != P(o - 1)) occ |= 1u << j;
         }
         for (int j = 0; j < 16; ++j) {
           if (!((occ >> j) & 1u)) continue;
