@@ -173,3 +173,29 @@ def audit_records(stats: torch.Tensor) -> list:
     return [{"n": int(ints[i, 0]), "n_zero": int(ints[i, 1]), "n_nan": int(ints[i, 2]),
              "median": float(host[i, 3]), "mad": float(host[i, 4]), "sigma_rob": float(host[i, 5])}
             for i in range(host.shape[0])]
+
+
+_DT_OF_TORCH = {torch.float32: "f32", torch.bfloat16: "bf16", torch.uint8: "fp8"}
+
+
+def layer_forward(x, k: int, w_router, w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None, sh_gate=None,
+                  sh_up=None, sh_down=None, sh_gate_w=None, flags: int = 0, stream=None):
+    """The whole layer in one call: returns (out [T, H], ids [T, k] int32, w [T, k] fp32).
+
+    Shapes come from the tensors: x [T, H] (bf16 or fp32), w_router [E, H], w_gate / w_up [E, I, H],
+    w_down [E, H, I] (bf16, fp32, or uint8 e4m3fn codes with fp32 128 x 128 block scales s_*), and
+    the optional shared expert sh_gate / sh_up [I_s, H], sh_down [H, I_s], sh_gate_w [1, H].
+    Outputs and the workspace are allocated on x's device; every computation runs in the library.
+    """
+    T, H = x.shape
+    E, I = w_gate.shape[0], w_gate.shape[1]
+    Is = sh_gate.shape[0] if sh_gate is not None else 0
+    wdt = _DT_OF_TORCH[w_gate.dtype]
+    P = problem(T, H, E, k, I, Is, _DT_OF_TORCH[x.dtype], wdt, 128, flags)
+    W = weights(w_router, w_gate, w_up, w_down, s_gate, s_up, s_down, sh_gate, sh_up, sh_down, sh_gate_w)
+    ws = workspace(P, device=x.device)
+    out = torch.empty((T, H), dtype=x.dtype, device=x.device)
+    ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    tw = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    moe_layer_forward(P, W, x, out, ids, tw, ws, stream)
+    return out, ids, tw

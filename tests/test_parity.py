@@ -261,3 +261,19 @@ def test_run_to_run_bit_identical():
     b = run_stages(p)
     for key in ("ids", "w", "offsets", "sorted", "pos", "y", "out", "out_layer"):
         assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("name", ["flash_prefill", "max_fp8"])
+def test_one_call_python_layer_forward(name):
+    # the convenience wrapper infers the problem from the tensors and gives the
+    # same bits as the stage-by-stage and struct-level calls
+    cfg = CONFIGS[name].with_(name="conv_" + name, T=40, H=256, E=8, k=2, I=128,
+                              I_shared=128 if name == "flash_prefill" else 0)
+    p = gpu_problem(cfg, 10)
+    ref = run_stages(p)
+    out, ids, w = lib.layer_forward(p.x, cfg.k, p.w_router, p.w_gate, p.w_up, p.w_down, p.s_gate, p.s_up, p.s_down,
+                                    p.sh_gate, p.sh_up, p.sh_down, p.sh_gate_w)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.float().cpu().numpy(), ref["out_layer"])
+    assert np.array_equal(ids.cpu().numpy(), ref["ids_layer"])
+    assert np.array_equal(w.cpu().numpy(), ref["w_layer"])
