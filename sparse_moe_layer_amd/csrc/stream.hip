@@ -91,10 +91,13 @@ constexpr int PAIR = 1040;
 // registers one batch ahead, writes them to the wave's LDS stage, and reads
 // MFMA fragments back.  The steady-state loop is branch-free; every load is
 // unconditional (clamped addresses, values zeroed after loading).
-template <int NB>
+// SPLIT (NB == 1): the 16-row block is two halves, rows 0-7 from wrow0[0]
+// and rows 8-15 from wrow0[1], with nvalid[0] and nvalid[1] valid rows.
+template <int NB, bool SPLIT = false>
 __device__ __forceinline__ void stream_dot_lds(const bf16* a_row, const bf16* a_any, const bf16* const* wrow0,
                                                const int* nvalid, int ldw, int kbeg, int kend, int lane, char* lds,
                                                f32x4* acc) {
+  static_assert(!SPLIT || NB == 1, "a split block is the only block");
   constexpr int NL = NB * 8;      // weight loads per batch
   constexpr int NA = SB / KSTEP;  // activation loads per batch
   const int kq = (lane >> 4) * 8;
@@ -111,8 +114,14 @@ __device__ __forceinline__ void stream_dot_lds(const bf16* a_row, const bf16* a_
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int r = 2 * i + h < nvalid[j] ? 2 * i + h : nvalid[j] - 1;
-        wb[j * 8 + i] = ld16(wrow0[j] + (uint32_t)(r * ldw + k));
+        if constexpr (SPLIT) {
+          const int half = i >> 2, rh = (2 * i + h) & 7;  // rows 0-7: first half, 8-15: second
+          const int r = rh < nvalid[half] ? rh : nvalid[half] - 1;
+          wb[i] = ld16(wrow0[half] + (uint32_t)(r * ldw + k));
+        } else {
+          const int r = 2 * i + h < nvalid[j] ? 2 * i + h : nvalid[j] - 1;
+          wb[j * 8 + i] = ld16(wrow0[j] + (uint32_t)(r * ldw + k));
+        }
       }
   };
   auto load_a = [&](int x, int b) {
@@ -272,9 +281,16 @@ __device__ __forceinline__ void stream_dot_lds8(const bf16* a_row, const bf16* a
   }
 }
 
-template <int PHASE, bool FP8>
+// SPLIT (bf16 gate/up only): items of 8 hidden columns, one 16-row block of
+// 8 gate rows and the 8 up rows of the same columns.  Half-size items end a
+// launch with less idle time; they pay off when the whole batch streams
+// (decode) and cost a few percent on large streaming tails, where 16-column
+// items (a 16-row gate block and a 16-row up block) keep more bytes in
+// flight per wave.  Down items are 32 output columns (2 blocks).
+template <int PHASE, bool FP8, bool SPLIT = false>
 __global__ __launch_bounds__(WAVES * 64, 2) void stream_kernel(FfnArgs f, int list_begin_idx, int list_end_idx) {
-  constexpr int NB = 2;  // gate+up, or 2 down blocks
+  static_assert(!SPLIT || (PHASE == 1 && !FP8), "split items are bf16 gate/up");
+  constexpr int NB = SPLIT ? 1 : 2;
   constexpr int STAGE_BYTES = NB * 8 * (FP8 ? PAIR8 : PAIR);  // per wave
   __shared__ __attribute__((aligned(16))) char stage[WAVES * STAGE_BYTES];
   const int lane = threadIdx.x & 63;
@@ -284,7 +300,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void stream_kernel(FfnArgs f, int li
   const int sb_begin = list_begin_idx < 0 ? 0 : f.plan[list_begin_idx];
   const int sb_end = f.plan[list_end_idx];
   const int wide = PHASE == 1 ? (f.I > f.Is ? f.I : f.Is) : f.H;
-  const int cols_per_item = PHASE == 1 ? 16 : 32;
+  const int cols_per_item = PHASE == 1 ? (SPLIT ? 8 : 16) : 32;
   const int n_slabs = (wide + cols_per_item - 1) / cols_per_item;
   const int total = (sb_end - sb_begin) * n_slabs;
   const int m = lane & 15;         // A row / B column within a 16-block
@@ -354,11 +370,13 @@ __global__ __launch_bounds__(WAVES * 64, 2) void stream_kernel(FfnArgs f, int li
       const bf16* a_any = reinterpret_cast<const bf16*>(PHASE == 1 ? f.x : f.h);
       stream_dot_lds8<NB>(a_row, a_any, w0, nv, K, s_row, 0, K, lane, stage + wave * STAGE_BYTES, acc);
     } else {
-      // first row and valid-row count of each 16-row weight block
-      const bf16* w0[NB];
-      int nv[NB];
+      // first row and valid-row count of each weight block (gate/up: of the
+      // gate half and the up half of the one split block)
+      constexpr int NW0 = SPLIT ? 2 : NB;
+      const bf16* w0[NW0];
+      int nv[NW0];
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
+      for (int j = 0; j < NW0; ++j) {
         int first = PHASE == 1 ? c0 : c0 + j * 16;
         first = first < Ncols ? first : Ncols - 1;
         nv[j] = Ncols - first;
@@ -372,20 +390,30 @@ __global__ __launch_bounds__(WAVES * 64, 2) void stream_kernel(FfnArgs f, int li
         w0[j] = mat + (int64_t)first * K;
       }
       const bf16* a_any = reinterpret_cast<const bf16*>(PHASE == 1 ? f.x : (shared ? f.h_sh : f.h));
-      stream_dot_lds<NB>(a_row, a_any, w0, nv, K, 0, K, lane, stage + wave * STAGE_BYTES, acc);
+      stream_dot_lds<NB, SPLIT>(a_row, a_any, w0, nv, K, 0, K, lane, stage + wave * STAGE_BYTES, acc);
     }
 
-    // C fragment: lane holds column (lane & 15), rows 4*(lane>>4) + i.
+    // C fragment: lane holds column (lane & 15), rows 4*(lane>>4) + i.  A split
+    // gate/up block has the up column of lane m (m < 8) in lane m + 8.
+    float up_v[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) up_v[i] = __shfl_xor(acc[0][i], 8, 64);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 4 * (lane >> 4) + i;
       if (row >= nrows) continue;
       const int64_t gr = base + r0 + row;
       if (PHASE == 1) {
-        const int col = c0 + m;
-        if (col < Ncols) {
-          bf16* dst = shared ? reinterpret_cast<bf16*>(f.h_sh) + gr * f.Is : reinterpret_cast<bf16*>(f.h) + gr * f.I;
-          dst[col] = f2bf(silu(acc[0][i]) * acc[1][i]);
+        bf16* dst = shared ? reinterpret_cast<bf16*>(f.h_sh) + gr * f.Is : reinterpret_cast<bf16*>(f.h) + gr * f.I;
+        if constexpr (SPLIT) {
+          // lane column m: gate column c0 + m (m < 8), up column c0 + m - 8 (m >= 8)
+          const int col = c0 + m;
+          if (m < 8 && col < Ncols) dst[col] = f2bf(silu(acc[0][i]) * up_v[i]);
+        } else {
+          const int col = c0 + m;
+          if (col < Ncols) dst[col] = f2bf(silu(acc[0][i]) * acc[1][i]);
         }
       } else {
 #pragma unroll
@@ -401,10 +429,11 @@ __global__ __launch_bounds__(WAVES * 64, 2) void stream_kernel(FfnArgs f, int li
   }
 }
 
-// Router for T <= 16 (a GEMV bound by reading W_r): one workgroup of RW
-// waves per 16 router rows (the shared-gate row counted as row E); wave w
-// covers K chunk w, and the RW partial 16x16 blocks are added through LDS in
-// wave order, so the logits are complete and deterministic.
+// Router for T <= 16 (a GEMV bound by reading W_r): workgroup (s, y) of RW
+// waves covers 16 router rows (the shared-gate row counted as row E) over K
+// chunk y; its waves take consecutive sub-chunks, their partial 16x16 blocks
+// are added through LDS in wave order, and the workgroup writes partial
+// logits [y][T][N], which the top-k kernel adds in chunk order.
 constexpr int RW = 8;
 
 __global__ __launch_bounds__(RW * 64) void router_stream_kernel(const bf16* __restrict__ x,
@@ -481,15 +510,19 @@ hipError_t launch_router_stream(const void* x, const void* w_router, const void*
 hipError_t launch_ffn_stream(const FfnArgs& a, int phase, hipStream_t s) {
   const int grid = stream_grid();
   const int blk = WAVES * 64;
+  // a batch of at most kStreamMaxRows tokens streams every group: split items
+  const bool split = a.T <= kStreamMaxRows;
   if (a.fp8) {
     if (phase == 1) stream_kernel<1, true><<<grid, blk, 0, s>>>(a, -1, 3);
     else stream_kernel<2, true><<<grid, blk, 0, s>>>(a, -1, 3);
     if (a.Is > 0) {
-      if (phase == 1) stream_kernel<1, false><<<grid, blk, 0, s>>>(a, 3, 1);
+      if (phase == 1 && split) stream_kernel<1, false, true><<<grid, blk, 0, s>>>(a, 3, 1);
+      else if (phase == 1) stream_kernel<1, false><<<grid, blk, 0, s>>>(a, 3, 1);
       else stream_kernel<2, false><<<grid, blk, 0, s>>>(a, 3, 1);
     }
   } else {
-    if (phase == 1) stream_kernel<1, false><<<grid, blk, 0, s>>>(a, -1, 1);
+    if (phase == 1 && split) stream_kernel<1, false, true><<<grid, blk, 0, s>>>(a, -1, 1);
+    else if (phase == 1) stream_kernel<1, false><<<grid, blk, 0, s>>>(a, -1, 1);
     else stream_kernel<2, false><<<grid, blk, 0, s>>>(a, -1, 1);
   }
   return hipGetLastError();
