@@ -93,11 +93,18 @@ constexpr int PAIR = 1040;
 // unconditional (clamped addresses, values zeroed after loading).
 // SPLIT (NB == 1): the 16-row block is two halves, rows 0-7 from wrow0[0]
 // and rows 8-15 from wrow0[1], with nvalid[0] and nvalid[1] valid rows.
-template <int NB, bool SPLIT = false>
+// DEPTH: batches of weights (and activations) loaded ahead of the one being
+// computed (2 doubles the bytes each wave keeps in flight; it needs the
+// registers of a second weight batch).  With DEPTH 2 every load is issued
+// unconditionally, so the compiler's load counters stay exact (a load under
+// a branch makes it wait for everything at the join): the loads of the two
+// batches past the end read one cached 16-byte chunk and are never used.
+template <int NB, bool SPLIT = false, int DEPTH = 1>
 __device__ __forceinline__ void stream_dot_lds(const bf16* a_row, const bf16* a_any, const bf16* const* wrow0,
                                                const int* nvalid, int ldw, int kbeg, int kend, int lane, char* lds,
                                                f32x4* acc) {
   static_assert(!SPLIT || NB == 1, "a split block is the only block");
+  static_assert(DEPTH == 1 || DEPTH == 2, "load depth");
   constexpr int NL = NB * 8;      // weight loads per batch
   constexpr int NA = SB / KSTEP;  // activation loads per batch
   const int kq = (lane >> 4) * 8;
@@ -105,11 +112,12 @@ __device__ __forceinline__ void stream_dot_lds(const bf16* a_row, const bf16* a_
   const int c = lane & 31;        // its 16-byte chunk of the 512-byte run
   const int nbatch = (kend - kbeg + SB - 1) / SB;
   const bf16* arow = a_row ? a_row : a_any;
-  u32x4 wb[NL];     // weights of the batch in flight
-  u32x4 av[2][NA];  // activations, double-buffered
-  auto load_w = [&](int b) {
+  u32x4 wb[DEPTH][NL];  // weights of the batches in flight
+  u32x4 av[2][NA];      // activations, double-buffered
+  auto load_w = [&](int x, int b) {
     int k = kbeg + b * SB + c * 8;
     k = k < kend ? k : kend - 8;  // past the end: any in-row chunk (its A is zero)
+    const bool live = DEPTH == 1 || b < nbatch;  // a batch past the end reads element 0
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -117,10 +125,10 @@ __device__ __forceinline__ void stream_dot_lds(const bf16* a_row, const bf16* a_
         if constexpr (SPLIT) {
           const int half = i >> 2, rh = (2 * i + h) & 7;  // rows 0-7: first half, 8-15: second
           const int r = rh < nvalid[half] ? rh : nvalid[half] - 1;
-          wb[i] = ld16(wrow0[half] + (uint32_t)(r * ldw + k));
+          wb[x][i] = ld16(wrow0[half] + (live ? (uint32_t)(r * ldw + k) : 0u));
         } else {
           const int r = 2 * i + h < nvalid[j] ? 2 * i + h : nvalid[j] - 1;
-          wb[j * 8 + i] = ld16(wrow0[j] + (uint32_t)(r * ldw + k));
+          wb[x][j * 8 + i] = ld16(wrow0[j] + (live ? (uint32_t)(r * ldw + k) : 0u));
         }
       }
   };
@@ -131,10 +139,10 @@ __device__ __forceinline__ void stream_dot_lds(const bf16* a_row, const bf16* a_
       av[x][s] = ld16(arow + (kk < kend ? kk : kend - 8));
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](int x) {
 #pragma unroll
     for (int q = 0; q < NL; ++q)
-      *reinterpret_cast<u32x4*>(lds + q * PAIR + h * 512 + ((c ^ (h << 3)) << 4)) = wb[q];
+      *reinterpret_cast<u32x4*>(lds + q * PAIR + h * 512 + ((c ^ (h << 3)) << 4)) = wb[x][q];
   };
   auto compute = [&](int x, int b) {
 #pragma unroll
@@ -152,30 +160,52 @@ __device__ __forceinline__ void stream_dot_lds(const bf16* a_row, const bf16* a_
       }
     }
   };
-  // batch b: stage its weights (loaded during the previous batch), start
-  // batch b+1's loads, run batch b's MFMAs from LDS
-  load_w(0);
-  load_a(0, 0);
-  int b = 0;
-  for (; b + 2 < nbatch; b += 2) {
-    stage();
-    load_w(b + 1);
-    load_a(1, b + 1);
-    compute(0, b);
-    stage();
-    load_w(b + 2);
-    load_a(0, b + 2);
-    compute(1, b + 1);
-  }
-  stage();
-  if (b + 1 < nbatch) {
-    load_w(b + 1);
-    load_a(1, b + 1);
-    compute(0, b);
-    stage();
-    compute(1, b + 1);
+  if constexpr (DEPTH == 2) {
+    // batch b (buffers x = b % 2): stage its weights, refill the weight
+    // buffer with batch b+2, run batch b's MFMAs, refill the activation
+    // buffer with batch b+2; batches b+1 and b+2 stay in flight meanwhile
+    auto step = [&](int x, int b) {
+      stage(x);
+      load_w(x, b + 2);
+      compute(x, b);
+      load_a(x, b + 2);
+    };
+    load_w(0, 0);
+    load_a(0, 0);
+    load_w(1, 1);
+    load_a(1, 1);
+    for (int b = 0;; b += 2) {
+      step(0, b);
+      if (b + 1 >= nbatch) break;
+      step(1, b + 1);
+      if (b + 2 >= nbatch) break;
+    }
   } else {
-    compute(0, b);
+    // batch b: stage its weights (loaded during the previous batch), start
+    // batch b+1's loads, run batch b's MFMAs from LDS
+    load_w(0, 0);
+    load_a(0, 0);
+    int b = 0;
+    for (; b + 2 < nbatch; b += 2) {
+      stage(0);
+      load_w(0, b + 1);
+      load_a(1, b + 1);
+      compute(0, b);
+      stage(0);
+      load_w(0, b + 2);
+      load_a(0, b + 2);
+      compute(1, b + 1);
+    }
+    stage(0);
+    if (b + 1 < nbatch) {
+      load_w(0, b + 1);
+      load_a(1, b + 1);
+      compute(0, b);
+      stage(0);
+      compute(1, b + 1);
+    } else {
+      compute(0, b);
+    }
   }
 }
 
@@ -390,7 +420,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void stream_kernel(FfnArgs f, int li
         w0[j] = mat + (int64_t)first * K;
       }
       const bf16* a_any = reinterpret_cast<const bf16*>(PHASE == 1 ? f.x : (shared ? f.h_sh : f.h));
-      stream_dot_lds<NB, SPLIT>(a_row, a_any, w0, nv, K, 0, K, lane, stage + wave * STAGE_BYTES, acc);
+      stream_dot_lds<NB, SPLIT, SPLIT ? 2 : 1>(a_row, a_any, w0, nv, K, 0, K, lane, stage + wave * STAGE_BYTES, acc);
     }
 
     // C fragment: lane holds column (lane & 15), rows 4*(lane>>4) + i.  A split
