@@ -217,7 +217,8 @@ FfnArgs ffn_args(const moe_problem* p, const moe_weights* w, const void* x, cons
 
 // MFMA GEMM kernel of the grouped GEMM path: the pipelined direct-load
 // kernel with 256-row tiles once experts average 128 rows or more (the MFMA
-// rate bounds them), else the register-staged kernel with 128-row tiles
+// rate bounds them; a group's last m-tile of at most 128 rows then goes to
+// the 128-row kernel), else the register-staged kernel with 128-row tiles
 // (about a hundred rows per expert: weight streaming bounds them).  The
 // 256-row kernel takes bf16 weights with H, I and I_shared multiples of 32.
 // The caller can pin either kernel for A/B runs.
@@ -246,8 +247,10 @@ moe_status run_ffn(const moe_problem* p, FfnArgs& a, int phases, void* plan_ws, 
   for (int phase = 1; phase <= 2; ++phase) {
     if (!(phases & phase)) continue;
     if (any_gemm) {
+      // 256-row tiles, then the groups' remainders of at most 128 rows in 128-row tiles
       const hipError_t e = big ? moe::launch_ffn_gemm_dma(a, phase, s) : moe::launch_ffn_gemm(a, phase, s);
       if (e != hipSuccess) return MOE_ERR_HIP;
+      if (big && moe::launch_ffn_gemm(a, phase, s, 4, 5) != hipSuccess) return MOE_ERR_HIP;
     }
     if (any_stream && moe::launch_ffn_stream(a, phase, s) != hipSuccess) return MOE_ERR_HIP;
   }

@@ -429,7 +429,11 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* offsets, cons
                                                     int max_mt, int max_sb) {
   __shared__ int tmp[32];
   __shared__ int tot;
-  int32_t* mt_group = plan + 4;
+  // with 256-row tiles a group's last m-tile of at most 128 rows goes to a
+  // second list, run by the 128-row kernel: a ragged remainder costs that
+  // kernel about two thirds of what a 256-row tile of it costs
+  const bool two_lists = bm > kGemmBM;
+  int32_t* mt_group = plan + kPlanHeader;
   int32_t* mt_row0 = mt_group + max_mt;
   int32_t* sb_group = mt_row0 + max_mt;
   int32_t* sb_row0 = sb_group + max_sb;
@@ -449,7 +453,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* offsets, cons
       else if (flags & 2u) gemm = false;      // force streaming
       else gemm = n > kStreamMaxRows;
     }
-    const int cm = gemm ? (n + bm - 1) / bm : 0;
+    const int rem = n % bm;
+    const int cm = !gemm ? 0 : two_lists ? n / bm + (rem > kGemmBM ? 1 : 0) : (n + bm - 1) / bm;
     const int cs = (n > 0 && !gemm) ? (n + kStreamBM - 1) / kStreamBM : 0;
     // routed groups first in each list, the shared group (g == E) last: since
     // g ascends with the scan order, this holds automatically.
@@ -482,10 +487,26 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* offsets, cons
     carry_mt += tm;
     carry_sb += ts;
   }
+  // second list (two_lists only): [plan[4], plan[5]) after the first
+  int carry_small = carry_mt;
+  for (int g0 = 0; two_lists && g0 < G; g0 += 1024) {
+    const int g = g0 + threadIdx.x;
+    int n = 0;
+    if (g < E) n = offsets[g + 1] - offsets[g];
+    else if (g < G) n = T;
+    const bool gemm = n > 0 && ((flags & 1u) || (!(flags & 2u) && n > kStreamMaxRows));
+    const int rem = n % bm;
+    const int cr = gemm && rem > 0 && rem <= kGemmBM ? 1 : 0;
+    const int o = block_excl_scan(cr, tmp, &tot) + carry_small;
+    if (cr) { mt_group[o] = g; mt_row0[o] = n - rem; }
+    carry_small += tot;
+  }
   if (threadIdx.x == 0) {
     plan[0] = carry_mt;
     plan[1] = carry_sb;
     if (!has_shared) { plan[2] = carry_mt; plan[3] = carry_sb; }
+    plan[4] = carry_mt;
+    plan[5] = carry_small;
   }
 }
 
@@ -510,14 +531,15 @@ int num_cus() {
 }  // namespace
 
 size_t ffn_plan_ints(int64_t T, int64_t E, int64_t k, bool shared) {
-  return 4 + 2 * (size_t)max_mtiles(T, E, k, shared) + (4 + kStreamBM) * (size_t)max_sblocks(T, E, k, shared);
+  return kPlanHeader + 2 * (size_t)max_mtiles(T, E, k, shared) +
+         (4 + kStreamBM) * (size_t)max_sblocks(T, E, k, shared);
 }
 
 void ffn_bind_plan(FfnArgs& a, int32_t* plan) {
   const bool sh = a.Is > 0;
   const int mm = max_mtiles(a.T, a.E, a.k, sh), ms = max_sblocks(a.T, a.E, a.k, sh);
   a.plan = plan;
-  a.mt_group = plan + 4;
+  a.mt_group = plan + kPlanHeader;
   a.mt_row0 = a.mt_group + mm;
   a.sb_group = a.mt_row0 + mm;
   a.sb_row0 = a.sb_group + ms;
@@ -565,7 +587,7 @@ hipError_t launch_router_logits_bf16(const void* x, const void* w_router, const 
 }
 
 // Tiled MFMA phase of the expert FFN (phase 1: gate/up + SiLU*mul, 2: down).
-hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s) {
+hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s, int list_begin_idx, int list_end_idx) {
   const bool sh = a.Is > 0;
   const int mm = max_mtiles(a.T, a.E, a.k, sh);
   const int wide = a.I > a.Is ? a.I : a.Is;
@@ -584,8 +606,9 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s) {
   } else {
     constexpr int per_cu = kBf16FfnBK == 32 ? 3 : 2;
     const int g3 = (int)(tiles < num_cus() * per_cu ? (tiles + 7) / 8 * 8 : num_cus() * per_cu);
-    if (phase == 1) gemm_kernel<M_GATEUP, false, 0, kBf16FfnBK><<<g3, NT, 0, s>>>(a, none, ntn, -1, 0);
-    else gemm_kernel<M_DOWN, false, 0, kBf16FfnBK><<<g3, NT, 0, s>>>(a, none, ntn, -1, 0);
+    if (phase == 1)
+      gemm_kernel<M_GATEUP, false, 0, kBf16FfnBK><<<g3, NT, 0, s>>>(a, none, ntn, list_begin_idx, list_end_idx);
+    else gemm_kernel<M_DOWN, false, 0, kBf16FfnBK><<<g3, NT, 0, s>>>(a, none, ntn, list_begin_idx, list_end_idx);
   }
   return hipGetLastError();
 }

@@ -13,6 +13,10 @@ namespace moe {
 constexpr int kGemmBM = 128;
 constexpr int kGemmBigBM = 256;
 constexpr int kStreamBM = 16;
+// plan ints ahead of the work lists: [0] m-tiles of the first list, [1] stream
+// m-blocks, [2] / [3] where the shared expert's m-tiles / m-blocks begin,
+// [4, 5) the second m-tile list (128-row remainders of 256-row tiling)
+constexpr int kPlanHeader = 8;
 // An expert with at most this many rows streams its weights (small-M path).
 constexpr int kStreamMaxRows = 16;
 
@@ -33,7 +37,7 @@ struct FfnArgs {
   void* y;                    // [R, H]  bf16
   void* y_sh;                 // [T, H]  bf16 (may be null when Is == 0)
   // device-built work lists
-  const int32_t* plan;        // plan[0] = #gemm m-tiles, plan[1] = #stream m-blocks
+  const int32_t* plan;        // kPlanHeader ints (see there), then the lists
   const int32_t* mt_group; const int32_t* mt_row0;
   const int32_t* sb_group; const int32_t* sb_row0;
   const int32_t* sb_base;   // first dispatched row of the group (0 for the shared expert)
@@ -69,7 +73,10 @@ hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* off
 hipError_t launch_ffn_plan(const int32_t* offsets, const int32_t* sorted, int T, int E, int k, int has_shared,
                            uint32_t flags, int bm, int32_t* plan_ws, hipStream_t s);
 void ffn_bind_plan(FfnArgs& a, int32_t* plan_ws);
-hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s);    // phase 1 gate/up, 2 down
+// phase 1 gate/up, 2 down; bf16 tiles run the m-tiles [plan[begin], plan[end])
+// (begin < 0: from 0), fp8 tiles the whole first list
+hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s, int list_begin_idx = -1,
+                           int list_end_idx = 0);
 // Pipelined direct-load MFMA GEMM with 256-row tiles (bf16 weights, H, I,
 // I_shared multiples of 32).
 bool ffn_dma_supported(const FfnArgs& a);

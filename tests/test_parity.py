@@ -167,6 +167,23 @@ def test_gemm_tile_kernels(tile):
     check(p, run_stages(p, lib.MOE_FLAG_FORCE_GEMM | tile))
 
 
+def test_256_row_tiles_with_128_row_remainders():
+    # skewed load in 256-row tiling: each group's last m-tile of at most 128
+    # rows runs in the 128-row kernel, every other m-tile in the 256-row one
+    cfg = CONFIGS["max_prefill"].with_(name="two_lists", T=1536, H=256, E=16, k=2, I=128, I_shared=64,
+                                       zipf_s=1.1)
+    p = gpu_problem(cfg, 13)
+    g = run_stages(p, lib.MOE_FLAG_GEMM_TILE_256)
+    n = np.diff(g["offsets"])
+    r = n % 256
+    assert np.any((n > 0) & (n <= 16))                 # streamed
+    assert np.any((n > 16) & (n <= 128))               # one 128-row tile only
+    assert np.any((n > 256) & (r > 0) & (r <= 128))    # 256-row tiles + a 128-row remainder
+    assert np.any((n > 128) & (r > 128))               # ends in a partial 256-row tile
+    assert cfg.T % 256 == 0                            # the shared expert: whole 256-row tiles
+    check(p, g)
+
+
 def test_one_expert_takes_every_token():
     # a steep per-expert bias: the rank-1 expert wins every token (k = 1)
     cfg = CONFIGS["max_prefill"].with_(name="all_to_one", T=300, H=256, E=8, k=1, I=128, I_shared=64, zipf_s=8.0)
