@@ -94,9 +94,11 @@ typedef struct {
  * streaming path (default: per expert, by its token count).  For A/B tests. */
 #define MOE_FLAG_FORCE_GEMM   (1u << 0)
 #define MOE_FLAG_FORCE_STREAM (1u << 1)
-/* Tile height of the MFMA GEMM path: 128-row LDS-tiled kernel or 256-row
- * direct-load kernel (default: 256 when experts average >= 256 rows).  The
- * 256-row kernel needs bf16 weights and H, I, I_shared multiples of 64;
+/* Tile height of the MFMA GEMM path: 128-row LDS-tiled kernel, or 256-row
+ * direct-load kernel with each group's last m-tile of at most 128 rows in
+ * the 128-row kernel (default: 256 when experts average >= 128 rows with
+ * bf16 weights, >= 32 rows with fp8 weights).  The 256-row kernel needs
+ * H, I, I_shared multiples of 32, and with fp8 weights H, I <= 16384;
  * otherwise the 128-row kernel runs whatever the flag says.  For A/B tests. */
 #define MOE_FLAG_GEMM_TILE_128 (1u << 2)
 #define MOE_FLAG_GEMM_TILE_256 (1u << 3)

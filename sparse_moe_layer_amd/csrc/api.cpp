@@ -226,7 +226,11 @@ bool use_big_tiles(const moe_problem* p, const FfnArgs& a) {
   if (!moe::ffn_dma_supported(a)) return false;
   if (p->flags & MOE_FLAG_GEMM_TILE_128) return false;
   if (p->flags & MOE_FLAG_GEMM_TILE_256) return true;
-  return p->T * p->k >= 128 * p->E;
+  // bf16 weights: once experts average 128 rows.  fp8 weights: from 32 rows
+  // (the 128-row fp8 tiles decode every weight once per m-tile; on the
+  // skewed 2.4T layer at 40 rows per expert the 256-row tiles of its large
+  // groups measured faster).
+  return p->T * p->k >= (a.fp8 ? 32 : 128) * p->E;
 }
 
 // phases: bit 0 gate/up, bit 1 down.  The plan kernel runs first (bf16/fp8).

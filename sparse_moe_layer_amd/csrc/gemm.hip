@@ -595,7 +595,11 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s, int list_
   const int64_t tiles = (int64_t)mm * ntn;
   const int grid = (int)(tiles < num_cus() * 2 ? (tiles + 7) / 8 * 8 : num_cus() * 2);
   RouterArgs none{};
-  if (a.fp8) {
+  if (a.fp8 && list_begin_idx >= 0) {
+    // an explicit list (128-row remainders): fp8 and shared bf16 tiles mixed
+    if (phase == 1) gemm_kernel<M_GATEUP, true><<<grid, NT, 0, s>>>(a, none, ntn, list_begin_idx, list_end_idx);
+    else gemm_kernel<M_DOWN, true><<<grid, NT, 0, s>>>(a, none, ntn, list_begin_idx, list_end_idx);
+  } else if (a.fp8) {
     // routed tiles [0, plan[2]) decode fp8; the shared expert stays bf16
     if (phase == 1) gemm_kernel<M_GATEUP, true><<<grid, NT, 0, s>>>(a, none, ntn, -1, 2);
     else gemm_kernel<M_DOWN, true><<<grid, NT, 0, s>>>(a, none, ntn, -1, 2);

@@ -23,6 +23,14 @@
 // load fetches the global chunk that belongs at its LDS position, so global
 // reads stay whole 64-byte row segments.
 //
+// fp8 weights (e4m3 codes with 128 x 128 block scales): the B stage holds
+// the codes, 32 bytes per row, laid out [16-byte chunk][row] within each
+// 32-row block, so a fragment read (8 codes of one row) by 32 lanes touches
+// 32 rows at a 16-byte stride.  The codes are decoded to bf16 with their
+// block scale as fragments leave LDS; the tile's scales (one per 128-wide K
+// block, for its gate and up row blocks or its two W_down row blocks) sit
+// in a small LDS table.  With a 32-wide K step, stage step s uses K block s/4.
+//
 // Work: (group, 256-row m-tile) entries from the device plan; tiles are
 // ordered in supertiles of a few m-tiles x all n-tiles and dealt to the
 // persistent grid so that consecutive tiles land on one XCD (workgroup i runs
@@ -34,10 +42,12 @@ namespace moe {
 namespace {
 
 
-template <int BM_, int BN_, int WM_, int WN_, int S_, int WG_PER_CU_, int BK_ = 32>
+template <int BM_, int BN_, int WM_, int WN_, int S_, int WG_PER_CU_, int BK_ = 32, bool F8_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_, BK = BK_;
+  static constexpr bool F8 = F8_;       // B holds fp8 codes (1 byte per element)
   static constexpr int RPL = 512 / BK;  // rows one 1 KB direct load fills
+  static constexpr int RPL8 = 1024 / BK;  // fp8 B rows one 1 KB direct load fills
   static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int WAVES_PER_EU = NW * WG_PER_CU_ / 4;
   static constexpr int WG_PER_CU = WG_PER_CU_;
@@ -45,15 +55,17 @@ struct Cfg {
   static constexpr int NJ = BN / (32 * WN);  // N-blocks per wave
   static constexpr int CW = NJ * 32;         // B tile rows per wave column
   static constexpr int LA = BM / (RPL * NW);  // A direct loads per lane per stage
-  static constexpr int LB = BN / (RPL * NW);  // B direct loads per lane per stage
+  static constexpr int LB = F8 ? BN / (RPL8 * NW) : BN / (RPL * NW);  // B direct loads per lane per stage
   static constexpr int L = LA + LB;
   static constexpr int STAGE = (BM + BN) * BK;  // elements per stage buffer
   static_assert(BK == 32 || BK == 64, "K step");
   static_assert(MI >= 1 && NJ >= 2 && NJ % 2 == 0 && LA >= 1 && LB >= 1, "tiling");
   static_assert(S >= 2 && S <= 6 && L * (S - 2) < 64, "pipeline depth");
   static_assert(S * STAGE * 2 * WG_PER_CU_ <= 160 * 1024, "LDS");
+  static_assert(!F8 || (BK == 32 && MI * NJ <= 8 && NJ == 2 && CW == 64), "fp8 B tiling");
 };
 using BigCfg = Cfg<256, 256, 2, 4, 4, 1>;
+using BigCfg8 = Cfg<256, 256, 2, 4, 4, 1, 32, true>;
 
 constexpr int vmcnt_imm(int n) { return 0xF70 | (n & 15) | (((n >> 4) & 3) << 14); }
 
@@ -82,7 +94,13 @@ __device__ __forceinline__ void issue_stage(bf16* st, const bf16* abase, const u
 #pragma unroll
   for (int i = 0; i < C::LA; ++i) dma16(abase + (aoff[i] + k0), st + (C::NW * i + wave) * 512);
 #pragma unroll
-  for (int i = 0; i < C::LB; ++i) dma16(bbase[i] + (boff[i] + k0), st + C::BM * C::BK + (C::NW * i + wave) * 512);
+  for (int i = 0; i < C::LB; ++i) {
+    // fp8: bbase holds byte pointers, boff byte offsets (k0 counts codes)
+    if constexpr (C::F8)
+      dma16(reinterpret_cast<const uint8_t*>(bbase[i]) + (boff[i] + k0), st + C::BM * C::BK + (C::NW * i + wave) * 512);
+    else
+      dma16(bbase[i] + (boff[i] + k0), st + C::BM * C::BK + (C::NW * i + wave) * 512);
+  }
 }
 
 // Element offsets of this lane's fragment reads inside a stage for K sub-step
@@ -91,6 +109,7 @@ __device__ __forceinline__ void issue_stage(bf16* st, const bf16* abase, const u
 // fragment read is one of these plus a compile-time offset.
 struct FragOff {
   int a[4], b[4];  // per 16-wide K sub-step of a stage
+  int b8;          // fp8 B: byte offset of this lane's first code (block 0, chunk 0)
 };
 
 template <class C>
@@ -102,6 +121,7 @@ __device__ __forceinline__ FragOff frag_offsets(int wm, int wn, int lane) {
     o.a[ks] = lds_pos<C::BK>(wm * 32 + (lane & 31), c);
     o.b[ks] = lds_pos<C::BK>(C::BM + wn * C::CW + (lane & 31), c);
   }
+  o.b8 = C::BM * C::BK * 2 + wn * (C::CW / 32) * 1024 + (lane & 31) * 16 + 8 * (lane >> 5);
   return o;
 }
 
@@ -117,8 +137,33 @@ __device__ __forceinline__ void load_frags(const bf16* st, int ks, const FragOff
 
 // MFMAs of one stage: 2 K sub-steps of 16, fragments of both loaded first.
 template <class C, int NB>
-__device__ __forceinline__ void compute_stage(f32x16 (&acc)[C::MI][C::NJ], const bf16* st, const FragOff& o) {
-  if constexpr (C::MI * C::NJ > 8) {
+__device__ __forceinline__ void compute_stage(f32x16 (&acc)[C::MI][C::NJ], const bf16* st, const FragOff& o,
+                                              float sc0, float sc1) {
+  if constexpr (C::F8) {
+    // B block jj: 8 codes of row (lane % 32) at K 16*ks + 8*(lane/32), in
+    // chunk ks of its 32-row block; block 0 takes scale sc0, block 1 sc1
+    // (one K sub-step at a time: the decode's temporaries leave no room for
+    // both sub-steps' fragments next to the 128 accumulators)
+    const char* sb = reinterpret_cast<const char*>(st) + o.b8;
+#pragma unroll
+    for (int ks = 0; ks < C::BK / 16; ++ks) {
+      bf16x8 af[NB], bfr[C::NJ];
+      u32x2 codes[C::NJ];
+#pragma unroll
+      for (int jj = 0; jj < C::NJ; ++jj) codes[jj] = *reinterpret_cast<const u32x2*>(sb + jj * 1024 + ks * 512);
+#pragma unroll
+      for (int ii = 0; ii < NB; ++ii)
+        af[ii] = *reinterpret_cast<const bf16x8*>(st + o.a[ks] + ii * C::WM * 32 * C::BK);
+#pragma unroll
+      for (int jj = 0; jj < C::NJ; ++jj)
+        bfr[jj] = __builtin_bit_cast(bf16x8, fp8x8_to_bf16x8(codes[jj], jj == 0 ? sc0 : sc1));
+#pragma unroll
+      for (int ii = 0; ii < NB; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < C::NJ; ++jj)
+          acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ii], bfr[jj], acc[ii][jj], 0, 0, 0);
+    }
+  } else if constexpr (C::MI * C::NJ > 8) {
     // 128 x 128 wave tiles: one K sub-step of fragments at a time
 #pragma unroll
     for (int ks = 0; ks < C::BK / 16; ++ks) {
@@ -148,22 +193,28 @@ __device__ __forceinline__ void compute_stage(f32x16 (&acc)[C::MI][C::NJ], const
 // landed (the S-2 younger stages may stay in flight), one barrier (every
 // wave's loads landed, every wave done with buffer b-1), refill buffer b-1
 // with step s+S-1 (past the end: the last step again, never read), MFMAs.
+// fp8: sc0 / sc1 are this wave's two LDS scale rows (indexed by K block).
 template <class C, int NB, int B>
 __device__ __forceinline__ void step(f32x16 (&acc)[C::MI][C::NJ], bf16* const* stg, const bf16* abase,
                                      const uint32_t* aoff, const bf16* const* bbase, const uint32_t* boff, int s,
-                                     uint32_t klast, int wave, const FragOff& o) {
+                                     uint32_t klast, int wave, const FragOff& o, const float* sc0,
+                                     const float* sc1) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((C::S - 2) * C::L));
   block_sync();
   const uint32_t kn = (uint32_t)(s + C::S - 1) * C::BK;
   issue_stage<C>(stg[(B + C::S - 1) % C::S], abase, aoff, bbase, boff, kn < klast ? kn : klast, wave);
-  compute_stage<C, NB>(acc, stg[B], o);
+  if constexpr (C::F8)
+    compute_stage<C, NB>(acc, stg[B], o, __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                             __builtin_bit_cast(int, sc0[s >> 2]))),
+                         __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sc1[s >> 2]))));
+  else compute_stage<C, NB>(acc, stg[B], o, 0.f, 0.f);
 }
 
 // The K loop of one tile over nk steps, nk % S == R: step s uses buffer s % S.
 template <class C, int NB, int R>
 __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::MI][C::NJ], bf16* const* stg, const bf16* abase,
                                          const uint32_t* aoff, const bf16* const* bbase, const uint32_t* boff,
-                                         int nk, int wave, const FragOff& o) {
+                                         int nk, int wave, const FragOff& o, const float* sc0, const float* sc1) {
   const uint32_t klast = (uint32_t)(nk - 1) * C::BK;
   // every wave's loads (vmcnt(0) before the call) and LDS reads of the
   // previous tile are finished before its buffers are refilled
@@ -175,41 +226,44 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::MI][C::NJ], bf16* cons
   }
   const int nfull = nk - R;
   for (int kt = 0; kt < nfull; kt += C::S) {
-    step<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, kt + 0, klast, wave, o);
-    step<C, NB, 1>(acc, stg, abase, aoff, bbase, boff, kt + 1, klast, wave, o);
-    if constexpr (C::S > 2) step<C, NB, 2>(acc, stg, abase, aoff, bbase, boff, kt + 2, klast, wave, o);
-    if constexpr (C::S > 3) step<C, NB, 3>(acc, stg, abase, aoff, bbase, boff, kt + 3, klast, wave, o);
-    if constexpr (C::S > 4) step<C, NB, 4>(acc, stg, abase, aoff, bbase, boff, kt + 4, klast, wave, o);
-    if constexpr (C::S > 5) step<C, NB, 5>(acc, stg, abase, aoff, bbase, boff, kt + 5, klast, wave, o);
+    step<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, kt + 0, klast, wave, o, sc0, sc1);
+    step<C, NB, 1>(acc, stg, abase, aoff, bbase, boff, kt + 1, klast, wave, o, sc0, sc1);
+    if constexpr (C::S > 2) step<C, NB, 2>(acc, stg, abase, aoff, bbase, boff, kt + 2, klast, wave, o, sc0, sc1);
+    if constexpr (C::S > 3) step<C, NB, 3>(acc, stg, abase, aoff, bbase, boff, kt + 3, klast, wave, o, sc0, sc1);
+    if constexpr (C::S > 4) step<C, NB, 4>(acc, stg, abase, aoff, bbase, boff, kt + 4, klast, wave, o, sc0, sc1);
+    if constexpr (C::S > 5) step<C, NB, 5>(acc, stg, abase, aoff, bbase, boff, kt + 5, klast, wave, o, sc0, sc1);
   }
-  if constexpr (R > 0) step<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, nfull + 0, klast, wave, o);
-  if constexpr (R > 1) step<C, NB, 1>(acc, stg, abase, aoff, bbase, boff, nfull + 1, klast, wave, o);
-  if constexpr (R > 2) step<C, NB, 2>(acc, stg, abase, aoff, bbase, boff, nfull + 2, klast, wave, o);
-  if constexpr (R > 3) step<C, NB, 3>(acc, stg, abase, aoff, bbase, boff, nfull + 3, klast, wave, o);
-  if constexpr (R > 4) step<C, NB, 4>(acc, stg, abase, aoff, bbase, boff, nfull + 4, klast, wave, o);
+  if constexpr (R > 0) step<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, nfull + 0, klast, wave, o, sc0, sc1);
+  if constexpr (R > 1) step<C, NB, 1>(acc, stg, abase, aoff, bbase, boff, nfull + 1, klast, wave, o, sc0, sc1);
+  if constexpr (R > 2) step<C, NB, 2>(acc, stg, abase, aoff, bbase, boff, nfull + 2, klast, wave, o, sc0, sc1);
+  if constexpr (R > 3) step<C, NB, 3>(acc, stg, abase, aoff, bbase, boff, nfull + 3, klast, wave, o, sc0, sc1);
+  if constexpr (R > 4) step<C, NB, 4>(acc, stg, abase, aoff, bbase, boff, nfull + 4, klast, wave, o, sc0, sc1);
 }
 
 template <class C, int NB>
 __device__ __forceinline__ void mainloop_r(f32x16 (&acc)[C::MI][C::NJ], bf16* const* stg, const bf16* abase,
                                            const uint32_t* aoff, const bf16* const* bbase, const uint32_t* boff,
-                                           int nk, int wave, const FragOff& o) {
+                                           int nk, int wave, const FragOff& o, const float* sc0, const float* sc1) {
   const int r = nk % C::S;
-  if (r == 0) mainloop<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, nk, wave, o);
-  else if (C::S > 1 && r == 1) mainloop<C, NB, 1 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, o);
-  else if (C::S > 2 && r == 2) mainloop<C, NB, 2 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, o);
-  else if (C::S > 3 && r == 3) mainloop<C, NB, 3 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, o);
-  else if (C::S > 4 && r == 4) mainloop<C, NB, 4 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, o);
-  else mainloop<C, NB, 5 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, o);
+  if (r == 0) mainloop<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, nk, wave, o, sc0, sc1);
+  else if (C::S > 1 && r == 1) mainloop<C, NB, 1 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, o, sc0, sc1);
+  else if (C::S > 2 && r == 2) mainloop<C, NB, 2 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, o, sc0, sc1);
+  else if (C::S > 3 && r == 3) mainloop<C, NB, 3 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, o, sc0, sc1);
+  else if (C::S > 4 && r == 4) mainloop<C, NB, 4 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, o, sc0, sc1);
+  else mainloop<C, NB, 5 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, o, sc0, sc1);
 }
 
+// m-tiles [plan[begin], plan[end]) of the plan's first list (begin < 0: from 0)
 template <class C, int MODE>
-__global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArgs f, int n_tiles_n, int super) {
+__global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArgs f, int n_tiles_n, int super,
+                                                                          int list_begin_idx, int list_end_idx) {
   __shared__ __attribute__((aligned(1024))) bf16 s0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) bf16 s1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) bf16 s2[C::S > 2 ? C::STAGE : 8];
   __shared__ __attribute__((aligned(1024))) bf16 s3[C::S > 3 ? C::STAGE : 8];
   __shared__ __attribute__((aligned(1024))) bf16 s4[C::S > 4 ? C::STAGE : 8];
   __shared__ __attribute__((aligned(1024))) bf16 s5[C::S > 5 ? C::STAGE : 8];
+  __shared__ float ssc[C::F8 ? 256 : 1];  // fp8: two rows of K-block scales
   bf16* const stg[6] = {s0, s1, s2, s3, s4, s5};
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -217,7 +271,9 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArg
   const int wm = wave / C::WN, wn = wave % C::WN;
   const FragOff fo = frag_offsets<C>(wm, wn, lane);
 
-  const int MT = f.plan[0];  // m-tiles: routed groups, then the shared expert
+  // m-tiles: routed groups, then the shared expert (fp8: routed ones only)
+  const int mt_first = list_begin_idx < 0 ? 0 : f.plan[list_begin_idx];
+  const int MT = f.plan[list_end_idx] - mt_first;
   const int total = MT * n_tiles_n;
   const int G = gridDim.x;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -230,7 +286,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArg
     const int grp = MT - sbase < super ? MT - sbase : super;
     const int r = t - sbase * n_tiles_n;
     const int nt = r / grp;
-    const int mt = sbase + r % grp;
+    const int mt = mt_first + sbase + r % grp;
 
     const int g = f.mt_group[mt];
     const int r0 = f.mt_row0[mt];
@@ -277,23 +333,71 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArg
     }
 #pragma unroll
     for (int i = 0; i < C::LB; ++i) {
-      const int grow0 = (C::NW * i + wave) * C::RPL;  // wave-uniform first row of the load
-      const int n = grow0 + lrow;                       // B tile row
-      const int gchunk = lpos ^ swz<C::BK>(n);
-      int col;
-      if (MODE == 1) {
-        // wave column wc (CW rows) holds CW/2 gate rows, then the up rows of
-        // the same CW/2 hidden columns
-        const bool up = (grow0 % C::CW) >= C::CW / 2;
-        col = nt * (C::BN / 2) + (n / C::CW) * (C::CW / 2) + (n % (C::CW / 2));
-        bbase[i] = shared ? reinterpret_cast<const bf16*>(up ? f.shu : f.shg)
-                          : reinterpret_cast<const bf16*>(up ? f.wu : f.wg) + (int64_t)g * (up ? f.su : f.sg);
+      if constexpr (C::F8) {
+        // load i of wave w fills B rows (NW*i + w)*32 .. +32 as [chunk][row]:
+        // lane l takes row +l%32, 16-byte chunk l/32 of the 32-code K slice
+        const int grow0 = (C::NW * i + wave) * C::RPL8;
+        const int n = grow0 + (lane & 31);
+        const int ch = lane >> 5;
+        int col;
+        const uint8_t* mat;
+        if (MODE == 1) {
+          const bool up = (grow0 % C::CW) >= C::CW / 2;
+          col = nt * (C::BN / 2) + (n / C::CW) * (C::CW / 2) + (n % (C::CW / 2));
+          mat = reinterpret_cast<const uint8_t*>(up ? f.wu : f.wg) + (int64_t)g * (up ? f.su : f.sg);
+        } else {
+          col = nt * C::BN + n;
+          mat = reinterpret_cast<const uint8_t*>(f.wd) + (int64_t)g * f.sd;
+        }
+        col = col < Ncols ? col : Ncols - 1;
+        bbase[i] = reinterpret_cast<const bf16*>(mat);
+        boff[i] = (uint32_t)col * (uint32_t)K + ch * 16;
       } else {
-        col = nt * C::BN + n;
-        bbase[i] = shared ? reinterpret_cast<const bf16*>(f.shd) : reinterpret_cast<const bf16*>(f.wd) + (int64_t)g * f.sd;
+        const int grow0 = (C::NW * i + wave) * C::RPL;  // wave-uniform first row of the load
+        const int n = grow0 + lrow;                       // B tile row
+        const int gchunk = lpos ^ swz<C::BK>(n);
+        int col;
+        if (MODE == 1) {
+          // wave column wc (CW rows) holds CW/2 gate rows, then the up rows of
+          // the same CW/2 hidden columns
+          const bool up = (grow0 % C::CW) >= C::CW / 2;
+          col = nt * (C::BN / 2) + (n / C::CW) * (C::CW / 2) + (n % (C::CW / 2));
+          bbase[i] = shared ? reinterpret_cast<const bf16*>(up ? f.shu : f.shg)
+                            : reinterpret_cast<const bf16*>(up ? f.wu : f.wg) + (int64_t)g * (up ? f.su : f.sg);
+        } else {
+          col = nt * C::BN + n;
+          bbase[i] = shared ? reinterpret_cast<const bf16*>(f.shd) : reinterpret_cast<const bf16*>(f.wd) + (int64_t)g * f.sd;
+        }
+        col = col < Ncols ? col : Ncols - 1;
+        boff[i] = (uint32_t)col * (uint32_t)K + gchunk * 8;
       }
-      col = col < Ncols ? col : Ncols - 1;
-      boff[i] = (uint32_t)col * (uint32_t)K + gchunk * 8;
+    }
+
+    // fp8: the tile's block scales, K block kb of row sel at ssc[sel*nkb + kb]
+    // (gate/up: sel 0 gate, 1 up, of hidden block nt; down: W_down row
+    // blocks 2nt and 2nt+1, the second clamped at the last)
+    const float* sc0 = nullptr;
+    const float* sc1 = nullptr;
+    if constexpr (C::F8) {
+      const int nkb = K / 128;
+      for (int t = tid; t < 2 * nkb; t += C::NT) {
+        const int sel = t / nkb, kb = t - sel * nkb;
+        float v;
+        if (MODE == 1) {
+          v = (sel ? f.scu : f.scg)[((int64_t)g * (f.I / 128) + nt) * nkb + kb];
+        } else {
+          int rb = 2 * nt + sel;
+          rb = rb < f.H / 128 ? rb : f.H / 128 - 1;
+          v = f.scd[((int64_t)g * (f.H / 128) + rb) * nkb + kb];
+        }
+        ssc[t] = v;
+      }
+      if (MODE == 1) {
+        sc0 = ssc;
+        sc1 = ssc + nkb;
+      } else {
+        sc0 = sc1 = ssc + (wn * C::CW / 128) * nkb;
+      }
     }
 
     f32x16 acc[C::MI][C::NJ];
@@ -310,13 +414,13 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArg
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // previous tile's loads and stores settled
     const int nk = K / C::BK;
     if constexpr (C::MI >= 4) {
-      if (nb >= 4) mainloop_r<C, 4>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo);
-      else if (nb == 3) mainloop_r<C, 3>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo);
-      else if (nb == 2) mainloop_r<C, 2>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo);
-      else mainloop_r<C, 1>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo);
+      if (nb >= 4) mainloop_r<C, 4>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo, sc0, sc1);
+      else if (nb == 3) mainloop_r<C, 3>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo, sc0, sc1);
+      else if (nb == 2) mainloop_r<C, 2>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo, sc0, sc1);
+      else mainloop_r<C, 1>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo, sc0, sc1);
     } else {
-      if (nb >= 2) mainloop_r<C, 2>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo);
-      else mainloop_r<C, 1>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo);
+      if (nb >= 2) mainloop_r<C, 2>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo, sc0, sc1);
+      else mainloop_r<C, 1>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo, sc0, sc1);
     }
 
     // ---- epilogue through LDS ----
@@ -389,7 +493,7 @@ int cu_count() {
 }
 
 template <class C>
-hipError_t launch(const FfnArgs& a, int phase, hipStream_t s) {
+hipError_t launch(const FfnArgs& a, int phase, hipStream_t s, int list_begin_idx, int list_end_idx) {
   const int wide = a.I > a.Is ? a.I : a.Is;
   const int ntn = phase == 1 ? (wide + C::BN / 2 - 1) / (C::BN / 2) : (a.H + C::BN - 1) / C::BN;
   const int grid = (cu_count() * C::WG_PER_CU + 7) / 8 * 8;  // resident workgroups, a multiple of 8 XCDs
@@ -398,8 +502,8 @@ hipError_t launch(const FfnArgs& a, int phase, hipStream_t s) {
   // m-tiles x all n-tiles per XCD, which fetches each A slice once, measured
   // slower on the 8192-token skewed layer.)
   const int super = 8;
-  if (phase == 1) dma_gemm_kernel<C, 1><<<grid, C::NT, 0, s>>>(a, ntn, super);
-  else dma_gemm_kernel<C, 2><<<grid, C::NT, 0, s>>>(a, ntn, super);
+  if (phase == 1) dma_gemm_kernel<C, 1><<<grid, C::NT, 0, s>>>(a, ntn, super, list_begin_idx, list_end_idx);
+  else dma_gemm_kernel<C, 2><<<grid, C::NT, 0, s>>>(a, ntn, super, list_begin_idx, list_end_idx);
   return hipGetLastError();
 }
 
@@ -407,9 +511,19 @@ hipError_t launch(const FfnArgs& a, int phase, hipStream_t s) {
 
 bool ffn_dma_supported(const FfnArgs& a) {
   constexpr int k = BigCfg::BK;
-  return !a.fp8 && a.H % k == 0 && a.I % k == 0 && (a.Is == 0 || a.Is % k == 0);
+  if (a.Is != 0 && a.Is % k != 0) return false;
+  // fp8: whole 128 x 128 scale blocks, at most 128 K blocks (the LDS scale table)
+  if (a.fp8) return a.H % 128 == 0 && a.I % 128 == 0 && a.H <= 128 * 128 && a.I <= 128 * 128;
+  return a.H % k == 0 && a.I % k == 0;
 }
 
-hipError_t launch_ffn_gemm_dma(const FfnArgs& a, int phase, hipStream_t s) { return launch<BigCfg>(a, phase, s); }
+hipError_t launch_ffn_gemm_dma(const FfnArgs& a, int phase, hipStream_t s) {
+  if (!a.fp8) return launch<BigCfg>(a, phase, s, -1, 0);
+  // fp8 layers: routed m-tiles [0, plan[2]) decode codes, the shared
+  // expert's [plan[2], plan[0]) are bf16
+  hipError_t e = launch<BigCfg8>(a, phase, s, -1, 2);
+  if (e == hipSuccess && a.Is > 0) e = launch<BigCfg>(a, phase, s, 2, 0);
+  return e;
+}
 
 }  // namespace moe

@@ -184,6 +184,22 @@ def test_256_row_tiles_with_128_row_remainders():
     check(p, g)
 
 
+@pytest.mark.parametrize("shared", [0, 128])
+@pytest.mark.parametrize("force", [0, lib.MOE_FLAG_FORCE_GEMM])
+def test_fp8_256_row_tiles(shared, force):
+    # fp8 codes through the 256-row direct-load tiles: several K blocks of
+    # scales (H = 384, I = 256), the last W_down row block of a tile past H
+    # (its scales clamped), ragged remainders in the 128-row fp8 tiles, the
+    # shared expert in bf16 tiles of both kernels
+    cfg = CONFIGS["max_fp8"].with_(name="fp8_tiles", T=1536, H=384, E=8, k=2, I=256, I_shared=shared,
+                                   zipf_s=1.1)
+    p = gpu_problem(cfg, 14)
+    g = run_stages(p, lib.MOE_FLAG_GEMM_TILE_256 | force)
+    n = np.diff(g["offsets"])
+    assert np.any(n >= 256) and np.any((n % 256 > 0) & (n % 256 <= 128))
+    check(p, g)
+
+
 def test_one_expert_takes_every_token():
     # a steep per-expert bias: the rank-1 expert wins every token (k = 1)
     cfg = CONFIGS["max_prefill"].with_(name="all_to_one", T=300, H=256, E=8, k=1, I=128, I_shared=64, zipf_s=8.0)
