@@ -353,31 +353,72 @@ __global__ __launch_bounds__(NT, BKT == 32 ? 3 : 2) void gemm_kernel(FfnArgs f, 
 
     // ---------------- epilogue ----------------
     // C fragment: lane holds column (lane & 31), rows 8*(v/4) + 4*(lane/32) + v%4.
+    if constexpr (MODE != M_ROUTER && BKT == 64) {
+      // Through LDS (the K loop ended with a barrier, so sA is free): the
+      // tile goes into sA as bf16 (gate/up: SiLU(g)*u), then every thread
+      // stores whole 16-byte row chunks (bf16 rows are multiples of 8
+      // elements).  Chunk c of row r sits at c ^ (4 * ((r >> 2) & 1)), so the
+      // two half-waves' rows (4 apart) write different banks.
+      constexpr int CC = MODE == M_GATEUP ? 64 : BN;  // output columns of the tile
+      constexpr int CPRO = CC / 8;                   // 16-byte chunks per row
+      static_assert(BM * CC <= 2 * BM * BKT, "the C tile fits the A buffers");
+      auto cpos = [](int r, int col) { return r * CC + (((col >> 3) ^ (((r >> 2) & 1) << 2)) << 3) + (col & 7); };
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < 2; ++i) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rl = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (rl >= nrows) continue;
-        const int64_t gr = base + r0 + rl;
-        if (MODE == M_GATEUP) {
-          const int col = nt * 64 + wn * 32 + (lane & 31);
-          if (col < Ncols) {
-            const float hv = silu(acc[i][0][v]) * acc[i][1][v];
-            bf16* dst = shared ? reinterpret_cast<bf16*>(f.h_sh) + gr * f.Is
-                               : reinterpret_cast<bf16*>(f.h) + gr * f.I;
-            dst[col] = f2bf(hv);
+        for (int v = 0; v < 16; ++v) {
+          const int rl = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (MODE == M_GATEUP) {
+            sA[cpos(rl, wn * 32 + (lane & 31))] = f2bf(silu(acc[i][0][v]) * acc[i][1][v]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) sA[cpos(rl, wn * 64 + j * 32 + (lane & 31))] = f2bf(acc[i][j][v]);
           }
-        } else {
+        }
+      }
+      __syncthreads();
+      bf16* obase;
+      int ld;
+      if (MODE == M_GATEUP) {
+        obase = shared ? reinterpret_cast<bf16*>(f.h_sh) : reinterpret_cast<bf16*>(f.h);
+        ld = shared ? f.Is : f.I;
+      } else {
+        obase = shared ? reinterpret_cast<bf16*>(f.y_sh) : reinterpret_cast<bf16*>(f.y);
+        ld = f.H;
+      }
+      for (int q = tid; q < BM * CPRO; q += NT) {
+        const int r = q / CPRO, c = q % CPRO;
+        const int col = nt * CC + c * 8;
+        if (r < nrows && col < Ncols) st16(obase + (int64_t)(base + r0 + r) * ld + col, ld16(sA + cpos(r, c * 8)));
+      }
+      __syncthreads();  // sA is read out before the next tile refills it
+    } else {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = nt * BN + wn * 64 + j * 32 + (lane & 31);
-            if (col >= Ncols) continue;
-            if (MODE == M_ROUTER) {
-              ra.logits[((int64_t)kc * ra.T + gr) * ra.N + col] = acc[i][j][v];
-            } else {
-              bf16* dst = shared ? reinterpret_cast<bf16*>(f.y_sh) : reinterpret_cast<bf16*>(f.y);
-              dst[gr * f.H + col] = f2bf(acc[i][j][v]);
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rl = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (rl >= nrows) continue;
+          const int64_t gr = base + r0 + rl;
+          if (MODE == M_GATEUP) {
+            const int col = nt * 64 + wn * 32 + (lane & 31);
+            if (col < Ncols) {
+              const float hv = silu(acc[i][0][v]) * acc[i][1][v];
+              bf16* dst = shared ? reinterpret_cast<bf16*>(f.h_sh) + gr * f.Is
+                                 : reinterpret_cast<bf16*>(f.h) + gr * f.I;
+              dst[col] = f2bf(hv);
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int col = nt * BN + wn * 64 + j * 32 + (lane & 31);
+              if (col >= Ncols) continue;
+              if (MODE == M_ROUTER) {
+                ra.logits[((int64_t)kc * ra.T + gr) * ra.N + col] = acc[i][j][v];
+              } else {
+                bf16* dst = shared ? reinterpret_cast<bf16*>(f.y_sh) : reinterpret_cast<bf16*>(f.y);
+                dst[gr * f.H + col] = f2bf(acc[i][j][v]);
+              }
             }
           }
         }
