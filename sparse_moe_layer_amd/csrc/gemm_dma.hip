@@ -62,7 +62,7 @@ struct Cfg {
   static_assert(MI >= 1 && NJ >= 2 && NJ % 2 == 0 && LA >= 1 && LB >= 1, "tiling");
   static_assert(S >= 2 && S <= 6 && L * (S - 2) < 64, "pipeline depth");
   static_assert(S * STAGE * 2 * WG_PER_CU_ <= 160 * 1024, "LDS");
-  static_assert(!F8 || (BK == 32 && MI * NJ <= 8 && NJ == 2 && CW == 64), "fp8 B tiling");
+  static_assert(!F8 || (BK == 32 && S == 4 && MI * NJ <= 8 && NJ == 2 && CW == 64), "fp8 B tiling");
 };
 using BigCfg = Cfg<256, 256, 2, 4, 4, 1>;
 using BigCfg8 = Cfg<256, 256, 2, 4, 4, 1, 32, true>;
@@ -145,24 +145,44 @@ __device__ __forceinline__ void compute_stage(f32x16 (&acc)[C::MI][C::NJ], const
     // (one K sub-step at a time: the decode's temporaries leave no room for
     // both sub-steps' fragments next to the 128 accumulators)
     const char* sb = reinterpret_cast<const char*>(st) + o.b8;
+    constexpr int KS = C::BK / 16;
+    bf16x8 af[KS][NB], bfr[KS][C::NJ];
+    u32x2 codes[KS][C::NJ];
 #pragma unroll
-    for (int ks = 0; ks < C::BK / 16; ++ks) {
-      bf16x8 af[NB], bfr[C::NJ];
-      u32x2 codes[C::NJ];
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int jj = 0; jj < C::NJ; ++jj) codes[jj] = *reinterpret_cast<const u32x2*>(sb + jj * 1024 + ks * 512);
+      for (int jj = 0; jj < C::NJ; ++jj) codes[ks][jj] = *reinterpret_cast<const u32x2*>(sb + jj * 1024 + ks * 512);
 #pragma unroll
       for (int ii = 0; ii < NB; ++ii)
-        af[ii] = *reinterpret_cast<const bf16x8*>(st + o.a[ks] + ii * C::WM * 32 * C::BK);
+        af[ks][ii] = *reinterpret_cast<const bf16x8*>(st + o.a[ks] + ii * C::WM * 32 * C::BK);
 #pragma unroll
       for (int jj = 0; jj < C::NJ; ++jj)
-        bfr[jj] = __builtin_bit_cast(bf16x8, fp8x8_to_bf16x8(codes[jj], jj == 0 ? sc0 : sc1));
+        bfr[ks][jj] = __builtin_bit_cast(bf16x8, fp8x8_to_bf16x8(codes[ks][jj], jj == 0 ? sc0 : sc1));
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int ii = 0; ii < NB; ++ii)
 #pragma unroll
         for (int jj = 0; jj < C::NJ; ++jj)
-          acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ii], bfr[jj], acc[ii][jj], 0, 0, 0);
+          acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][ii], bfr[ks][jj], acc[ii][jj], 0, 0, 0);
+    // Schedule as in the bf16 path, with each sub-step's decode (VALU) placed
+    // among the previous sub-step's MFMAs.
+    constexpr int NR = NB + C::NJ;  // fragment reads per sub-step
+    constexpr int NM = NB * C::NJ;  // MFMAs per sub-step
+    constexpr int NV = 16 * C::NJ;  // decode instructions per sub-step
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+#pragma unroll
+    for (int ks = 0; ks + 1 < KS; ++ks) {
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, NV / NM, 0);
+      }
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
   } else if constexpr (C::MI * C::NJ > 8) {
     // 128 x 128 wave tiles: one K sub-step of fragments at a time
 #pragma unroll
@@ -186,6 +206,25 @@ __device__ __forceinline__ void compute_stage(f32x16 (&acc)[C::MI][C::NJ], const
 #pragma unroll
         for (int jj = 0; jj < C::NJ; ++jj)
           acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][ii], bfr[ks][jj], acc[ii][jj], 0, 0, 0);
+    // Schedule: sub-step 0's fragment reads, then each sub-step's MFMAs
+    // alternating with the next sub-step's reads, so LDS latency hides under
+    // MFMAs (left alone, the compiler reuses one set of fragment registers
+    // and waits on LDS before every few MFMAs).
+    constexpr int NR = NB + C::NJ;  // fragment reads per sub-step
+    constexpr int NM = NB * C::NJ;  // MFMAs per sub-step
+    constexpr int NP = NR < NM ? NR : NM;
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+    for (int ks = 0; ks + 1 < C::BK / 16; ++ks) {
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if constexpr (NM > NP) __builtin_amdgcn_sched_group_barrier(0x008, NM - NP, 0);
+      if constexpr (NR > NP) __builtin_amdgcn_sched_group_barrier(0x100, NR - NP, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
   }
 }
 
@@ -193,21 +232,23 @@ __device__ __forceinline__ void compute_stage(f32x16 (&acc)[C::MI][C::NJ], const
 // landed (the S-2 younger stages may stay in flight), one barrier (every
 // wave's loads landed, every wave done with buffer b-1), refill buffer b-1
 // with step s+S-1 (past the end: the last step again, never read), MFMAs.
-// fp8: sc0 / sc1 are this wave's two LDS scale rows (indexed by K block).
+// fp8: sc0 / sc1 are this wave's two LDS scale rows (indexed by K block);
+// with four stages of 32-wide K steps, stage 0 starts each 128-wide K block,
+// where the block's two scales are read into scl0 / scl1.
 template <class C, int NB, int B>
 __device__ __forceinline__ void step(f32x16 (&acc)[C::MI][C::NJ], bf16* const* stg, const bf16* abase,
                                      const uint32_t* aoff, const bf16* const* bbase, const uint32_t* boff, int s,
                                      uint32_t klast, int wave, const FragOff& o, const float* sc0,
-                                     const float* sc1) {
+                                     const float* sc1, float& scl0, float& scl1) {
+  if constexpr (C::F8 && B == 0) {
+    scl0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sc0[s >> 2])));
+    scl1 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sc1[s >> 2])));
+  }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((C::S - 2) * C::L));
   block_sync();
   const uint32_t kn = (uint32_t)(s + C::S - 1) * C::BK;
   issue_stage<C>(stg[(B + C::S - 1) % C::S], abase, aoff, bbase, boff, kn < klast ? kn : klast, wave);
-  if constexpr (C::F8)
-    compute_stage<C, NB>(acc, stg[B], o, __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
-                                             __builtin_bit_cast(int, sc0[s >> 2]))),
-                         __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sc1[s >> 2]))));
-  else compute_stage<C, NB>(acc, stg[B], o, 0.f, 0.f);
+  compute_stage<C, NB>(acc, stg[B], o, scl0, scl1);
 }
 
 // The K loop of one tile over nk steps, nk % S == R: step s uses buffer s % S.
@@ -216,6 +257,7 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::MI][C::NJ], bf16* cons
                                          const uint32_t* aoff, const bf16* const* bbase, const uint32_t* boff,
                                          int nk, int wave, const FragOff& o, const float* sc0, const float* sc1) {
   const uint32_t klast = (uint32_t)(nk - 1) * C::BK;
+  float scl0 = 0.f, scl1 = 0.f;  // fp8: the current K block's scales
   // every wave's loads (vmcnt(0) before the call) and LDS reads of the
   // previous tile are finished before its buffers are refilled
   block_sync();
@@ -226,18 +268,18 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::MI][C::NJ], bf16* cons
   }
   const int nfull = nk - R;
   for (int kt = 0; kt < nfull; kt += C::S) {
-    step<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, kt + 0, klast, wave, o, sc0, sc1);
-    step<C, NB, 1>(acc, stg, abase, aoff, bbase, boff, kt + 1, klast, wave, o, sc0, sc1);
-    if constexpr (C::S > 2) step<C, NB, 2>(acc, stg, abase, aoff, bbase, boff, kt + 2, klast, wave, o, sc0, sc1);
-    if constexpr (C::S > 3) step<C, NB, 3>(acc, stg, abase, aoff, bbase, boff, kt + 3, klast, wave, o, sc0, sc1);
-    if constexpr (C::S > 4) step<C, NB, 4>(acc, stg, abase, aoff, bbase, boff, kt + 4, klast, wave, o, sc0, sc1);
-    if constexpr (C::S > 5) step<C, NB, 5>(acc, stg, abase, aoff, bbase, boff, kt + 5, klast, wave, o, sc0, sc1);
+    step<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, kt + 0, klast, wave, o, sc0, sc1, scl0, scl1);
+    step<C, NB, 1>(acc, stg, abase, aoff, bbase, boff, kt + 1, klast, wave, o, sc0, sc1, scl0, scl1);
+    if constexpr (C::S > 2) step<C, NB, 2>(acc, stg, abase, aoff, bbase, boff, kt + 2, klast, wave, o, sc0, sc1, scl0, scl1);
+    if constexpr (C::S > 3) step<C, NB, 3>(acc, stg, abase, aoff, bbase, boff, kt + 3, klast, wave, o, sc0, sc1, scl0, scl1);
+    if constexpr (C::S > 4) step<C, NB, 4>(acc, stg, abase, aoff, bbase, boff, kt + 4, klast, wave, o, sc0, sc1, scl0, scl1);
+    if constexpr (C::S > 5) step<C, NB, 5>(acc, stg, abase, aoff, bbase, boff, kt + 5, klast, wave, o, sc0, sc1, scl0, scl1);
   }
-  if constexpr (R > 0) step<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, nfull + 0, klast, wave, o, sc0, sc1);
-  if constexpr (R > 1) step<C, NB, 1>(acc, stg, abase, aoff, bbase, boff, nfull + 1, klast, wave, o, sc0, sc1);
-  if constexpr (R > 2) step<C, NB, 2>(acc, stg, abase, aoff, bbase, boff, nfull + 2, klast, wave, o, sc0, sc1);
-  if constexpr (R > 3) step<C, NB, 3>(acc, stg, abase, aoff, bbase, boff, nfull + 3, klast, wave, o, sc0, sc1);
-  if constexpr (R > 4) step<C, NB, 4>(acc, stg, abase, aoff, bbase, boff, nfull + 4, klast, wave, o, sc0, sc1);
+  if constexpr (R > 0) step<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, nfull + 0, klast, wave, o, sc0, sc1, scl0, scl1);
+  if constexpr (R > 1) step<C, NB, 1>(acc, stg, abase, aoff, bbase, boff, nfull + 1, klast, wave, o, sc0, sc1, scl0, scl1);
+  if constexpr (R > 2) step<C, NB, 2>(acc, stg, abase, aoff, bbase, boff, nfull + 2, klast, wave, o, sc0, sc1, scl0, scl1);
+  if constexpr (R > 3) step<C, NB, 3>(acc, stg, abase, aoff, bbase, boff, nfull + 3, klast, wave, o, sc0, sc1, scl0, scl1);
+  if constexpr (R > 4) step<C, NB, 4>(acc, stg, abase, aoff, bbase, boff, nfull + 4, klast, wave, o, sc0, sc1, scl0, scl1);
 }
 
 template <class C, int NB>
