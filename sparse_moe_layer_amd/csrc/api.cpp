@@ -103,7 +103,7 @@ LayerWs layer_layout(const moe_problem* p, void* base) {
 // ---------------------------------------------------------------------------
 moe_status check_problem(const moe_problem* p) {
   if (!p) return MOE_ERR_NULL;
-  if (p->T < 0 || p->H < 1 || p->E < 1 || p->E > 1024 || p->k < 1 || p->k > p->E || p->k > 64 || p->I < 1 ||
+  if (p->T < 0 || p->H < 1 || p->E < 1 || p->E > moe::kMaxExperts || p->k < 1 || p->k > p->E || p->k > 64 || p->I < 1 ||
       p->I_shared < 0)
     return MOE_ERR_SHAPE;
   if (p->T > (int64_t)INT32_MAX / p->k || p->H > (1 << 24) || p->I > (1 << 24) || p->I_shared > (1 << 24))
@@ -238,16 +238,22 @@ moe_status run_ffn(const moe_problem* p, FfnArgs& a, int phases, void* plan_ws, 
   if (p->act_dtype == MOE_F32) return hip_status(moe::launch_ffn_f32(a, phases, s));
   int32_t* plan = static_cast<int32_t*>(plan_ws);
   const bool big = use_big_tiles(p, a);
-  if (moe::launch_ffn_plan(a.offsets, a.sorted, a.T, a.E, a.k, a.Is > 0 ? 1 : 0, p->flags,
-                           big ? moe::kGemmBigBM : moe::kGemmBM, plan, s) != hipSuccess)
-    return MOE_ERR_HIP;
-  moe::ffn_bind_plan(a, plan);
   // A group holds at most T rows, so with T <= kStreamMaxRows no group can
   // reach the GEMM path unless it is forced; with the GEMM path forced no
   // group streams.  Launches that cannot have work are skipped.
   const bool any_gemm = (p->flags & MOE_FLAG_FORCE_GEMM) ||
                         (!(p->flags & MOE_FLAG_FORCE_STREAM) && p->T > moe::kStreamMaxRows);
   const bool any_stream = !(p->flags & MOE_FLAG_FORCE_GEMM);
+  // Every group streaming as one m-block (T <= kStreamMaxRows): the
+  // streaming kernels list the groups themselves, with no plan kernel ahead
+  // of them in the chain.
+  const bool self_plan = !any_gemm && p->T <= moe::kStreamMaxRows;
+  if (!self_plan) {
+    if (moe::launch_ffn_plan(a.offsets, a.sorted, a.T, a.E, a.k, a.Is > 0 ? 1 : 0, p->flags,
+                             big ? moe::kGemmBigBM : moe::kGemmBM, plan, s) != hipSuccess)
+      return MOE_ERR_HIP;
+    moe::ffn_bind_plan(a, plan);
+  }
   for (int phase = 1; phase <= 2; ++phase) {
     if (!(phases & phase)) continue;
     if (any_gemm) {
@@ -256,7 +262,7 @@ moe_status run_ffn(const moe_problem* p, FfnArgs& a, int phases, void* plan_ws, 
       if (e != hipSuccess) return MOE_ERR_HIP;
       if (big && moe::launch_ffn_gemm(a, phase, s, 4, 5) != hipSuccess) return MOE_ERR_HIP;
     }
-    if (any_stream && moe::launch_ffn_stream(a, phase, s) != hipSuccess) return MOE_ERR_HIP;
+    if (any_stream && moe::launch_ffn_stream(a, phase, s, self_plan) != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;
 }

@@ -13,6 +13,7 @@ namespace moe {
 constexpr int kGemmBM = 128;
 constexpr int kGemmBigBM = 256;
 constexpr int kStreamBM = 16;
+constexpr int kMaxExperts = 1024;
 // plan ints ahead of the work lists: [0] m-tiles of the first list, [1] stream
 // m-blocks, [2] / [3] where the shared expert's m-tiles / m-blocks begin,
 // [4, 5) the second m-tile list (128-row remainders of 256-row tiling)
@@ -81,7 +82,9 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s, int list_
 // I_shared multiples of 32).
 bool ffn_dma_supported(const FfnArgs& a);
 hipError_t launch_ffn_gemm_dma(const FfnArgs& a, int phase, hipStream_t s);
-hipError_t launch_ffn_stream(const FfnArgs& a, int phase, hipStream_t s);  // phase 1 gate/up, 2 down
+// phase 1 gate/up, 2 down.  self_plan: T <= kStreamMaxRows and no plan kernel
+// ran; the kernels list the touched groups from the offsets themselves.
+hipError_t launch_ffn_stream(const FfnArgs& a, int phase, hipStream_t s, bool self_plan = false);
 hipError_t launch_ffn_f32(const FfnArgs& a, int phases, hipStream_t s);  // bit 0 gate/up, bit 1 down
 hipError_t launch_combine(const void* y, const int32_t* pos, const float* w, const void* y_sh,
                           const float* shared_logit, void* out, int T, int H, int k, int f32,

@@ -317,18 +317,53 @@ __device__ __forceinline__ void stream_dot_lds8(const bf16* a_row, const bf16* a
 // (decode) and cost a few percent on large streaming tails, where 16-column
 // items (a 16-row gate block and a 16-row up block) keep more bytes in
 // flight per wave.  Down items are 32 output columns (2 blocks).
+//
+// SELF_PLAN (batches of at most kStreamMaxRows tokens, where every group
+// streams as one m-block): no plan kernel runs before the launch; each
+// workgroup lists the touched groups itself, in ascending order with the
+// shared expert last, from the expert offsets (the plan's stream list for
+// such a batch).  List positions: begin -1 = 0, index 3 = the routed
+// groups' count, index 1 = all groups (the plan's [3] and [1]).
 template <int PHASE, bool FP8, bool SPLIT = false>
-__global__ __launch_bounds__(WAVES * 64, 2) void stream_kernel(FfnArgs f, int list_begin_idx, int list_end_idx) {
+__global__ __launch_bounds__(WAVES * 64, 2) void stream_kernel(FfnArgs f, int list_begin_idx, int list_end_idx,
+                                                               int self_plan) {
   static_assert(!SPLIT || (PHASE == 1 && !FP8), "split items are bf16 gate/up");
   constexpr int NB = SPLIT ? 1 : 2;
   constexpr int STAGE_BYTES = NB * 8 * (FP8 ? PAIR8 : PAIR);  // per wave
   __shared__ __attribute__((aligned(16))) char stage[WAVES * STAGE_BYTES];
+  __shared__ int glist[kMaxExperts + 1];  // SELF_PLAN: touched groups
+  __shared__ int wtot[WAVES];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int gw = blockIdx.x * WAVES + (threadIdx.x >> 6);
   const int nw = gridDim.x * WAVES;
-  const int sb_begin = list_begin_idx < 0 ? 0 : f.plan[list_begin_idx];
-  const int sb_end = f.plan[list_end_idx];
+  int sb_begin, sb_end;
+  if (self_plan) {
+    // ordered compaction of the routed groups with rows, 64*WAVES at a time:
+    // a wave's ballot gives each lane its rank, the waves' totals its offset
+    int n_routed = 0;
+    for (int g0 = 0; g0 < f.E; g0 += WAVES * 64) {
+      const int g = g0 + threadIdx.x;
+      const bool t = g < f.E && f.offsets[g + 1] > f.offsets[g];
+      const uint64_t bal = __ballot(t);
+      const int rank = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) wtot[wave] = __popcll(bal);
+      __syncthreads();
+      int off = n_routed;
+      for (int w = 0; w < wave; ++w) off += wtot[w];
+      if (t) glist[off + rank] = g;
+      for (int w = 0; w < WAVES; ++w) n_routed += wtot[w];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) glist[n_routed] = f.E;  // the shared expert (read only when present)
+    __syncthreads();
+    const int n_all = n_routed + (f.Is > 0 ? 1 : 0);
+    sb_begin = list_begin_idx < 0 ? 0 : (list_begin_idx == 3 ? n_routed : n_all);
+    sb_end = list_end_idx == 3 ? n_routed : n_all;
+  } else {
+    sb_begin = list_begin_idx < 0 ? 0 : f.plan[list_begin_idx];
+    sb_end = f.plan[list_end_idx];
+  }
   const int wide = PHASE == 1 ? (f.I > f.Is ? f.I : f.Is) : f.H;
   const int cols_per_item = PHASE == 1 ? (SPLIT ? 8 : 16) : 32;
   const int n_slabs = (wide + cols_per_item - 1) / cols_per_item;
@@ -338,10 +373,18 @@ __global__ __launch_bounds__(WAVES * 64, 2) void stream_kernel(FfnArgs f, int li
   for (int item = gw; item < total; item += nw) {
     const int sb = sb_begin + item / n_slabs;
     const int slab = item % n_slabs;
-    const int g = f.sb_group[sb];
-    const int r0 = f.sb_row0[sb];
-    const int base = f.sb_base[sb];
-    const int nrows = f.sb_nrows[sb];
+    int g, r0, base, nrows;
+    if (self_plan) {
+      g = glist[sb];
+      r0 = 0;
+      base = g < f.E ? f.offsets[g] : 0;
+      nrows = g < f.E ? f.offsets[g + 1] - base : f.T;
+    } else {
+      g = f.sb_group[sb];
+      r0 = f.sb_row0[sb];
+      base = f.sb_base[sb];
+      nrows = f.sb_nrows[sb];
+    }
     const bool shared = g >= f.E;
     const int K = PHASE == 1 ? f.H : (shared ? f.Is : f.I);
     const int Ncols = PHASE == 1 ? (shared ? f.Is : f.I) : f.H;
@@ -353,7 +396,11 @@ __global__ __launch_bounds__(WAVES * 64, 2) void stream_kernel(FfnArgs f, int li
     if (m < nrows) {
       const int gr = base + r0 + m;
       if (PHASE == 1) {
-        a_row = reinterpret_cast<const bf16*>(f.x) + (int64_t)f.sb_tok[sb * kStreamBM + m] * f.H;
+        int tok;
+        if (!self_plan) tok = f.sb_tok[sb * kStreamBM + m];
+        else tok = g < f.E ? f.sorted[gr] / f.k : m;
+        tok = tok < f.T ? tok : f.T - 1;
+        a_row = reinterpret_cast<const bf16*>(f.x) + (int64_t)tok * f.H;
       } else {
         a_row = shared ? reinterpret_cast<const bf16*>(f.h_sh) + (int64_t)gr * f.Is
                        : reinterpret_cast<const bf16*>(f.h) + (int64_t)gr * f.I;
@@ -537,23 +584,24 @@ hipError_t launch_router_stream(const void* x, const void* w_router, const void*
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_stream(const FfnArgs& a, int phase, hipStream_t s) {
+hipError_t launch_ffn_stream(const FfnArgs& a, int phase, hipStream_t s, bool self_plan) {
   const int grid = stream_grid();
   const int blk = WAVES * 64;
+  const int sp = self_plan ? 1 : 0;
   // a batch of at most kStreamMaxRows tokens streams every group: split items
   const bool split = a.T <= kStreamMaxRows;
   if (a.fp8) {
-    if (phase == 1) stream_kernel<1, true><<<grid, blk, 0, s>>>(a, -1, 3);
-    else stream_kernel<2, true><<<grid, blk, 0, s>>>(a, -1, 3);
+    if (phase == 1) stream_kernel<1, true><<<grid, blk, 0, s>>>(a, -1, 3, sp);
+    else stream_kernel<2, true><<<grid, blk, 0, s>>>(a, -1, 3, sp);
     if (a.Is > 0) {
-      if (phase == 1 && split) stream_kernel<1, false, true><<<grid, blk, 0, s>>>(a, 3, 1);
-      else if (phase == 1) stream_kernel<1, false><<<grid, blk, 0, s>>>(a, 3, 1);
-      else stream_kernel<2, false><<<grid, blk, 0, s>>>(a, 3, 1);
+      if (phase == 1 && split) stream_kernel<1, false, true><<<grid, blk, 0, s>>>(a, 3, 1, sp);
+      else if (phase == 1) stream_kernel<1, false><<<grid, blk, 0, s>>>(a, 3, 1, sp);
+      else stream_kernel<2, false><<<grid, blk, 0, s>>>(a, 3, 1, sp);
     }
   } else {
-    if (phase == 1 && split) stream_kernel<1, false, true><<<grid, blk, 0, s>>>(a, -1, 1);
-    else if (phase == 1) stream_kernel<1, false><<<grid, blk, 0, s>>>(a, -1, 1);
-    else stream_kernel<2, false><<<grid, blk, 0, s>>>(a, -1, 1);
+    if (phase == 1 && split) stream_kernel<1, false, true><<<grid, blk, 0, s>>>(a, -1, 1, sp);
+    else if (phase == 1) stream_kernel<1, false><<<grid, blk, 0, s>>>(a, -1, 1, sp);
+    else stream_kernel<2, false><<<grid, blk, 0, s>>>(a, -1, 1, sp);
   }
   return hipGetLastError();
 }

@@ -228,6 +228,32 @@ def test_single_token_and_many_empty_experts():
     check(p, g)
 
 
+@pytest.mark.parametrize("shared", [0, 128])
+def test_fp8_decode_batch(shared):
+    # T <= 16: the streaming kernels list the groups themselves; fp8 routed
+    # groups and the bf16 shared expert in their two launches
+    cfg = CONFIGS["max_fp8"].with_(name="fp8_decode", T=12, H=512, E=64, k=4, I=256, I_shared=shared, zipf_s=0.0)
+    p = gpu_problem(cfg, 15)
+    check(p, run_stages(p))
+
+
+def test_decode_batch_max_experts():
+    # E = 1024, the most experts a layer may have: the groups are listed in
+    # four 256-group chunks
+    cfg = CONFIGS["flash_decode"].with_(name="e1024", T=16, H=256, E=1024, k=8, I=64, I_shared=64)
+    p = gpu_problem(cfg, 16)
+    g = run_stages(p)
+    assert np.count_nonzero(np.diff(g["offsets"])[768:]) > 0  # touched groups in the last chunk
+    check(p, g)
+
+
+def test_decode_batch_forced_gemm():
+    # T <= 16 with the GEMM path forced: the plan kernel runs, no group streams
+    cfg = CONFIGS["flash_decode"].with_(name="decode_gemm", T=16, H=256, E=32, k=4, I=128, I_shared=64)
+    p = gpu_problem(cfg, 17)
+    check(p, run_stages(p, lib.MOE_FLAG_FORCE_GEMM))
+
+
 def test_empty_batch_is_noop():
     cfg = CONFIGS["flash_prefill"].with_(name="empty", T=0, H=128, E=8, k=2, I=64, I_shared=64)
     p = make_problem(cfg, 0, device="cuda")
