@@ -79,7 +79,8 @@ __global__ __launch_bounds__(NT, BKT == 32 ? 3 : 2) void gemm_kernel(FfnArgs f, 
     mt_begin = 0;
     mt_end = (ra.T + BM - 1) / BM;
   } else {
-    // plan ints: [0] gemm tiles total, [2] routed gemm tiles (shared ones follow)
+    // plan ints: [0] first-list m-tiles, [2] its routed ones (shared ones
+    // follow), [4] / [5] the second list
     mt_begin = list_begin_idx < 0 ? 0 : f.plan[list_begin_idx];
     mt_end = f.plan[list_end_idx];
   }
@@ -431,11 +432,13 @@ __global__ __launch_bounds__(NT, BKT == 32 ? 3 : 2) void gemm_kernel(FfnArgs f, 
 // Work planning: per group (routed expert or the shared one) decide the path
 // and emit (group, first row) entries for GEMM m-tiles and streaming m-blocks.
 // Layout of plan ints:
-//   [0] gemm m-tiles total        [1] stream m-blocks total
-//   [2] gemm m-tiles of routed groups (shared group's tiles follow)
+//   [0] m-tiles of the first list  [1] stream m-blocks total
+//   [2] first-list m-tiles of routed groups (the shared group's tiles follow)
 //   [3] stream m-blocks of routed groups
-//   [4..]  mt_group[max_mt], mt_row0[max_mt], sb_group[max_sb], sb_row0[max_sb],
-//          sb_base[max_sb], sb_nrows[max_sb], sb_tok[max_sb][kStreamBM]
+//   [4], [5] the second m-tile list [plan[4], plan[5]) (256-row tiling:
+//        groups' last m-tiles of at most 128 rows); [6], [7] unused
+//   [kPlanHeader..]  mt_group[max_mt], mt_row0[max_mt], sb_group[max_sb],
+//        sb_row0[max_sb], sb_base[max_sb], sb_nrows[max_sb], sb_tok[max_sb][kStreamBM]
 // ---------------------------------------------------------------------------
 __device__ int block_excl_scan(int v, int* tmp, int* total) {
   // blockDim.x == 1024 (16 waves)
