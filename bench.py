@@ -121,11 +121,13 @@ def cpu_baseline(problem, n_tokens):
                       f"{dt:.1f} s wall"}
 
 
-def gated_residual(lib, acc, args, cfg, dev, stream):
+def gated_residual(lib, acc, args, cfg, dev, stream, comb):
     """The four-stream gated residual read and write around the layer at the
     workload's T and H (read bottleneck width 320), each entry point timed
-    over --steps calls with HIP events on the launch stream.  Not part of the
-    step: the layer is the step."""
+    over --steps calls with HIP events on the launch stream, and the write
+    fused into the layer's combine (comb: the layer's problem and the
+    combine's inputs from the staged run).  Not part of the step: the layer
+    is the step."""
     import torch
     from synthetic import make_gr_problem
 
@@ -140,7 +142,10 @@ def gated_residual(lib, acc, args, cfg, dev, stream):
     for _ in range(max(1, args.warmup)):
         lib.moe_gr_read(P, G, g.resid, x, s, ws, stream)
         lib.moe_gr_write(P, g.resid, g.s, g.f, out, stream)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    PL, y, pos, tw, y_sh, sl = comb
+    for _ in range(max(1, args.warmup)):
+        lib.moe_combine_gr_write(PL, y, pos, tw, y_sh, sl, g.resid, g.s, None, out, stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     ev[0].record(stream)
     for _ in range(args.steps):
         lib.moe_gr_read(P, G, g.resid, x, s, ws, stream)
@@ -148,14 +153,20 @@ def gated_residual(lib, acc, args, cfg, dev, stream):
     for _ in range(args.steps):
         lib.moe_gr_write(P, g.resid, g.s, g.f, out, stream)
     ev[2].record(stream)
+    for _ in range(args.steps):
+        lib.moe_combine_gr_write(PL, y, pos, tw, y_sh, sl, g.resid, g.s, None, out, stream)
+    ev[3].record(stream)
     torch.cuda.synchronize()
     t_read = ev[0].elapsed_time(ev[1]) / args.steps * 1e-3
     t_write = ev[1].elapsed_time(ev[2]) / args.steps * 1e-3
+    t_cw = ev[2].elapsed_time(ev[3]) / args.steps * 1e-3
     fr, br = acc.gr_read_work(T, H, rank)
     fw, bw = acc.gr_write_work(T, H)
+    fc, bc = acc.combine_gr_write_work(T, H, cfg.k, y_sh is not None)
     return {"rank": rank,
             "read_us": round(t_read * 1e6, 2), "read_roofline": acc.roofline(fr, br, t_read),
-            "write_us": round(t_write * 1e6, 2), "write_roofline": acc.roofline(fw, bw, t_write)}
+            "write_us": round(t_write * 1e6, 2), "write_roofline": acc.roofline(fw, bw, t_write),
+            "combine_write_us": round(t_cw * 1e6, 2), "combine_write_roofline": acc.roofline(fc, bc, t_cw)}
 
 
 def weight_audit(lib, acc, args, prob, stream):
@@ -290,7 +301,8 @@ def main():
             "traffic": load_traffic(args.workload, kname), "kernel": kname,
             "algorithmic": {"flops": f_dom, "bytes": b_dom}}
 
-    gr = gated_residual(lib, acc, args, cfg, dev, stream) if cfg.act == "bf16" else None
+    gr = (gated_residual(lib, acc, args, cfg, dev, stream, (P, y, pos, tw, y_sh, sl))
+          if cfg.act == "bf16" else None)
     audit = weight_audit(lib, acc, args, prob, stream) if cfg.wdt == "bf16" else None
 
     t_s = ms_step * 1e-3

@@ -257,6 +257,19 @@ moe_status moe_gr_read(const moe_problem* p, const moe_gr_weights* g, const void
 moe_status moe_gr_write(const moe_problem* p, const void* resid, const float* s, const void* f, void* resid_out,
                         void* stream);
 
+/* moe_combine and moe_gr_write in one pass: the combine's F(x) = MoE(x)
+ * (rounded to bf16 as moe_combine stores it) goes straight into
+ *   resid_out [T, 4, H] = resid + s[:, i] * F(x)
+ * without being written and read back; the result equals moe_combine
+ * followed by moe_gr_write bit for bit.  out [T, H] bf16 receives F(x) too
+ * when non-NULL.  Arguments as moe_combine and moe_gr_write (y_shared and
+ * shared_logit both NULL or both non-NULL); resid_out may alias resid, out
+ * must not overlap resid or resid_out.  bf16 activations only
+ * (MOE_ERR_UNSUPPORTED otherwise), H a multiple of 32. */
+moe_status moe_combine_gr_write(const moe_problem* p, const void* y, const int32_t* assign_pos,
+                                const float* topk_w, const void* y_shared, const float* shared_logit,
+                                const void* resid, const float* s, void* out, void* resid_out, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Expert-weight audit (model-hub discussion "singular matrices in
  * Qwen3.8-2.4T-A95B"): for a bf16 weight tensor cut into `slices` equal

@@ -138,6 +138,12 @@ def moe_gr_write(p, resid, s, f, resid_out, stream=None):
            "moe_gr_write")
 
 
+def moe_combine_gr_write(p, y, assign_pos, topk_w, y_shared, shared_logit, resid, s, out, resid_out, stream=None):
+    _check(LIB.moe_combine_gr_write(ctypes.byref(p), _ptr(y), _ptr(assign_pos), _ptr(topk_w), _ptr(y_shared),
+                                    _ptr(shared_logit), _ptr(resid), _ptr(s), _ptr(out), _ptr(resid_out),
+                                    _stream(stream)), "moe_combine_gr_write")
+
+
 # numpy dtype of one moe_audit_stats record (int64 n, n_zero, n_nan; float64 median, mad, sigma_rob)
 AUDIT_STATS_FIELDS = ("n", "n_zero", "n_nan", "median", "mad", "sigma_rob")
 

@@ -24,7 +24,7 @@ MOE_FLAG_PAGE_ROUTING = 16
 
 EXPORTS = ["moe_abi_version", "moe_status_str", "moe_validate", "moe_workspace_bytes", "moe_route",
            "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",
-           "moe_layer_forward", "moe_gr_workspace_bytes", "moe_gr_read", "moe_gr_write",
+           "moe_layer_forward", "moe_gr_workspace_bytes", "moe_gr_read", "moe_gr_write", "moe_combine_gr_write",
            "moe_audit_workspace_bytes", "moe_weight_audit"]
 
 
@@ -75,6 +75,7 @@ def _load():
         "moe_gr_workspace_bytes": (sz, [P, ctypes.c_int64]),
         "moe_gr_read": (i32, [P, G, vp, vp, vp, vp, sz, vp]),
         "moe_gr_write": (i32, [P, vp, vp, vp, vp, vp]),
+        "moe_combine_gr_write": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "moe_audit_workspace_bytes": (sz, [ctypes.c_int64]),
         "moe_weight_audit": (i32, [vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp, vp, sz,
                                    vp]),

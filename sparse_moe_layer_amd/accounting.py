@@ -88,6 +88,18 @@ def gr_write_work(T: int, H: int):
     return 2.0 * T * 4 * H, 2.0 * (2 * T * 4 * H + T * H) + 4.0 * T * 4
 
 
+def combine_gr_write_work(T: int, H: int, k: int, shared: bool):
+    """The combine with the gated-residual write in its epilogue: read the k
+    routed output rows of every token (and its shared-expert row), the
+    weights, positions and gate logit, and the four bf16 streams with their
+    gates; write the four streams.  F(x) itself does not cross HBM.  FLOPs:
+    the weighted sum (2 per term) and the update (2 per stream element)."""
+    terms = k + (1 if shared else 0)
+    flops = 2.0 * T * H * terms + 2.0 * T * 4 * H
+    byts = 2.0 * T * H * terms + 8.0 * T * k + (4.0 * T if shared else 0.0) + 2.0 * 2 * T * 4 * H + 4.0 * T * 4
+    return flops, byts
+
+
 def audit_work(values: int) -> float:
     """Expert-weight audit: every bf16 value is read once (the histograms it
     writes are a few hundred KB per slice and are not counted)."""

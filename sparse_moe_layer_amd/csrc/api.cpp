@@ -460,6 +460,22 @@ moe_status moe_gr_write(const moe_problem* p, const void* resid, const float* s,
   return hip_status(moe::launch_gr_write(resid, s, f, resid_out, (int)p->T, (int)p->H, (hipStream_t)stream));
 }
 
+moe_status moe_combine_gr_write(const moe_problem* p, const void* y, const int32_t* assign_pos,
+                                const float* topk_w, const void* y_shared, const float* shared_logit,
+                                const void* resid, const float* s, void* out, void* resid_out, void* stream) {
+  if (!p) return MOE_ERR_NULL;
+  moe_status st = check_gr(p, 16);
+  if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;
+  if (!y || !assign_pos || !topk_w || !resid || !s || !resid_out) return MOE_ERR_NULL;
+  if ((y_shared == nullptr) != (shared_logit == nullptr)) return MOE_ERR_NULL;
+  if (!al16(y) || !al16(resid) || !al16(resid_out) || (out && !al16(out)) || (y_shared && !al16(y_shared)) ||
+      reinterpret_cast<uintptr_t>(s) % 4)
+    return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_combine_gr_write(y, assign_pos, topk_w, y_shared, shared_logit, out, resid, s,
+                                                 resid_out, (int)p->T, (int)p->H, (int)p->k, (hipStream_t)stream));
+}
+
 size_t moe_audit_workspace_bytes(int64_t slices) {
   if (slices < 1 || slices > 65535) return 0;
   return moe::audit_workspace_bytes(slices);

@@ -4,6 +4,12 @@
 // 16-byte loads of y rows (8 bf16 or 4 fp32 per thread), fp32 accumulation
 // with j ascending, one rounding to the output dtype.  HBM-bound: reads k+1
 // rows of H and writes one.
+//
+// With the gated residual around the layer (same study, "Gated residual:
+// four streams, one sublayer input"), the stream write R'_i = R_i + s_i F(x)
+// can run in the combine's epilogue: the thread that rounds F(x) for 8
+// columns of token t updates the same 8 columns of the token's four
+// streams, so F(x) need not be written and read back.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,11 +34,16 @@ __device__ __forceinline__ void accumulate(float* acc, float wgt, u32x4 v) {
 // token t.  The token's k row positions and weights are staged in LDS once;
 // a thread then issues the y loads of up to 8 assignments before adding them
 // (j ascending), so the k+1 row reads overlap instead of forming a chain.
-template <bool F32>
+// GRW (bf16 only): the gated-residual stream write in the epilogue;
+// resid / s / resid_out as gr_write (resid_out may alias resid: each element
+// is read and then written by one thread), out may be null.
+template <bool F32, bool GRW = false>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y, const int32_t* __restrict__ pos,
                                                       const float* __restrict__ w, const void* __restrict__ y_sh,
                                                       const float* __restrict__ sl, void* __restrict__ out, int H,
-                                                      int k) {
+                                                      int k, const bf16* resid, const float* __restrict__ s,
+                                                      bf16* resid_out) {
+  static_assert(!(F32 && GRW), "the gated residual is bf16");
   constexpr int VEC = F32 ? 4 : 8;
   constexpr int ESZ = F32 ? 4 : 2;
   constexpr int BATCH = 8;
@@ -49,6 +60,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   if (c >= H / VEC) return;
   const int64_t col = (int64_t)c * VEC;
   const char* yb = reinterpret_cast<const char*>(y);
+  // the streams' loads go first, so they are in flight with the y rows
+  constexpr int STREAMS = 4;
+  u32x4 r[GRW ? STREAMS : 1];
+  if constexpr (GRW) {
+#pragma unroll
+    for (int i = 0; i < STREAMS; ++i) r[i] = ld16(resid + ((int64_t)t * STREAMS + i) * H + col);
+  }
   float acc[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
@@ -65,14 +83,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     const u32x4 v = ld16(reinterpret_cast<const char*>(y_sh) + ((int64_t)t * H + col) * ESZ);
     accumulate<F32>(acc, sigmoid(sl[t]), v);
   }
-  char* dst = reinterpret_cast<char*>(out) + ((int64_t)t * H + col) * ESZ;
+  char* dst = out ? reinterpret_cast<char*>(out) + ((int64_t)t * H + col) * ESZ : nullptr;
   if constexpr (F32) {
     st16(dst, __builtin_bit_cast(u32x4, f32x4{acc[0], acc[1], acc[2], acc[3]}));
   } else {
     bf16x8 o;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = f2bf(acc[i]);
-    st16(dst, __builtin_bit_cast(u32x4, o));
+    if (dst) st16(dst, __builtin_bit_cast(u32x4, o));
+    if constexpr (GRW) {
+      // R'_i = R_i + s_i F(x) with F(x) rounded as stored, as gr_write does
+#pragma unroll
+      for (int i = 0; i < STREAMS; ++i) {
+        const float si = s[(int64_t)t * STREAMS + i];
+        const bf16x8 rv = __builtin_bit_cast(bf16x8, r[i]);
+        bf16x8 ov;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ov[e] = f2bf(fmaf(si, bf2f(o[e]), bf2f(rv[e])));
+        st16(resid_out + ((int64_t)t * STREAMS + i) * H + col, __builtin_bit_cast(u32x4, ov));
+      }
+    }
   }
 }
 
@@ -82,8 +112,20 @@ hipError_t launch_combine(const void* y, const int32_t* pos, const float* w, con
                           const float* shared_logit, void* out, int T, int H, int k, int f32, hipStream_t s) {
   const int vec = f32 ? 4 : 8;
   const dim3 grid(T, (H / vec + 255) / 256);
-  if (f32) combine_kernel<true><<<grid, 256, 0, s>>>(y, pos, w, y_sh, shared_logit, out, H, k);
-  else combine_kernel<false><<<grid, 256, 0, s>>>(y, pos, w, y_sh, shared_logit, out, H, k);
+  if (f32)
+    combine_kernel<true><<<grid, 256, 0, s>>>(y, pos, w, y_sh, shared_logit, out, H, k, nullptr, nullptr, nullptr);
+  else
+    combine_kernel<false><<<grid, 256, 0, s>>>(y, pos, w, y_sh, shared_logit, out, H, k, nullptr, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_gr_write(const void* y, const int32_t* pos, const float* w, const void* y_sh,
+                                   const float* shared_logit, void* out, const void* resid, const float* gate,
+                                   void* resid_out, int T, int H, int k, hipStream_t s) {
+  const dim3 grid(T, (H / 8 + 255) / 256);
+  combine_kernel<false, true><<<grid, 256, 0, s>>>(y, pos, w, y_sh, shared_logit, out, H, k,
+                                                   reinterpret_cast<const bf16*>(resid), gate,
+                                                   reinterpret_cast<bf16*>(resid_out));
   return hipGetLastError();
 }
 

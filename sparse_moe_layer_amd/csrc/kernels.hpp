@@ -89,6 +89,11 @@ hipError_t launch_ffn_f32(const FfnArgs& a, int phases, hipStream_t s);  // bit 
 hipError_t launch_combine(const void* y, const int32_t* pos, const float* w, const void* y_sh,
                           const float* shared_logit, void* out, int T, int H, int k, int f32,
                           hipStream_t s);
+// bf16 combine with the gated-residual stream write in its epilogue: out
+// (F(x), may be null) and resid_out [T, 4, H] = resid + gate[:, i] * F(x).
+hipError_t launch_combine_gr_write(const void* y, const int32_t* pos, const float* w, const void* y_sh,
+                                   const float* shared_logit, void* out, const void* resid, const float* gate,
+                                   void* resid_out, int T, int H, int k, hipStream_t s);
 
 // Gated residual read / write (bf16).
 // Expert-weight audit (bf16): histograms of the bit patterns per slice and

@@ -160,10 +160,21 @@ def test_gated_residual_entry_points_validate_before_any_launch():
     assert L.moe_gr_write(P, fake, fake + 2, fake, fake, None) == _lib.MOE_ERR_ALIGN
     pf = lib.problem(64, 256, 16, 4, 128, 0, "f32", "f32")
     assert L.moe_gr_write(ctypes.byref(pf), fake, fake, fake, fake, None) == _lib.MOE_ERR_UNSUPPORTED
+    # combine + write: y, pos, w, y_sh, logit, resid, s, out (optional), resid_out
+    cw = L.moe_combine_gr_write
+    assert cw(P, None, fake, fake, None, None, fake, fake, None, fake, None) == _lib.MOE_ERR_NULL
+    assert cw(P, fake, fake, fake, None, None, None, fake, None, fake, None) == _lib.MOE_ERR_NULL
+    assert cw(P, fake, fake, fake, None, None, fake, fake, None, None, None) == _lib.MOE_ERR_NULL
+    assert cw(P, fake, fake, fake, fake, None, fake, fake, None, fake, None) == _lib.MOE_ERR_NULL  # y_sh w/o logit
+    assert cw(P, fake, fake, fake, None, None, fake + 8, fake, None, fake, None) == _lib.MOE_ERR_ALIGN
+    assert cw(P, fake, fake, fake, None, None, fake, fake + 2, None, fake, None) == _lib.MOE_ERR_ALIGN
+    assert cw(P, fake, fake, fake, None, None, fake, fake, fake + 8, fake, None) == _lib.MOE_ERR_ALIGN
+    assert cw(ctypes.byref(pf), fake, fake, fake, None, None, fake, fake, None, fake, None) == _lib.MOE_ERR_UNSUPPORTED
     # empty batch: valid no-op
     p0 = lib.problem(0, 2560, 512, 10, 640, 640)
     assert L.moe_gr_read(ctypes.byref(p0), G, None, None, None, None, 0, None) == OK
     assert L.moe_gr_write(ctypes.byref(p0), None, None, None, None, None) == OK
+    assert cw(ctypes.byref(p0), None, None, None, None, None, None, None, None, None, None) == OK
 
 
 def test_audit_entry_points_validate_before_any_launch():

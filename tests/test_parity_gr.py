@@ -1,4 +1,5 @@
-"""GPU parity of the gated residual read/write (moe_gr_read, moe_gr_write)
+"""GPU parity of the gated residual read/write (moe_gr_read, moe_gr_write,
+and the write fused into the combine, moe_combine_gr_write)
 against the fp64 oracle (oracle/gr.py), Qwen3.8-Flash-Next study, section
 "Gated residual: four streams, one sublayer input".
 
@@ -22,7 +23,8 @@ import torch
 
 import sparse_moe_layer_amd as lib
 from oracle import gr as ogr
-from synthetic import make_gr_problem
+from sparse_moe_layer_amd.tensors import structs
+from synthetic import CONFIGS, make_gr_problem, make_problem
 
 pytestmark = pytest.mark.gpu
 
@@ -114,6 +116,51 @@ def test_gr_write_matches_oracle_and_may_alias():
     lib.moe_gr_write(P, r, g.s, g.f, r)
     torch.cuda.synchronize()
     assert torch.equal(r, out)
+
+
+@pytest.mark.parametrize("shared", [640, 0])
+def test_combine_with_fused_write_equals_combine_then_write(shared):
+    # The fused pass must give moe_combine followed by moe_gr_write bit for
+    # bit (both are checked against the oracle on their own), with and
+    # without F(x) stored, and in place.
+    cfg = CONFIGS["flash_prefill"].with_(name="combine_write", T=300, k=10, I_shared=shared)
+    print(f"[gr] combine+write T={cfg.T} H={cfg.H} shared={shared}", flush=True)
+    prob = make_problem(cfg, 21, device="cuda")
+    T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
+    P, W = structs(prob)
+    ws = lib.workspace(P)
+    dev = prob.x.device
+    sh = shared > 0
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    sl = torch.empty(T, dtype=torch.float32, device=dev) if sh else None
+    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sa = torch.empty(T * k, dtype=torch.int32, device=dev)
+    pos = torch.empty(T * k, dtype=torch.int32, device=dev)
+    y = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    ysh = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if sh else None
+    lib.moe_route(P, prob.x, prob.w_router, prob.sh_gate_w, ids, w, sl, ws)
+    lib.moe_dispatch(P, ids, offs, sa, pos, ws)
+    lib.moe_expert_ffn(P, W, prob.x, offs, sa, y, ysh, ws)
+    g = make_gr_problem(T, H, 16, seed=22, device="cuda")
+    f = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ref = torch.empty_like(g.resid)
+    lib.moe_combine(P, y, pos, w, ysh, sl, f)
+    lib.moe_gr_write(P, g.resid, g.s, f, ref)
+    f2 = torch.full_like(f, float("nan"))
+    out2 = torch.full_like(g.resid, float("nan"))
+    lib.moe_combine_gr_write(P, y, pos, w, ysh, sl, g.resid, g.s, f2, out2)
+    out3 = torch.full_like(g.resid, float("nan"))
+    lib.moe_combine_gr_write(P, y, pos, w, ysh, sl, g.resid, g.s, None, out3)
+    r = g.resid.clone()
+    lib.moe_combine_gr_write(P, y, pos, w, ysh, sl, r, g.s, None, r)
+    torch.cuda.synchronize()
+    assert torch.equal(f2, f)
+    assert torch.equal(out2, ref) and torch.equal(out3, ref) and torch.equal(r, ref)
+    # and against the oracle's write of the stored F(x)
+    want = ogr.gr_write(g.host(g.resid), g.host(g.s), f.float().cpu().numpy())
+    got = out2.float().cpu().numpy()
+    assert not (np.abs(got - want) > np.abs(want) * (2.0 ** -8 + 2.0 ** -23)).any()
 
 
 def test_gr_empty_batch_is_a_no_op():
