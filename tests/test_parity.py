@@ -74,6 +74,9 @@ def run_stages(p, flags=0):
                        y2.view(torch.int16) if y2.dtype == torch.bfloat16 else y2), "split GEMM phases differ"
     if sh:
         assert torch.equal(ysh.float(), y2_sh.float()), "split GEMM phases differ (shared)"
+    # the one-call layer runs the same kernels: same bits as the stage calls
+    assert torch.equal(ids2, ids) and torch.equal(w2, w), "layer call routing differs"
+    assert torch.equal(out2.float(), out.float()), "layer call output differs"
     return dict(ids=f(ids), w=f(w), sl=f(sl), offsets=f(offs), sorted=f(sa), pos=f(pos), y=f(y), ysh=f(ysh),
                 out=f(out), out_layer=f(out2), ids_layer=f(ids2), w_layer=f(w2))
 
