@@ -260,7 +260,8 @@ moe_status run_ffn(const moe_problem* p, FfnArgs& a, int phases, void* plan_ws, 
       // 256-row tiles, then the groups' remainders of at most 128 rows in 128-row tiles
       const hipError_t e = big ? moe::launch_ffn_gemm_dma(a, phase, s) : moe::launch_ffn_gemm(a, phase, s);
       if (e != hipSuccess) return MOE_ERR_HIP;
-      if (big && moe::launch_ffn_gemm(a, phase, s, 4, 5) != hipSuccess) return MOE_ERR_HIP;
+      if (big && moe::launch_ffn_gemm(a, phase, s, moe::kPlanTiles2Begin, moe::kPlanTiles2End) != hipSuccess)
+        return MOE_ERR_HIP;
     }
     if (any_stream && moe::launch_ffn_stream(a, phase, s, self_plan) != hipSuccess) return MOE_ERR_HIP;
   }

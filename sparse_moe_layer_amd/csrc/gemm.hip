@@ -81,7 +81,7 @@ __global__ __launch_bounds__(NT, BKT == 32 ? 3 : 2) void gemm_kernel(FfnArgs f, 
   } else {
     // plan ints: [0] first-list m-tiles, [2] its routed ones (shared ones
     // follow), [4] / [5] the second list
-    mt_begin = list_begin_idx < 0 ? 0 : f.plan[list_begin_idx];
+    mt_begin = list_begin_idx == kPlanStart ? 0 : f.plan[list_begin_idx];
     mt_end = f.plan[list_end_idx];
   }
   const int nsplit = MODE == M_ROUTER ? ra.nsplit : 1;
@@ -624,9 +624,9 @@ hipError_t launch_router_logits_bf16(const void* x, const void* w_router, const 
   const int grid = tiles < num_cus() * 2 ? (tiles + 7) / 8 * 8 : num_cus() * 2;
   FfnArgs none{};
   if (gated_residual)
-    gemm_kernel<M_ROUTER, false, 1><<<grid, NT, 0, s>>>(none, ra, ntn, -1, 0);
+    gemm_kernel<M_ROUTER, false, 1><<<grid, NT, 0, s>>>(none, ra, ntn, kPlanStart, kPlanTiles);
   else
-    gemm_kernel<M_ROUTER, false><<<grid, NT, 0, s>>>(none, ra, ntn, -1, 0);
+    gemm_kernel<M_ROUTER, false><<<grid, NT, 0, s>>>(none, ra, ntn, kPlanStart, kPlanTiles);
   return hipGetLastError();
 }
 
@@ -645,11 +645,11 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s, int list_
     else gemm_kernel<M_DOWN, true><<<grid, NT, 0, s>>>(a, none, ntn, list_begin_idx, list_end_idx);
   } else if (a.fp8) {
     // routed tiles [0, plan[2]) decode fp8; the shared expert stays bf16
-    if (phase == 1) gemm_kernel<M_GATEUP, true><<<grid, NT, 0, s>>>(a, none, ntn, -1, 2);
-    else gemm_kernel<M_DOWN, true><<<grid, NT, 0, s>>>(a, none, ntn, -1, 2);
+    if (phase == 1) gemm_kernel<M_GATEUP, true><<<grid, NT, 0, s>>>(a, none, ntn, kPlanStart, kPlanRoutedTiles);
+    else gemm_kernel<M_DOWN, true><<<grid, NT, 0, s>>>(a, none, ntn, kPlanStart, kPlanRoutedTiles);
     if (sh) {
-      if (phase == 1) gemm_kernel<M_GATEUP, false><<<grid, NT, 0, s>>>(a, none, ntn, 2, 0);
-      else gemm_kernel<M_DOWN, false><<<grid, NT, 0, s>>>(a, none, ntn, 2, 0);
+      if (phase == 1) gemm_kernel<M_GATEUP, false><<<grid, NT, 0, s>>>(a, none, ntn, kPlanRoutedTiles, kPlanTiles);
+      else gemm_kernel<M_DOWN, false><<<grid, NT, 0, s>>>(a, none, ntn, kPlanRoutedTiles, kPlanTiles);
     }
   } else {
     constexpr int per_cu = kBf16FfnBK == 32 ? 3 : 2;

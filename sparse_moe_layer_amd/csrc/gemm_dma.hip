@@ -314,7 +314,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArg
   const FragOff fo = frag_offsets<C>(wm, wn, lane);
 
   // m-tiles: routed groups, then the shared expert (fp8: routed ones only)
-  const int mt_first = list_begin_idx < 0 ? 0 : f.plan[list_begin_idx];
+  const int mt_first = list_begin_idx == kPlanStart ? 0 : f.plan[list_begin_idx];
   const int MT = f.plan[list_end_idx] - mt_first;
   const int total = MT * n_tiles_n;
   const int G = gridDim.x;
@@ -560,11 +560,11 @@ bool ffn_dma_supported(const FfnArgs& a) {
 }
 
 hipError_t launch_ffn_gemm_dma(const FfnArgs& a, int phase, hipStream_t s) {
-  if (!a.fp8) return launch<BigCfg>(a, phase, s, -1, 0);
+  if (!a.fp8) return launch<BigCfg>(a, phase, s, kPlanStart, kPlanTiles);
   // fp8 layers: routed m-tiles [0, plan[2]) decode codes, the shared
   // expert's [plan[2], plan[0]) are bf16
-  hipError_t e = launch<BigCfg8>(a, phase, s, -1, 2);
-  if (e == hipSuccess && a.Is > 0) e = launch<BigCfg>(a, phase, s, 2, 0);
+  hipError_t e = launch<BigCfg8>(a, phase, s, kPlanStart, kPlanRoutedTiles);
+  if (e == hipSuccess && a.Is > 0) e = launch<BigCfg>(a, phase, s, kPlanRoutedTiles, kPlanTiles);
   return e;
 }
 

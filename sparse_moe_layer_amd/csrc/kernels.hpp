@@ -18,6 +18,17 @@ constexpr int kMaxExperts = 1024;
 // m-blocks, [2] / [3] where the shared expert's m-tiles / m-blocks begin,
 // [4, 5) the second m-tile list (128-row remainders of 256-row tiling)
 constexpr int kPlanHeader = 8;
+// Positions in the plan header, as the kernels' list bounds: a kernel runs
+// the entries [plan[begin], plan[end]) of its list, begin kPlanStart meaning 0.
+enum PlanPos : int {
+  kPlanStart = -1,
+  kPlanTiles = 0,          // end of the first m-tile list
+  kPlanBlocks = 1,         // end of the stream m-block list
+  kPlanRoutedTiles = 2,    // end of the routed groups' m-tiles (the shared expert's follow)
+  kPlanRoutedBlocks = 3,   // end of the routed groups' m-blocks (the shared expert's follow)
+  kPlanTiles2Begin = 4,    // the second m-tile list
+  kPlanTiles2End = 5,
+};
 // An expert with at most this many rows streams its weights (small-M path).
 constexpr int kStreamMaxRows = 16;
 
@@ -76,8 +87,8 @@ hipError_t launch_ffn_plan(const int32_t* offsets, const int32_t* sorted, int T,
 void ffn_bind_plan(FfnArgs& a, int32_t* plan_ws);
 // phase 1 gate/up, 2 down; bf16 tiles run the m-tiles [plan[begin], plan[end])
 // (begin < 0: from 0), fp8 tiles the whole first list
-hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s, int list_begin_idx = -1,
-                           int list_end_idx = 0);
+hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s, int list_begin_idx = kPlanStart,
+                           int list_end_idx = kPlanTiles);
 // Pipelined direct-load MFMA GEMM with 256-row tiles (bf16 weights, H, I,
 // I_shared multiples of 32).
 bool ffn_dma_supported(const FfnArgs& a);

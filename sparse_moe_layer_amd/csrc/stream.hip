@@ -322,8 +322,7 @@ __device__ __forceinline__ void stream_dot_lds8(const bf16* a_row, const bf16* a
 // streams as one m-block): no plan kernel runs before the launch; each
 // workgroup lists the touched groups itself, in ascending order with the
 // shared expert last, from the expert offsets (the plan's stream list for
-// such a batch).  List positions: begin -1 = 0, index 3 = the routed
-// groups' count, index 1 = all groups (the plan's [3] and [1]).
+// such a batch); the list bounds name plan positions as without it.
 template <int PHASE, bool FP8, bool SPLIT = false>
 __global__ __launch_bounds__(WAVES * 64, 2) void stream_kernel(FfnArgs f, int list_begin_idx, int list_end_idx,
                                                                int self_plan) {
@@ -358,10 +357,10 @@ __global__ __launch_bounds__(WAVES * 64, 2) void stream_kernel(FfnArgs f, int li
     if (threadIdx.x == 0) glist[n_routed] = f.E;  // the shared expert (read only when present)
     __syncthreads();
     const int n_all = n_routed + (f.Is > 0 ? 1 : 0);
-    sb_begin = list_begin_idx < 0 ? 0 : (list_begin_idx == 3 ? n_routed : n_all);
-    sb_end = list_end_idx == 3 ? n_routed : n_all;
+    sb_begin = list_begin_idx == kPlanStart ? 0 : (list_begin_idx == kPlanRoutedBlocks ? n_routed : n_all);
+    sb_end = list_end_idx == kPlanRoutedBlocks ? n_routed : n_all;
   } else {
-    sb_begin = list_begin_idx < 0 ? 0 : f.plan[list_begin_idx];
+    sb_begin = list_begin_idx == kPlanStart ? 0 : f.plan[list_begin_idx];
     sb_end = f.plan[list_end_idx];
   }
   const int wide = PHASE == 1 ? (f.I > f.Is ? f.I : f.Is) : f.H;
@@ -591,17 +590,17 @@ hipError_t launch_ffn_stream(const FfnArgs& a, int phase, hipStream_t s, bool se
   // a batch of at most kStreamMaxRows tokens streams every group: split items
   const bool split = a.T <= kStreamMaxRows;
   if (a.fp8) {
-    if (phase == 1) stream_kernel<1, true><<<grid, blk, 0, s>>>(a, -1, 3, sp);
-    else stream_kernel<2, true><<<grid, blk, 0, s>>>(a, -1, 3, sp);
+    if (phase == 1) stream_kernel<1, true><<<grid, blk, 0, s>>>(a, kPlanStart, kPlanRoutedBlocks, sp);
+    else stream_kernel<2, true><<<grid, blk, 0, s>>>(a, kPlanStart, kPlanRoutedBlocks, sp);
     if (a.Is > 0) {
-      if (phase == 1 && split) stream_kernel<1, false, true><<<grid, blk, 0, s>>>(a, 3, 1, sp);
-      else if (phase == 1) stream_kernel<1, false><<<grid, blk, 0, s>>>(a, 3, 1, sp);
-      else stream_kernel<2, false><<<grid, blk, 0, s>>>(a, 3, 1, sp);
+      if (phase == 1 && split) stream_kernel<1, false, true><<<grid, blk, 0, s>>>(a, kPlanRoutedBlocks, kPlanBlocks, sp);
+      else if (phase == 1) stream_kernel<1, false><<<grid, blk, 0, s>>>(a, kPlanRoutedBlocks, kPlanBlocks, sp);
+      else stream_kernel<2, false><<<grid, blk, 0, s>>>(a, kPlanRoutedBlocks, kPlanBlocks, sp);
     }
   } else {
-    if (phase == 1 && split) stream_kernel<1, false, true><<<grid, blk, 0, s>>>(a, -1, 1, sp);
-    else if (phase == 1) stream_kernel<1, false><<<grid, blk, 0, s>>>(a, -1, 1, sp);
-    else stream_kernel<2, false><<<grid, blk, 0, s>>>(a, -1, 1, sp);
+    if (phase == 1 && split) stream_kernel<1, false, true><<<grid, blk, 0, s>>>(a, kPlanStart, kPlanBlocks, sp);
+    else if (phase == 1) stream_kernel<1, false><<<grid, blk, 0, s>>>(a, kPlanStart, kPlanBlocks, sp);
+    else stream_kernel<2, false><<<grid, blk, 0, s>>>(a, kPlanStart, kPlanBlocks, sp);
   }
   return hipGetLastError();
 }
