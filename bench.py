@@ -47,8 +47,8 @@ def parse():
     ap.add_argument("--path", default="auto", choices=["auto", "gemm", "stream"],
                     help="pin every expert to one path (A/B runs); default picks per expert by rows")
     ap.add_argument("--cpu-tokens", type=int, default=-1,
-                    help="tokens of the same workload the CPU oracle runs on (0: skip; -1: as many as fit "
-                         "in about 15 s after a 64-token probe)")
+                    help="tokens of the same workload the CPU oracle runs on (0: skip; -1: grown from 64 "
+                         "until one run takes 10 s or covers the batch)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scale factor for HBM byte counters)")
     return ap.parse_args()
@@ -87,8 +87,11 @@ def load_traffic(workload, kernel):
 
 def cpu_baseline(problem, n_tokens):
     """The fp64 oracle, as it stands, on the first n tokens of the workload.
-    n_tokens < 0 sizes the sample by time: a 64-token probe, then as many
-    tokens as the probe's rate fits in about 15 s (at most the whole batch)."""
+    n_tokens < 0 sizes the sample by time: from 64 tokens, the sample grows
+    (by the last run's rate, at least doubling) until one run takes 10 s or
+    more or covers the whole batch; that run is reported.  (The oracle's time
+    is not proportional to n: converting the touched experts' weights is a
+    large fixed part, so one small probe underestimates the rate.)"""
     import types
 
     from threadpoolctl import threadpool_info
@@ -108,12 +111,14 @@ def cpu_baseline(problem, n_tokens):
 
     T = problem.cfg.T
     if n_tokens < 0:
-        n0 = min(64, T)
-        rate = n0 / run(n0)
-        n = min(T, max(n0, int(15.0 * rate)))
+        n = min(64, T)
+        dt = run(n)
+        while dt < 10.0 and n < T:
+            n = min(T, max(2 * n, int(n * 15.0 / max(dt, 1e-3))))
+            dt = run(n)
     else:
         n = min(n_tokens, T)
-    dt = run(n)
+        dt = run(n)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} of {T} tokens of the same workload, full layer "
