@@ -168,6 +168,7 @@ __device__ void finalize_one(CT* __restrict__ h, moe_audit_stats* __restrict__ o
   __shared__ int ord_k[2];
   __shared__ unsigned long long dmin[2];
   __shared__ unsigned long long zero_cnt;
+  __shared__ int srch[3][4];  // MAD search: first passing chunk, per round and search
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // wave w owns groups kGpw w .. (positions 64 kGpw w ..); in its j-th step
   // lane l takes position 64 (kGpw w + j) + l, so every access is one
@@ -294,32 +295,56 @@ __device__ void finalize_one(CT* __restrict__ h, moe_audit_stats* __restrict__ o
         }
         return above + (below_all - P(c - 1));
       };
-      // candidates (occupied positions) dealt round-robin, position
-      // tid + kFinThreads j, so that the positions, which cluster around the
-      // median, spread over all threads; sixteen occupancy tests' loads are
-      // in flight together
-      unsigned long long best1 = ~0ull, best2 = ~0ull;
-      constexpr int kPer = kBins / kFinThreads;
-      for (int j0 = 0; j0 < kPer; j0 += 16) {
-        uint32_t occ = 0;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int o = tid + kFinThreads * (j0 + j);
-          if (o >= kOrdFirst && o <= kOrdLast && gsum[o >> 6] != 0 && P(o) != P(o - 1)) occ |= 1u << j;
+      // The MAD of rank k is the least occupied distance D with
+      // within(D) >= k + 1.  On each side of om the distance grows with the
+      // step away from om, and within grows with D, so each side's least
+      // qualifying position is found by a search; the lesser of the two
+      // sides' distances is attained at an occupied position (within only
+      // changes there).  Four searches (ranks k1, k2 x above, below), 128
+      // threads each: a round tests the last position of 128 equal chunks
+      // of the live span and keeps the first chunk whose test passes, so
+      // 65536 positions take three rounds.
+      constexpr int kLanes = kFinThreads / 4;
+      static_assert(kLanes == 128, "four searches of 128 threads");
+      const int combo = tid / kLanes, lt = tid % kLanes;
+      const unsigned long long need = ((combo & 1) ? k2 : k1) + 1;
+      const bool above = combo < 2;
+      const int span_n = above ? kOrdLast + 1 - om : om - kOrdFirst;
+      // distance of the i-th position away from m on this side
+      auto dist = [&](int i) -> double {
+        return above ? val_of_ord(om + i) - m : m - val_of_ord(om - 1 - i);
+      };
+      int slo = 0, shi = span_n;  // the answer lies in [slo, shi], shi meaning none
+      bool found = false;
+      if (tid < 12) srch[tid / 4][tid % 4] = kLanes;
+      __syncthreads();
+      for (int round = 0; round < 3; ++round) {
+        const int span = shi - slo;
+        const int step = (span + kLanes - 1) / kLanes;
+        if (span > 0) {
+          int q = slo + (lt + 1) * step - 1;
+          q = q < shi - 1 ? q : shi - 1;
+          if (slo + lt * step < shi && within(dist(q)) >= need) atomicMin(&srch[round][combo], lt);
         }
-        for (int j = 0; j < 16; ++j) {
-          if (!((occ >> j) & 1u)) continue;
-          const int o = tid + kFinThreads * (j0 + j);
-          const double D = __builtin_fabs(val_of_ord(o) - m);
-          const unsigned long long bits = dbits(D);
-          if (bits >= best1 && bits >= best2) continue;  // cannot lower either minimum
-          const unsigned long long w = within(D);
-          if (w >= k1 + 1 && bits < best1) best1 = bits;
-          if (w >= k2 + 1 && bits < best2) best2 = bits;
+        __syncthreads();
+        const int c = srch[round][combo];
+        if (span > 0) {
+          if (c < kLanes) {
+            const int nlo = slo + c * step;
+            const int nhi = nlo + step < shi ? nlo + step : shi;
+            slo = nlo;
+            shi = nhi;
+            found = true;
+          } else if (!found) {
+            slo = shi;  // no position on this side qualifies
+          }
         }
       }
-      if (best1 != ~0ull) atomicMin(&dmin[0], best1);
-      if (best2 != ~0ull) atomicMin(&dmin[1], best2);
+      // [slo, shi) is now one position (or empty when none qualifies)
+      if (lt == 0 && found && slo < span_n) {
+        const unsigned long long bits = dbits(__builtin_fabs(dist(slo)));
+        atomicMin(&dmin[combo & 1], bits);
+      }
       __syncthreads();
       mad = (__longlong_as_double((long long)dmin[0]) + __longlong_as_double((long long)dmin[1])) * 0.5;
     }
