@@ -330,6 +330,11 @@ def main():
         "layer": {"tflops": round(work.flops / t_s / 1e12, 2), "hbm_gbps": round(work.bytes / t_s / 1e9, 1),
                   "mfma_frac": round(work.flops / t_s / 1e12 / mfma_peak, 4),
                   "hbm_frac": round(work.bytes / t_s / 1e9 / acc.PEAK_HBM_GBPS, 4),
+                  # the whole layer against its binding roof: t_roof = max(F/P, B/BW)
+                  "bound": "mfma" if work.flops / (mfma_peak * 1e12) >= work.bytes / (acc.PEAK_HBM_GBPS * 1e9)
+                           else "hbm",
+                  "roof_frac": round(max(work.flops / (mfma_peak * 1e12), work.bytes / (acc.PEAK_HBM_GBPS * 1e9))
+                                     / t_s, 4),
                   "staged_ms": round(staged_ms, 4)},
         "stages_ms": {n: round(v, 4) for n, v in stage_ms.items()},
         "roofline": roof,
