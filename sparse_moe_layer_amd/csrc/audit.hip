@@ -7,12 +7,14 @@
 // A bf16 value is one of 65536 bit patterns, so one streaming pass that
 // counts every pattern gives the exact multiset of each slice:
 //   audit_hist_kernel     streams the tensor once (16-byte loads) and counts
-//                         patterns: zeros in registers, |w| < 2 (exponent
-//                         field < 128: 32768 patterns with the sign) in a
-//                         128 KB LDS histogram, the rare rest with global
-//                         atomics; each workgroup then adds its non-empty
-//                         LDS bins into the slice's histogram and the whole
-//                         tensor's (uint64) in HBM.
+//                         patterns: zeros in registers, 2^-63 <= |w| < 2
+//                         (exponent field 64..127: 16384 patterns with the
+//                         sign) in a 64 KB LDS histogram, the rare rest with
+//                         global atomics; each workgroup then adds its
+//                         non-empty LDS bins into the slice's histogram and
+//                         the whole tensor's (uint64) in HBM.  Two
+//                         workgroups share a CU, so one's flush overlaps
+//                         the other's stream.
 //   audit_finalize_kernel one workgroup per histogram (the slices' and the
 //                         tensor's in one launch).  Positions o in value
 //                         order (-inf .. -0 | +0 .. +inf, NaN patterns at
@@ -38,7 +40,7 @@ namespace moe {
 namespace {
 
 constexpr int kBins = 65536;       // bf16 bit patterns
-constexpr int kLdsBins = 32768;    // patterns with exponent field < 128, sign included
+constexpr int kLdsBins = 16384;    // patterns with exponent field 64..127, sign included
 constexpr int kHistThreads = 1024;
 constexpr int kFinThreads = 512;   // four finalize workgroups fit on a CU
 constexpr int kOrdFirst = 0x7F;    // value-order position of -inf (below it: negative NaNs)
@@ -81,8 +83,8 @@ __global__ __launch_bounds__(kHistThreads) void audit_hist_kernel(const uint16_t
   auto one = [&](uint32_t v) {
     if ((v & 0x7FFFu) == 0u) {
       ++zeros;
-    } else if ((v & 0x4000u) == 0u) {  // exponent field < 128: |w| < 2
-      atomicAdd(&lds[((v >> 15) << 14) | (v & 0x3FFFu)], 1u);
+    } else if ((v & 0x6000u) == 0x2000u) {  // exponent field 64..127: 2^-63 <= |w| < 2
+      atomicAdd(&lds[((v >> 15) << 13) | (v & 0x1FFFu)], 1u);
     } else {
       __hip_atomic_fetch_add(gh + v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_fetch_add(whole + v, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(kHistThreads) void audit_hist_kernel(const uint16_t
   for (int i = tid; i < kLdsBins; i += kHistThreads) {
     const uint32_t c = lds[i];
     if (c) {
-      const int pat = ((i >> 14) << 15) | (i & 0x3FFF);
+      const int pat = ((i >> 13) << 15) | 0x2000 | (i & 0x1FFF);
       __hip_atomic_fetch_add(gh + pat, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_fetch_add(whole + pat, (unsigned long long)c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -170,7 +172,7 @@ __device__ void finalize_one(CT* __restrict__ h, moe_audit_stats* __restrict__ o
   __shared__ unsigned long long zero_cnt;
   __shared__ int srch[3][4];  // MAD search: first passing chunk, per round and search
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // wave w owns groups kGpw w .. (positions 64 kGpw w ..); in its j-th step
+  // in pass 1 wave w owns groups kGpw w .. (positions 64 kGpw w ..); in its j-th step
   // lane l takes position 64 (kGpw w + j) + l, so every access is one
   // coalesced run
   const int g0 = wave * kGpw;
@@ -228,17 +230,20 @@ __device__ void finalize_one(CT* __restrict__ h, moe_audit_stats* __restrict__ o
   const unsigned long long k1 = n ? (n - 1) / 2 : 0, k2 = n / 2;
   // pass 2, occupied groups only, eight groups' loads in flight together:
   // counts -> inclusive counts in value order, in place (stored at each
-  // position's own pattern); find the positions of ranks k1 and k2
+  // position's own pattern); find the positions of ranks k1 and k2.  The
+  // occupied groups cluster around the median, so here wave w takes groups
+  // w, w + kWaves, ... to share them out.
   for (int j0 = 0; j0 < kGpw; j0 += 8) {
     CT cb[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int o = 64 * (g0 + j0 + j) + lane;
-      cb[j] = (gsum[g0 + j0 + j] == 0 || o < kOrdFirst || o > kOrdLast) ? (CT)0 : h[pat_of_ord(o)];
+      const int g = (j0 + j) * kWaves + wave;
+      const int o = 64 * g + lane;
+      cb[j] = (gsum[g] == 0 || o < kOrdFirst || o > kOrdLast) ? (CT)0 : h[pat_of_ord(o)];
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int g = g0 + j0 + j;
+      const int g = (j0 + j) * kWaves + wave;
       if (gsum[g] == 0) continue;  // wave-uniform
       const int o = 64 * g + lane;
       const CT c = cb[j];
@@ -400,9 +405,9 @@ hipError_t launch_audit(const void* w, int64_t slices, int64_t n, int64_t stride
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (n > 0) {
-    // about four workgroups per CU over all slices (one is resident at a time:
-    // the LDS histogram takes 128 KB), each with at least 64 Ki elements
-    int64_t B = (4 * audit_cus() + slices - 1) / slices;
+    // about eight workgroups per CU over all slices (two are resident at a
+    // time: the LDS histogram takes 64 KB), each with at least 64 Ki elements
+    int64_t B = (8 * audit_cus() + slices - 1) / slices;
     const int64_t bmax = n / 65536 > 1 ? n / 65536 : 1;
     B = B < bmax ? B : bmax;
     B = B > 0 ? B : 1;

@@ -60,7 +60,8 @@ def test_audit_matches_oracle(slices, n, zero_frac):
 
 
 def test_audit_special_values_and_layout():
-    # NaN, +-inf, |w| >= 2 (outside the LDS histogram), subnormals, -0, an
+    # NaN, +-inf, |w| >= 2 and normal |w| < 2^-63 (outside the LDS histogram,
+    # with 2^-63 itself the least value inside it), subnormals, -0, an
     # unaligned first slice and gaps between slices (stride > n)
     slices, n, stride = 4, 3001, 3011
     print(f"[audit] special values slices={slices} n={n} stride={stride}", flush=True)
@@ -72,6 +73,8 @@ def test_audit_special_values_and_layout():
     base[2 * stride: 2 * stride + 500] = torch.linspace(-300, 300, 500, device="cuda").to(torch.bfloat16)
     base[3 * stride: 3 * stride + 40] = torch.tensor([1e-39, -2e-39] * 20, device="cuda").to(torch.bfloat16)
     base[3 * stride + 40: 3 * stride + 1700] = -0.0
+    tiny = [2.0 ** -63, -(2.0 ** -63), 2.0 ** -64, -(2.0 ** -64), 1e-25, -3e-30, 2.0 ** -126]
+    base[3 * stride + 1700: 3 * stride + 1700 + 7 * 30] = torch.tensor(tiny * 30, device="cuda").to(torch.bfloat16)
     recs = run_audit(None, slices, n, stride, base=base)
     hs = host_slices(base, slices, n, stride)
     assert recs[0]["n_nan"] == 1 and math.isnan(recs[0]["sigma_rob"])
