@@ -17,7 +17,9 @@ duration), and the fp64 CPU oracle timed on a bounded sample of the same
 workload on this host's cores.  For bf16 workloads it also reports the
 four-stream gated residual read and write around the layer at the same T and
 H, and the expert-weight audit of the layer's gate tensor (event-timed, with
-their own rooflines); they are not part of the step.
+their own rooflines); they are not part of the step.  Every workload also
+reports one GPU's share under expert parallelism over 8 GPUs: the grouped
+FFN of each rank's E/8 experts on the rows the same routing sends them.
 """
 from __future__ import annotations
 
@@ -204,6 +206,75 @@ def weight_audit(lib, acc, args, prob, stream):
                       "sigma_rob": whole["sigma_rob"]}}
 
 
+def ep_share(lib, acc, args, cfg, dev, stream, prob, offs, sa, ranks=8):
+    """One GPU's share of the layer under expert parallelism over `ranks`
+    GPUs (the Flash-Next MoE section, expert parallelism: each routed row
+    travels to the GPU that owns its expert and its result travels back to
+    the token's GPU for the combine).  Rank r owns
+    the experts e = r (mod ranks) and runs the grouped FFN on every row that
+    the whole batch's routing sends them, received as a compact [R_r, H]
+    block: moe_expert_ffn with the owned experts addressed through expert
+    strides.  Each rank's FFN is timed over --steps calls with HIP events on
+    the launch stream, against its own roof max(F/P, B/BW) with
+    F = 6 R_r H I and B = its touched experts' weights + the received rows
+    + y.  The all-to-all exchanges, the shared expert (it runs at the token's
+    home GPU) and the combine are not in it.  Not part of the step."""
+    import torch
+
+    E, k, H, I = cfg.E, cfg.k, cfg.H, cfg.I
+    if E % ranks:
+        return None
+    Ep = E // ranks
+    offs_h = offs.cpu().long()
+    counts = torch.diff(offs_h)
+    tok = sa.long() // k  # token of every dispatched row, in expert order
+    fp8 = cfg.wdt == "fp8"
+    a_b, w_b = acc.WBYTES[cfg.act], acc.WBYTES[cfg.wdt]
+    res = {"ranks": ranks, "experts_per_rank": Ep, "rows": [], "touched": [], "ms": [], "roof_frac": []}
+    for r in range(ranks):
+        c = counts[r::ranks]
+        Rr = int(c.sum())
+        touched = int((c > 0).sum())
+        res["rows"].append(Rr)
+        res["touched"].append(touched)
+        if Rr == 0:
+            res["ms"].append(0.0)
+            res["roof_frac"].append(None)
+            continue
+        idx = torch.cat([torch.arange(int(offs_h[e]), int(offs_h[e + 1])) for e in range(r, E, ranks)])
+        xr = prob.x.index_select(0, tok[idx.to(dev)])  # the rows this rank receives
+        offr = torch.zeros(Ep + 1, dtype=torch.int32)
+        offr[1:] = torch.cumsum(c, 0)
+        offr = offr.to(dev)
+        sar = torch.arange(Rr, dtype=torch.int32, device=dev)
+        P = lib.problem(Rr, H, Ep, 1, I, 0, cfg.act, cfg.wdt, cfg.scale_block, 0)
+        sc = [t[r::ranks].contiguous() if fp8 else None for t in (prob.s_gate, prob.s_up, prob.s_down)]
+        W = lib.weights(None, prob.w_gate[r], prob.w_up[r], prob.w_down[r], *sc,
+                        stride_gate=ranks * I * H, stride_up=ranks * I * H, stride_down=ranks * H * I)
+        ws = lib.workspace(P)
+        y = torch.empty((Rr, H), dtype=prob.x.dtype, device=dev)
+        for _ in range(max(1, args.warmup)):
+            lib.moe_expert_ffn(P, W, xr, offr, sar, y, None, ws, stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            lib.moe_expert_ffn(P, W, xr, offr, sar, y, None, ws, stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        t = ev[0].elapsed_time(ev[1]) / args.steps * 1e-3
+        f = 6.0 * Rr * H * I
+        b = touched * 3.0 * I * H * w_b + 2.0 * Rr * H * a_b
+        if fp8:
+            b += touched * 3.0 * (I // cfg.scale_block) * (H // cfg.scale_block) * 4
+        t_roof = max(f / (acc.PEAK_BF16_TFLOPS * 1e12), b / (acc.PEAK_HBM_GBPS * 1e9))
+        res["ms"].append(round(t * 1e3, 4))
+        res["roof_frac"].append(round(t_roof / t, 4))
+        del xr, y, ws
+    res["max_ms"] = max(res["ms"])
+    res["mean_ms"] = round(sum(res["ms"]) / ranks, 4)
+    return res
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -309,6 +380,7 @@ def main():
     gr = (gated_residual(lib, acc, args, cfg, dev, stream, (P, y, pos, tw, y_sh, sl))
           if cfg.act == "bf16" else None)
     audit = weight_audit(lib, acc, args, prob, stream) if cfg.wdt == "bf16" else None
+    ep = ep_share(lib, acc, args, cfg, dev, stream, prob, offs, sa)
 
     t_s = ms_step * 1e-3
     res = {
@@ -340,6 +412,7 @@ def main():
         "roofline": roof,
         "gated_residual": gr,
         "weight_audit": audit,
+        "ep_share": ep,
     }
     if args.cpu_tokens != 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -316,6 +316,44 @@ def test_fused_gate_up_strides():
     assert np.array_equal(out.float().cpu().numpy(), ref["out_layer"])
 
 
+@pytest.mark.parametrize("name,flags", [
+    ("max_prefill", lib.MOE_FLAG_FORCE_GEMM | lib.MOE_FLAG_GEMM_TILE_128),
+    ("max_prefill", lib.MOE_FLAG_FORCE_GEMM | lib.MOE_FLAG_GEMM_TILE_256),
+    ("max_prefill", lib.MOE_FLAG_FORCE_STREAM),
+    ("max_fp8", lib.MOE_FLAG_FORCE_GEMM | lib.MOE_FLAG_GEMM_TILE_256)])
+def test_expert_parallel_share(name, flags):
+    # one GPU's share under expert parallelism over 4 ranks: rank r owns the
+    # experts e = r (mod 4), addressed through expert strides, and receives
+    # the rows the routing sends them as a compact block; with the kernel
+    # pinned, every row of its y has the bits of the whole layer's y row
+    ranks = 4
+    cfg = CONFIGS[name].with_(name="ep_" + name, T=384, H=256, E=16, k=4, I=128, I_shared=0)
+    p = gpu_problem(cfg, 12)
+    full = run_stages(p, flags)
+    offs = full["offsets"].astype(np.int64)
+    counts = np.diff(offs)
+    tok = full["sorted"].astype(np.int64) // cfg.k
+    fp8 = cfg.wdt == "fp8"
+    for r in range(ranks):
+        own = list(range(r, cfg.E, ranks))
+        rows = np.concatenate([np.arange(offs[e], offs[e + 1]) for e in own])
+        Rr = len(rows)
+        print(f"[parity] ep share rank {r}: {Rr} rows", flush=True)
+        if Rr == 0:
+            continue
+        xr = p.x.index_select(0, torch.from_numpy(tok[rows]).cuda())
+        offr = torch.from_numpy(np.concatenate([[0], np.cumsum(counts[r::ranks])]).astype(np.int32)).cuda()
+        sar = torch.arange(Rr, dtype=torch.int32, device="cuda")
+        P = lib.problem(Rr, cfg.H, len(own), 1, cfg.I, 0, cfg.act, cfg.wdt, cfg.scale_block, flags)
+        sc = [t[r::ranks].contiguous() if fp8 else None for t in (p.s_gate, p.s_up, p.s_down)]
+        W = lib.weights(None, p.w_gate[r], p.w_up[r], p.w_down[r], *sc, stride_gate=ranks * cfg.I * cfg.H,
+                        stride_up=ranks * cfg.I * cfg.H, stride_down=ranks * cfg.H * cfg.I)
+        y = torch.zeros((Rr, cfg.H), dtype=p.x.dtype, device="cuda")
+        lib.moe_expert_ffn(P, W, xr, offr, sar, y, None, lib.workspace(P))
+        torch.cuda.synchronize()
+        assert np.array_equal(y.float().cpu().numpy(), full["y"][rows]), f"rank {r}"
+
+
 def test_run_to_run_bit_identical():
     cfg = CONFIGS["flash_prefill"].with_(name="determinism", T=512, H=512, E=64, k=6, I=128, I_shared=128)
     p = gpu_problem(cfg, 9)
