@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=-1,
                     help="tokens of the same workload the CPU oracle runs on (0: skip; -1: grown from 64 "
                          "until one run takes 10 s or covers the batch)")
+    ap.add_argument("--no-ep-share", action="store_true",
+                    help="skip the expert-parallel share runs (they launch the layer's own FFN kernels, so "
+                         "kernel traces and counter runs of the layer leave them out)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scale factor for HBM byte counters)")
     return ap.parse_args()
@@ -380,7 +383,7 @@ def main():
     gr = (gated_residual(lib, acc, args, cfg, dev, stream, (P, y, pos, tw, y_sh, sl))
           if cfg.act == "bf16" else None)
     audit = weight_audit(lib, acc, args, prob, stream) if cfg.wdt == "bf16" else None
-    ep = ep_share(lib, acc, args, cfg, dev, stream, prob, offs, sa)
+    ep = None if args.no_ep_share else ep_share(lib, acc, args, cfg, dev, stream, prob, offs, sa)
 
     t_s = ms_step * 1e-3
     res = {
