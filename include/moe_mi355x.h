@@ -292,7 +292,8 @@ typedef struct moe_audit_stats {
 } moe_audit_stats;
 
 /* Scratch bytes of moe_weight_audit: one 65536-bin uint32 histogram per
- * slice and one uint64 histogram of the whole tensor.  0 if slices < 1 or
+ * slice, with a table of its 1024 group counts (64 value-order positions a
+ * group), and one uint64 histogram of the whole tensor.  0 if slices < 1 or
  * slices > 65535. */
 size_t moe_audit_workspace_bytes(int64_t slices);
 

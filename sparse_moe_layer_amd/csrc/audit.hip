@@ -12,11 +12,19 @@
 //                         sign) in a 64 KB LDS histogram, the rare rest with
 //                         global atomics; each workgroup then adds its
 //                         non-empty LDS bins into the slice's histogram and
-//                         the whole tensor's (uint64) in HBM.  Two
-//                         workgroups share a CU, so one's flush overlaps
+//                         the whole tensor's (uint64) in HBM, and the count
+//                         of each 64-position group in value order into the
+//                         slice's group table (a wave's 64 LDS bins are one
+//                         group).
+//                         Two workgroups share a CU, so one's flush overlaps
 //                         the other's stream.
 //   audit_finalize_kernel one workgroup per histogram (the slices' and the
-//                         tensor's in one launch).  Positions o in value
+//                         tensor's in one launch).  A slice's workgroup takes
+//                         the group counts from the group table and reads
+//                         only occupied groups of the histogram; the
+//                         tensor's reads its whole histogram once for them
+//                         (a tensor-wide table would put every workgroup's
+//                         flush on the same few addresses).  Positions o in value
 //                         order (-inf .. -0 | +0 .. +inf, NaN patterns at
 //                         both ends) are dealt 8192 per wave; wave scans and
 //                         a scan of the wave sums turn each histogram, in place,
@@ -46,25 +54,48 @@ constexpr int kFinThreads = 512;   // four finalize workgroups fit on a CU
 constexpr int kOrdFirst = 0x7F;    // value-order position of -inf (below it: negative NaNs)
 constexpr int kOrdLast = 0xFF80;   // +inf (above it: positive NaNs)
 constexpr int kOrdZero = 0x8000;   // +0, which holds the count of every zero
+constexpr int kGroups = kBins / 64; // 64-position groups in value order
 constexpr double kSigmaRobScale = 1.4826;
 
 // value order <-> pattern: negative patterns in descending magnitude, then
 // the positive ones in ascending order
 __device__ __forceinline__ int pat_of_ord(int o) { return o < 0x8000 ? (0x8000 | (0x7FFF - o)) : (o - 0x8000); }
+__device__ __forceinline__ int ord_of_pat(uint32_t v) { return (v & 0x8000u) ? 0x7FFF - (int)(v & 0x7FFFu) : (int)v + 0x8000; }
 __device__ __forceinline__ double val_of_ord(int o) {
   return (double)__uint_as_float((uint32_t)pat_of_ord(o) << 16);
 }
 
-__global__ void audit_clear_kernel(uint32_t* __restrict__ hist, int64_t n32, unsigned long long* __restrict__ whole) {
+// Inclusive scan over the 64 lanes of a wave.
+template <typename CT>
+__device__ __forceinline__ CT wave_incl_scan(CT v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const CT t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+template <typename CT>
+__device__ __forceinline__ CT wave_total(CT v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__global__ void audit_clear_kernel(uint32_t* __restrict__ hist, int64_t n32, unsigned long long* __restrict__ whole,
+                                   uint32_t* __restrict__ grp, int64_t g32) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t step = (int64_t)gridDim.x * blockDim.x;
   for (int64_t j = i; j < n32; j += step) hist[j] = 0u;
   for (int64_t j = i; j < kBins; j += step) whole[j] = 0ull;
+  for (int64_t j = i; j < g32; j += step) grp[j] = 0u;
 }
 
 __global__ __launch_bounds__(kHistThreads) void audit_hist_kernel(const uint16_t* __restrict__ w, int64_t n,
                                                                   int64_t stride, uint32_t* __restrict__ hist,
-                                                                  unsigned long long* __restrict__ whole) {
+                                                                  unsigned long long* __restrict__ whole,
+                                                                  uint32_t* __restrict__ grp) {
   __shared__ uint32_t lds[kLdsBins];
   __shared__ uint32_t zsum;
   const int tid = threadIdx.x;
@@ -73,6 +104,8 @@ __global__ __launch_bounds__(kHistThreads) void audit_hist_kernel(const uint16_t
   __syncthreads();
   const int slice = blockIdx.y, B = gridDim.x, b = blockIdx.x;
   uint32_t* gh = hist + (int64_t)slice * kBins;
+  uint32_t* gg = grp + (int64_t)slice * kGroups;
+  const int lane = tid & 63;
   const uint16_t* p = w + (int64_t)slice * stride;
   // this workgroup's element range, cut at multiples of 8 elements
   const int64_t units = (n + 7) / 8;
@@ -88,6 +121,7 @@ __global__ __launch_bounds__(kHistThreads) void audit_hist_kernel(const uint16_t
     } else {
       __hip_atomic_fetch_add(gh + v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_fetch_add(whole + v, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(gg + (ord_of_pat(v) >> 6), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
   if (lo < hi) {
@@ -119,47 +153,38 @@ __global__ __launch_bounds__(kHistThreads) void audit_hist_kernel(const uint16_t
   }
   if (zeros) atomicAdd(&zsum, zeros);
   __syncthreads();
+  // a wave's 64 consecutive LDS bins are 64 consecutive patterns from a
+  // multiple of 64, which is one 64-position group in value order
+  static_assert(kHistThreads % 64 == 0 && kLdsBins % kHistThreads == 0, "whole waves over the LDS bins");
   for (int i = tid; i < kLdsBins; i += kHistThreads) {
     const uint32_t c = lds[i];
+    const int pat = ((i >> 13) << 15) | 0x2000 | (i & 0x1FFF);
     if (c) {
-      const int pat = ((i >> 13) << 15) | 0x2000 | (i & 0x1FFF);
       __hip_atomic_fetch_add(gh + pat, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_fetch_add(whole + pat, (unsigned long long)c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (__ballot(c != 0)) {
+      const uint32_t gs = wave_total<uint32_t>(c);
+      if (lane == 0)
+        __hip_atomic_fetch_add(gg + (ord_of_pat((uint32_t)pat) >> 6), gs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (tid == 0 && zsum) {
     __hip_atomic_fetch_add(gh, zsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_fetch_add(whole, (unsigned long long)zsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(gg + (kOrdZero >> 6), zsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-}
-
-// Inclusive scan over the 64 lanes of a wave.
-template <typename CT>
-__device__ __forceinline__ CT wave_incl_scan(CT v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const CT t = __shfl_up(v, off, 64);
-    if (lane >= off) v += t;
-  }
-  return v;
-}
-
-template <typename CT>
-__device__ __forceinline__ CT wave_total(CT v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
 }
 
 __device__ __forceinline__ unsigned long long dbits(double d) { return (unsigned long long)__double_as_longlong(d); }
 
 // Statistics of one histogram h (in place: the occupied groups become
-// value-order prefix counts).  Positions come in 1024 groups of 64; a group
-// with no values is never read again after pass 1, and its prefix count
-// lives in LDS.
+// value-order prefix counts) with its group table gtab (values in each
+// 64-position group), or, with gtab null, the group counts taken from h.
+// A group with no values is not read again, and its prefix count lives in
+// LDS.
 template <typename CT>
-__device__ void finalize_one(CT* __restrict__ h, moe_audit_stats* __restrict__ out) {
-  constexpr int kGroups = kBins / 64;
+__device__ void finalize_one(CT* __restrict__ h, const CT* __restrict__ gtab, moe_audit_stats* __restrict__ out) {
   constexpr int kWaves = kFinThreads / 64;
   constexpr int kGpw = kGroups / kWaves;        // groups per wave
   constexpr int kGpt = kGroups / kFinThreads;   // groups per thread in the group scan
@@ -172,10 +197,6 @@ __device__ void finalize_one(CT* __restrict__ h, moe_audit_stats* __restrict__ o
   __shared__ unsigned long long zero_cnt;
   __shared__ int srch[3][4];  // MAD search: first passing chunk, per round and search
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // in pass 1 wave w owns groups kGpw w .. (positions 64 kGpw w ..); in its j-th step
-  // lane l takes position 64 (kGpw w + j) + l, so every access is one
-  // coalesced run
-  const int g0 = wave * kGpw;
   if (tid == 0) {
     nan_sum = 0ull;
     ord_k[0] = ord_k[1] = -1;
@@ -183,26 +204,48 @@ __device__ void finalize_one(CT* __restrict__ h, moe_audit_stats* __restrict__ o
     zero_cnt = 0ull;
   }
   __syncthreads();
-  // pass 1: every group's count (NaN patterns are counted apart and take no
-  // place in the order)
-  unsigned long long nans = 0;
-  for (int j0 = 0; j0 < kGpw; j0 += 16) {
-    CT cb[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) cb[j] = h[pat_of_ord(64 * (g0 + j0 + j) + lane)];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int o = 64 * (g0 + j0 + j) + lane;
-      CT c = cb[j];
-      if (o < kOrdFirst || o > kOrdLast) {
-        nans += (unsigned long long)c;
-        c = 0;
+  // pass 1: every group's count.  NaN patterns take no place in the order:
+  // they sit below kOrdFirst (groups 0 and 1) and above kOrdLast (groups
+  // 1022 and 1023), and are counted apart.
+  if (gtab) {
+    for (int g = tid; g < kGroups; g += kFinThreads) gsum[g] = gtab[g];
+    __syncthreads();
+    if (wave == 0) {  // the four edge groups
+      unsigned long long nans = 0;
+      for (int e = 0; e < 4; ++e) {
+        const int g = e < 2 ? e : kGroups - 4 + e;
+        if (gsum[g] == 0) continue;  // wave-uniform
+        const int o = 64 * g + lane;
+        const CT c = (o < kOrdFirst || o > kOrdLast) ? h[pat_of_ord(o)] : (CT)0;
+        const CT tot = wave_total<CT>(c);
+        nans += (unsigned long long)tot;
+        if (lane == 0) gsum[g] -= tot;
       }
-      const CT gs = __ballot(c != 0) ? wave_total<CT>(c) : (CT)0;
-      if (lane == 0) gsum[g0 + j0 + j] = gs;
+      if (lane == 0) nan_sum = nans;
     }
+  } else {
+    // wave w reads groups kGpw w ..; in its j-th step lane l takes position
+    // 64 (kGpw w + j) + l, so every access is one coalesced run
+    const int g0 = wave * kGpw;
+    unsigned long long nans = 0;
+    for (int j0 = 0; j0 < kGpw; j0 += 16) {
+      CT cb[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) cb[j] = h[pat_of_ord(64 * (g0 + j0 + j) + lane)];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int o = 64 * (g0 + j0 + j) + lane;
+        CT c = cb[j];
+        if (o < kOrdFirst || o > kOrdLast) {
+          nans += (unsigned long long)c;
+          c = 0;
+        }
+        const CT gs = __ballot(c != 0) ? wave_total<CT>(c) : (CT)0;
+        if (lane == 0) gsum[g0 + j0 + j] = gs;
+      }
+    }
+    if (nans) atomicAdd(&nan_sum, nans);
   }
-  if (nans) atomicAdd(&nan_sum, nans);
   __syncthreads();
   // exclusive prefix of the group counts: thread t holds groups kGpt t ..
   {
@@ -370,9 +413,11 @@ __device__ void finalize_one(CT* __restrict__ h, moe_audit_stats* __restrict__ o
 // the whole tensor's (uint64), all in one launch.
 __global__ __launch_bounds__(kFinThreads) void audit_finalize_kernel(uint32_t* __restrict__ hist,
                                                                      unsigned long long* __restrict__ whole,
-                                                                     int slices, moe_audit_stats* __restrict__ out) {
-  if ((int)blockIdx.x < slices) finalize_one<uint32_t>(hist + (int64_t)blockIdx.x * kBins, out + blockIdx.x);
-  else finalize_one<unsigned long long>(whole, out + slices);
+                                                                     const uint32_t* __restrict__ grp, int slices, moe_audit_stats* __restrict__ out) {
+  if ((int)blockIdx.x < slices)
+    finalize_one<uint32_t>(hist + (int64_t)blockIdx.x * kBins, grp + (int64_t)blockIdx.x * kGroups, out + blockIdx.x);
+  else
+    finalize_one<unsigned long long>(whole, nullptr, out + slices);
 }
 
 int audit_cus() {
@@ -390,18 +435,23 @@ inline size_t up256(size_t b) { return (b + 255) / 256 * 256; }
 
 }  // namespace
 
+// workspace: slice histograms [slices][65536] u32 | tensor histogram [65536]
+// u64 | slice group tables [slices][1024] u32
 size_t audit_workspace_bytes(int64_t slices) {
-  return up256((size_t)slices * kBins * sizeof(uint32_t)) + (size_t)kBins * sizeof(unsigned long long);
+  return up256((size_t)slices * kBins * sizeof(uint32_t)) + (size_t)kBins * sizeof(unsigned long long) +
+         (size_t)slices * kGroups * sizeof(uint32_t);
 }
 
 hipError_t launch_audit(const void* w, int64_t slices, int64_t n, int64_t stride, moe_audit_stats* stats, void* ws,
                         hipStream_t st) {
   uint32_t* hist = static_cast<uint32_t*>(ws);
-  auto* whole = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) +
-                                                      up256((size_t)slices * kBins * sizeof(uint32_t)));
-  const int64_t n32 = slices * (int64_t)kBins;
+  char* b = static_cast<char*>(ws) + up256((size_t)slices * kBins * sizeof(uint32_t));
+  auto* whole = reinterpret_cast<unsigned long long*>(b);
+  b += (size_t)kBins * sizeof(unsigned long long);
+  auto* grp = reinterpret_cast<uint32_t*>(b);
+  const int64_t n32 = slices * (int64_t)kBins, g32 = slices * (int64_t)kGroups;
   const int64_t cgrid = (n32 + 255) / 256;
-  audit_clear_kernel<<<(unsigned)(cgrid < 4096 ? cgrid : 4096), 256, 0, st>>>(hist, n32, whole);
+  audit_clear_kernel<<<(unsigned)(cgrid < 4096 ? cgrid : 4096), 256, 0, st>>>(hist, n32, whole, grp, g32);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (n > 0) {
@@ -412,11 +462,11 @@ hipError_t launch_audit(const void* w, int64_t slices, int64_t n, int64_t stride
     B = B < bmax ? B : bmax;
     B = B > 0 ? B : 1;
     audit_hist_kernel<<<dim3((unsigned)B, (unsigned)slices), kHistThreads, 0, st>>>(
-        static_cast<const uint16_t*>(w), n, stride, hist, whole);
+        static_cast<const uint16_t*>(w), n, stride, hist, whole, grp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  audit_finalize_kernel<<<(unsigned)(slices + 1), kFinThreads, 0, st>>>(hist, whole, (int)slices, stats);
+  audit_finalize_kernel<<<(unsigned)(slices + 1), kFinThreads, 0, st>>>(hist, whole, grp, (int)slices, stats);
   return hipGetLastError();
 }
 
