@@ -153,9 +153,9 @@ moe_status moe_validate(const moe_problem* p);
  * maximum over entry points; 0 if p is invalid).  Host only. */
 size_t moe_workspace_bytes(const moe_problem* p);
 
-/* Router, softmax, top-k and renormalisation ("Router [T, 512]" and
- * "Top 10 + normalize" in the pipeline figure; "Selected router
- * probabilities are normalized").
+/* Router, softmax, top-k and renormalisation (the router and top-k stages of
+ * the pipeline figure in the Qwen3.8-Flash-Next study's MoE section, which
+ * renormalises the chosen experts' probabilities to sum to one).
  *   x [T,H] act, w_router [E,H] act, sh_gate_w [1,H] act or NULL.
  * Outputs: topk_ids [T,k] int32, descending logit (ties -> lower id);
  *          topk_w   [T,k] fp32, exp(l_j - l_max) / sum over the k chosen;
@@ -167,9 +167,12 @@ moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
                      const void* sh_gate_w, int32_t* topk_ids, float* topk_w,
                      float* shared_logit, void* ws, size_t ws_bytes, void* stream);
 
-/* Dispatch ("Dispatch R tokens"): dropless, stable counting sort of the R = T*k
- * flat assignments a = t*k + j by expert id.
- *   topk_ids [T,k] int32 in [0,E).
+/* Dispatch (the dispatch stage of the pipeline figure): dropless, stable
+ * counting sort of the R = T*k flat assignments a = t*k + j by expert id.
+ *   topk_ids [T,k] int32 in [0,E).  The router gives k distinct ids per
+ *   token; repeated ids are still sorted stably (each assignment its own
+ *   slot), and ids outside [0,E) are clamped into range, so the outputs are
+ *   always a permutation and its inverse.
  * Outputs: expert_offsets [E+1] int32 (exclusive prefix sum of per-expert
  *          counts, offsets[E] = R); sorted_assign [R] int32 (assignments in
  *          (expert, a) order); assign_pos [R] int32 (its inverse).           */
@@ -177,8 +180,8 @@ moe_status moe_dispatch(const moe_problem* p, const int32_t* topk_ids,
                         int32_t* expert_offsets, int32_t* sorted_assign,
                         int32_t* assign_pos, void* ws, size_t ws_bytes, void* stream);
 
-/* Grouped expert FFN ("Grouped expert GEMMs"): for every dispatched row
- * r in [offsets[e], offsets[e+1]) with token t = sorted_assign[r] / k,
+/* Grouped expert FFN (the grouped expert GEMM stage of the figure): for
+ * every dispatched row r in [offsets[e], offsets[e+1]) with token t = sorted_assign[r] / k,
  *   y[r] = expert_e(x_t)              (y [R,H] act, permuted order)
  * and, if the problem has a shared expert and y_shared != NULL,
  *   y_shared[t] = shared(x_t)         (y_shared [T,H] act).
@@ -204,8 +207,8 @@ moe_status moe_expert_down(const moe_problem* p, const moe_weights* w, const int
                            const void* h, const void* h_shared, void* y, void* y_shared,
                            void* ws, size_t ws_bytes, void* stream);
 
-/* Weighted combine + gated shared expert ("Weighted combine + gated shared
- * expert"; eq. MoE(x)):
+/* Weighted combine + gated shared expert (the figure's last stage;
+ * eq. MoE(x)):
  *   out[t] = sum_{j<k} topk_w[t,j] * y[assign_pos[t*k+j]]
  *            + sigmoid(shared_logit[t]) * y_shared[t]
  * in fp32, j ascending, then rounded to act dtype.  y_shared and

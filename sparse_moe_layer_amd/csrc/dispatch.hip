@@ -1,6 +1,7 @@
-// Dispatch (Qwen3.8-Flash-Next study, MoE section: "Dispatch R tokens"; the
-// glance section defines R = 10T assignments, i.e. no drops): a stable
-// counting sort of the R = T*k flat assignments a = t*k + j by expert id.
+// Dispatch (Qwen3.8-Flash-Next study, MoE section: the dispatch stage of its
+// pipeline figure; its glance section defines R = 10T assignments, i.e. no
+// drops): a stable counting sort of the R = T*k flat assignments
+// a = t*k + j by expert id.
 //
 //  1. count  : one workgroup per chunk of 32 tokens; per-expert counts of
 //              the chunk in LDS (LDS atomics only count, order comes later).
@@ -8,13 +9,15 @@
 //              chunks (64 experts per workgroup, chunks split over 16 waves)
 //              and the expert's total.
 //  3. scatter: one wave per chunk scans the E totals into expert_offsets,
-//              then walks its tokens in order; the k lanes of a token hit k
-//              distinct experts, so each lane bumps its expert's LDS cursor
-//              without conflict, and positions come out ascending in a
-//              within every expert (stable).
-// Expert ids outside [0, E) are clamped into range so the result is always a
-// permutation (memory-safe); ids repeated within a token give an
-// unspecified (still in-range) order.
+//              then walks its tokens in order; lane j of a token takes its
+//              expert's LDS cursor plus the number of lanes j' < j of the
+//              same token with the same expert, and the last such lane
+//              advances the cursor by the group's size, so positions come
+//              out ascending in a within every expert (stable).
+// The router never repeats an expert within a token, but moe_dispatch takes
+// caller ids: a repeated id still gets its own slot (ordered by j), and ids
+// outside [0, E) are clamped into range, so sorted_assign is always a
+// permutation of [0, R) and assign_pos its inverse.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -24,6 +27,72 @@ namespace {
 constexpr int CH = 32;  // tokens per chunk
 
 __device__ __forceinline__ int clamp_e(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
+
+// Lanes 0..k-1 of a wave hold the experts of one token.  For lane `lane`
+// (< k): how many lanes before it hold the same expert, and how many hold it
+// in all.  Lanes >= k pass e = -1, which matches no lane < k.  The lane index
+// j of the readlane is uniform, so this is k scalar reads of e with no LDS
+// round trip.
+struct TokenRank {
+  int before, group;
+};
+__device__ __forceinline__ TokenRank token_rank(int e, int lane, int k) {
+  TokenRank r{0, 0};
+  for (int j = 0; j < k; ++j) {
+    const int ej = __builtin_amdgcn_readlane(e, j);
+    const int same = ej == e ? 1 : 0;
+    r.group += same;
+    r.before += j < lane ? same : 0;
+  }
+  return r;
+}
+
+// Wave-level scatter of up to CH consecutive tokens t0 .. t0+nt-1 in token
+// order (lane j < k handles assignment a = t*k + j).  Every lane first loads
+// its expert of every token.  Per token, each lane writes its lane index to
+// mark[e] and reads it back: with no other lane of the token on e it reads
+// its own index, so a mismatch anywhere means a repeated expert.  The router
+// never repeats one, and then each lane takes p = cur[e], cur[e] = p + 1.
+// Otherwise every lane adds its rank among the token's lanes with the same
+// expert, and the last of them advances the cursor by the group's size.
+__device__ __forceinline__ void scatter_tokens(const int32_t* __restrict__ ids, int t0, int nt, int E, int k,
+                                               int lane, int* cur, int* mark, int32_t* __restrict__ sorted,
+                                               int32_t* __restrict__ pos) {
+  int ev[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i)
+    ev[i] = (lane < k && i < nt) ? clamp_e(ids[(int64_t)(t0 + i) * k + lane], E) : -1;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    if (i < nt) {
+      const int e = ev[i];
+      const bool mine = lane < k;
+      // volatile: the read must observe the write instruction's winner, not
+      // this lane's own stored value
+      volatile int* mk = mark;
+      if (mine) mk[e] = lane;
+      const bool rep = mine && mk[e] != lane;
+      const int64_t a = (int64_t)(t0 + i) * k + lane;
+      if (__ballot(rep) == 0) {
+        if (mine) {
+          const int p = cur[e];
+          cur[e] = p + 1;
+          sorted[p] = (int32_t)a;
+          pos[a] = p;
+        }
+      } else {
+        const TokenRank rk = token_rank(e, lane, k);
+        if (mine) {
+          const int p = cur[e] + rk.before;
+          if (rk.before + 1 == rk.group) cur[e] = p + 1;  // the token's last lane on e advances it
+          sorted[p] = (int32_t)a;
+          pos[a] = p;
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
 
 __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
                                                     int32_t* __restrict__ chunk_counts) {
@@ -83,14 +152,14 @@ __global__ __launch_bounds__(1024) void chunk_scan_kernel(int32_t* __restrict__ 
 
 // One wave per chunk.  The wave first turns the per-expert totals into
 // expert offsets (every block redoes this small scan; block 0 publishes
-// them), then walks its tokens in order: the k lanes of a token hit k
-// distinct experts, so each bumps its expert's LDS cursor without conflict.
+// them), then walks its tokens in order: lane j of a token takes its
+// expert's cursor plus its rank among the token's lanes with that expert.
 __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
                                                      const int32_t* __restrict__ chunk_prefix,
                                                      const int32_t* __restrict__ totals,
                                                      int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
                                                      int32_t* __restrict__ pos) {
-  extern __shared__ int cur[];
+  extern __shared__ int cur[];  // [E] cursors, then [E] marks
   const int lane = threadIdx.x;
   // lane owns experts [lane*per, lane*per + per)
   const int per = (E + 63) / 64;
@@ -115,18 +184,8 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
   if (blockIdx.x == 0 && lane == 63) offsets[E] = incl;
   __syncthreads();
   const int t0 = blockIdx.x * CH;
-  const int t1 = t0 + CH < T ? t0 + CH : T;
-  for (int t = t0; t < t1; ++t) {
-    if (lane < k) {
-      const int64_t a = (int64_t)t * k + lane;
-      const int e = clamp_e(ids[a], E);
-      const int p = cur[e];
-      cur[e] = p + 1;
-      sorted[p] = (int32_t)a;
-      pos[a] = p;
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
+  const int nt = T - t0 < CH ? T - t0 : CH;
+  scatter_tokens(ids, t0, nt, E, k, lane, cur, cur + E, sorted, pos);
 }
 
 // Whole dispatch of a batch of at most CH tokens in one 1024-thread
@@ -136,6 +195,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ sorted, int32_t* __restrict__ pos) {
   __shared__ int cur[1024];
+  __shared__ int mark[1024];
   __shared__ int wsum[16];
   const int tid = threadIdx.x;
   cur[tid] = 0;
@@ -171,19 +231,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
   }
   if (tid == 0) offsets[E] = R;
   __syncthreads();
-  if (w == 0) {
-    for (int t = 0; t < T; ++t) {
-      if (lane < k) {
-        const int a = t * k + lane;
-        const int e = clamp_e(ids[a], E);
-        const int p = cur[e];
-        cur[e] = p + 1;
-        sorted[p] = a;
-        pos[a] = p;
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
+  if (w == 0) scatter_tokens(ids, 0, T, E, k, lane, cur, mark, sorted, pos);
 }
 
 }  // namespace
@@ -200,7 +248,7 @@ hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* off
   int32_t* totals = ws + (size_t)nch * E;
   count_kernel<<<nch, 256, E * sizeof(int), s>>>(ids, T, E, k, ws);
   chunk_scan_kernel<<<(E + 63) / 64, 1024, 0, s>>>(ws, nch, E, totals);
-  scatter_kernel<<<nch, 64, E * sizeof(int), s>>>(ids, T, E, k, ws, totals, offsets, sorted, pos);
+  scatter_kernel<<<nch, 64, 2 * E * sizeof(int), s>>>(ids, T, E, k, ws, totals, offsets, sorted, pos);
   return hipGetLastError();
 }
 

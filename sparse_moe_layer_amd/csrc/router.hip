@@ -1,7 +1,8 @@
 // Router epilogue: the fp32 logits (sum of K-chunk partials, chunk order
 // fixed), softmax, top-k and renormalisation, one wavefront per token
-// (Qwen3.8-Flash-Next study, MoE section: "Top 10 + normalize" in the
-// pipeline figure; "Selected router probabilities are normalized").
+// (Qwen3.8-Flash-Next study, MoE section: the top-k stage of its pipeline
+// figure, where the chosen experts' probabilities are renormalised to sum to
+// one).
 //
 // Each lane holds E/64 logits as 64-bit keys: an order-preserving image of
 // the fp32 value in the high word, the complement of the expert id in the low

@@ -32,7 +32,7 @@ __global__ void gateup_f32(FfnArgs f, int R, int rows) {
     if (j >= f.I) return;
     const int e = expert_of_row(f.offsets, f.E, r);
     int tok = f.sorted[r] / f.k;
-    tok = tok < f.T ? tok : f.T - 1;
+    tok = (unsigned)tok < (unsigned)f.T ? tok : f.T - 1;  // also clamps a negative index
     a = x + (int64_t)tok * f.H;
     wg = reinterpret_cast<const float*>(f.wg) + (int64_t)e * f.sg + (int64_t)j * f.H;
     wu = reinterpret_cast<const float*>(f.wu) + (int64_t)e * f.su + (int64_t)j * f.H;

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import sparse_moe_layer_amd as lib
-from oracle import adapter
+from oracle import adapter, moe
 from sparse_moe_layer_amd.tensors import structs
 from synthetic import CONFIGS, make_problem
 
@@ -266,6 +266,35 @@ def test_empty_batch_is_noop():
     lib.moe_layer_forward(P, W, p.x, out, None, None, ws)
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
+
+
+@pytest.mark.parametrize("T", [20, 300])
+def test_dispatch_repeated_and_out_of_range_ids(T):
+    # moe_dispatch takes caller ids (the router never repeats one within a
+    # token): a repeated id still gets its own slot, in ascending flat index
+    # like the oracle's stable sort, and ids outside [0, E) are clamped into
+    # range, so the outputs stay a permutation and its inverse.  T = 20 runs
+    # the one-workgroup dispatch, T = 300 the chunked one.
+    E, k = 24, 6
+    rng = np.random.default_rng(T)
+    ids = rng.integers(0, 3, size=(T, k)).astype(np.int32)  # three experts: many repeats per token
+    ids[::3] = rng.integers(0, E, size=ids[::3].shape)
+    P = lib.problem(T, 64, E, k, 64, 0)
+    ws = lib.workspace(P)
+    for case in ("repeated", "clamped"):
+        host = ids.copy()
+        if case == "clamped":
+            host[0, 0], host[1, 3], host[T - 1, k - 1] = -5, E + 7, -1
+        print(f"[parity] dispatch T={T} {case}", flush=True)
+        offs = torch.full((E + 1,), -1, dtype=torch.int32, device="cuda")
+        sa = torch.full((T * k,), -1, dtype=torch.int32, device="cuda")
+        pos = torch.full((T * k,), -1, dtype=torch.int32, device="cuda")
+        lib.moe_dispatch(P, torch.from_numpy(host).cuda(), offs, sa, pos, ws)
+        torch.cuda.synchronize()
+        _, r_off, r_sa, r_pos = moe.dispatch(np.clip(host, 0, E - 1), E)
+        assert np.array_equal(offs.cpu().numpy(), r_off)
+        assert np.array_equal(sa.cpu().numpy(), r_sa)
+        assert np.array_equal(pos.cpu().numpy(), r_pos)
 
 
 @pytest.mark.parametrize("shared", [0, 128])
