@@ -1,25 +1,27 @@
 #!/usr/bin/env python3
 """Throughput of the routed MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--also NAMES]
 
 One step is one pass of the whole layer over one batch of synthetic input
 resident in HBM: router + top-k, dispatch, grouped gate/up GEMM, grouped down
 GEMM, weighted combine with the gated shared expert, as one moe_layer_forward
-call on the current stream.  K steps are timed back to back between two device
-synchronisations.  The same layer is then run K more times stage by stage,
-each stage through its own C-ABI entry point with HIP events between them;
-those events give the per-stage durations.
+call on the current stream.  The headline workload (default: the 2.4T-shape
+prefill layer, 8192 tokens) is timed as K steps back to back between two
+device synchronisations; `value` is its tokens/s.  K more steps are timed one
+by one with HIP events after a 512 MiB device fill that evicts the caches
+(`cold_ms`: median, p10, p90), and K more stage by stage through the five
+entry points with HIP events between them (`stages_ms`).
 
-Prints one JSON line: tokens/s for the whole step, the roofline of the
-dominant kernel (algorithmic bytes or FLOPs per launch over its event-timed
-duration), and the fp64 CPU oracle timed on a bounded sample of the same
-workload on this host's cores.  For bf16 workloads it also reports the
-four-stream gated residual read and write around the layer at the same T and
-H, and the expert-weight audit of the layer's gate tensor (event-timed, with
-their own rooflines); they are not part of the step.  Every workload also
-reports one GPU's share under expert parallelism over 8 GPUs: the grouped
-FFN of each rank's E/8 experts on the rows the same routing sends them.
+Prints one JSON line: tokens/s for the whole step, the whole layer against
+its binding roof, the roofline of the dominant kernel (algorithmic bytes or
+FLOPs per launch over its event-timed duration), the fp64 CPU oracle timed on
+a bounded sample of the same workload on this host's cores, and the same
+layer-level numbers for the other workloads (`--also`; the decode layer's
+repeated under `decode`).  For bf16 workloads it also reports the four-stream
+gated residual read and write around the layer at the same T and H, and the
+expert-weight audit of the layer's gate tensor (event-timed, with their own
+rooflines); they are not part of the step.
 """
 from __future__ import annotations
 
@@ -42,7 +44,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="flash_prefill", choices=WORKLOADS)
+    ap.add_argument("--workload", default="max_prefill", choices=WORKLOADS,
+                    help="the workload of the headline line (default: the 2.4T-shape 8192-token prefill layer)")
+    ap.add_argument("--also", default="flash_decode,max_fp8,flash_prefill",
+                    help="comma-separated workloads also measured in the same run (layer-level numbers; the "
+                         "decode layer's are repeated under the line's 'decode' key); '' for none")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--gemm-tile", default="auto", choices=["auto", "128", "256"],
                     help="pin the MFMA GEMM kernel (A/B runs); default picks by rows per expert")
@@ -51,9 +57,11 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=-1,
                     help="tokens of the same workload the CPU oracle runs on (0: skip; -1: grown from 64 "
                          "until one run takes 10 s or covers the batch)")
-    ap.add_argument("--no-ep-share", action="store_true",
-                    help="skip the expert-parallel share runs (they launch the layer's own FFN kernels, so "
-                         "kernel traces and counter runs of the layer leave them out)")
+    ap.add_argument("--ep-share", action="store_true",
+                    help="also time one GPU's share under 8-way expert parallelism (off by default)")
+    ap.add_argument("--no-ep-share", action="store_true", help="accepted for older commands (the default)")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="skip the gated-residual and weight-audit rows (kernel traces of the layer alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scale factor for HBM byte counters)")
     return ap.parse_args()
@@ -125,7 +133,9 @@ def cpu_baseline(problem, n_tokens):
         n = min(n_tokens, T)
         dt = run(n)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    model, blas = host_info()
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu_model": model,
+            "blas": blas,
             "sample": f"first {n} of {T} tokens of the same workload, full layer "
                       f"(route, dispatch, every routed and shared expert, combine) in fp64 NumPy; "
                       f"{dt:.1f} s wall"}
@@ -278,6 +288,238 @@ def ep_share(lib, acc, args, cfg, dev, stream, prob, offs, sa, ranks=8):
     return res
 
 
+def host_info():
+    """CPU model and BLAS vendor of this host (for the CPU baseline)."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{p.get('internal_api')} {p.get('version')}" for p in threadpool_info() if p.get("user_api") == "blas"]
+        blas = ", ".join(libs) or None
+    except Exception:
+        pass
+    return model, blas
+
+
+def source_ids():
+    """Git commit of the tree when .git is present (it is not on a copied tree),
+    and a hash of the library and bench sources either way."""
+    sha = None
+    try:
+        import subprocess
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"], capture_output=True, text=True,
+                           timeout=10)
+        if r.returncode == 0:
+            sha = r.stdout.strip()
+    except Exception:
+        pass
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_moe_layer_amd", "csrc")
+    for f in sorted(os.listdir(csrc)) + ["../../include/moe_mi355x.h", "../../bench.py"]:
+        path = os.path.join(csrc, f)
+        if os.path.isfile(path):
+            h.update(open(path, "rb").read())
+    return sha, h.hexdigest()[:16]
+
+
+class ClockSampler:
+    """Samples the GPU shader clock level the driver reports (sysfs
+    pp_dpm_sclk, the level marked '*') from a host thread while a timed region
+    runs.  Reads a text file only; null where the file is not readable."""
+
+    def __init__(self, period=0.02):
+        import glob
+        import threading
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.period = period
+        self.samples = []
+        self._stop = threading.Event()
+        self._th = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        for p in self.paths:
+            try:
+                for line in open(p):
+                    if line.rstrip().endswith("*"):
+                        return int(line.split(":")[1].strip().lower().split("mhz")[0])
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.paths:
+            self._th.start()
+        return self
+
+    def __exit__(self, *a):
+        self._stop.set()
+        if self.paths:
+            self._th.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v)}
+
+
+def pct(vals, q):
+    v = sorted(vals)
+    i = min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))
+    return v[i]
+
+
+def measure(lib, acc, cfg, args, dev, stream, flags, full):
+    """One workload: the contract's timed region (K moe_layer_forward calls
+    back to back between two device synchronisations), then K steps each
+    timed alone with HIP events on the launch stream after a 512 MiB device
+    fill that evicts the L2s and the 256 MB memory-side cache (median, p10,
+    p90), then K steps stage by stage with events between the entry points.
+    full: also the roofline object and the widened rows."""
+    import torch
+    from sparse_moe_layer_amd.tensors import structs
+    from synthetic import make_problem
+
+    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    prob = make_problem(cfg, args.seed, device=dev)
+    T, H, E, k, I, Is = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared
+    R = T * k
+    adt = prob.x.dtype
+    sh = Is > 0
+    P, W = structs(prob, flags)
+    ws = lib.workspace(P)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    sl = torch.empty(T, dtype=torch.float32, device=dev) if sh else None
+    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sa = torch.empty(R, dtype=torch.int32, device=dev)
+    pos = torch.empty(R, dtype=torch.int32, device=dev)
+    h = torch.empty((R, I), dtype=adt, device=dev)
+    h_sh = torch.empty((T, Is), dtype=adt, device=dev) if sh else None
+    y = torch.empty((R, H), dtype=adt, device=dev)
+    y_sh = torch.empty((T, H), dtype=adt, device=dev) if sh else None
+    out = torch.empty((T, H), dtype=adt, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def layer():
+        lib.moe_layer_forward(P, W, prob.x, out, None, None, ws, stream)
+
+    def step(ev):
+        ev[0].record(stream)
+        lib.moe_route(P, prob.x, prob.w_router, prob.sh_gate_w, ids, tw, sl, ws, stream)
+        ev[1].record(stream)
+        lib.moe_dispatch(P, ids, offs, sa, pos, ws, stream)
+        ev[2].record(stream)
+        lib.moe_expert_gate_up(P, W, prob.x, offs, sa, h, h_sh, ws, stream)
+        ev[3].record(stream)
+        lib.moe_expert_down(P, W, offs, h, h_sh, y, y_sh, ws, stream)
+        ev[4].record(stream)
+        lib.moe_combine(P, y, pos, tw, y_sh, sl, out, stream)
+        ev[5].record(stream)
+
+    # the contract's timed region: K whole-layer calls back to back
+    for _ in range(args.warmup):
+        layer()
+    torch.cuda.synchronize()
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            layer()
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # each step alone after evicting the caches, HIP events around the call
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        flush.fill_(i & 255)
+        evs[i][0].record(stream)
+        layer()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    cold = [a.elapsed_time(b) for a, b in evs]
+
+    # stage by stage, events between the entry points
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for _ in range(max(1, args.warmup)):
+        step(mk())
+    torch.cuda.synchronize()
+    sevs = [mk() for _ in range(args.steps)]
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        step(sevs[i])
+    torch.cuda.synchronize()
+    staged_ms = (time.perf_counter() - t2) * 1e3 / args.steps
+    names = ["route", "dispatch", "gate_up", "down", "combine"]
+    stage_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in sevs) / args.steps for j, n in enumerate(names)}
+
+    counts = torch.diff(offs).cpu()
+    touched = int((counts > 0).sum())
+    work = acc.layer_work(T, H, E, k, I, Is, cfg.act, cfg.wdt, touched, cfg.scale_block)
+    mfma_peak = acc.PEAK_BF16_TFLOPS  # every contraction runs on bf16 MFMA (fp8 weights are decoded to bf16)
+    t_roof = max(work.flops / (mfma_peak * 1e12), work.bytes / (acc.PEAK_HBM_GBPS * 1e9))
+    t_s = ms_step * 1e-3
+    res = {
+        "ms_per_step": round(ms_step, 4),
+        "tokens_per_s": round(T / t_s, 1),
+        "cold_ms": {"median": round(pct(cold, 0.5), 4), "p10": round(pct(cold, 0.1), 4),
+                    "p90": round(pct(cold, 0.9), 4)},
+        "config": {"workload": cfg.name, "T": T, "H": H, "E": E, "k": k, "I": I, "I_shared": Is,
+                   "act": cfg.act, "weights": cfg.wdt, "touched_experts": touched,
+                   "max_tokens_per_expert": int(counts.max())},
+        "layer": {"tflops": round(work.flops / t_s / 1e12, 2), "hbm_gbps": round(work.bytes / t_s / 1e9, 1),
+                  "mfma_frac": round(work.flops / t_s / 1e12 / mfma_peak, 4),
+                  "hbm_frac": round(work.bytes / t_s / 1e9 / acc.PEAK_HBM_GBPS, 4),
+                  # the whole layer against its binding roof: t_roof = max(F/P, B/BW)
+                  "bound": "mfma" if work.flops / (mfma_peak * 1e12) >= work.bytes / (acc.PEAK_HBM_GBPS * 1e9)
+                           else "hbm",
+                  "t_roof_ms": round(t_roof * 1e3, 4),
+                  "roof_frac": round(t_roof / t_s, 4),
+                  "roof_frac_cold_median": round(t_roof / (pct(cold, 0.5) * 1e-3), 4),
+                  "staged_ms": round(staged_ms, 4)},
+        "stages_ms": {n: round(v, 4) for n, v in stage_ms.items()},
+        "sclk": clk.summary(),
+    }
+    if not full:
+        del prob
+        return res, None
+
+    # dominant kernel: the longer grouped GEMM phase; its bound from its intensity vs the ridge
+    dom = "gate_up" if stage_ms["gate_up"] >= stage_ms["down"] else "down"
+    f_dom = work.flops_gate_up if dom == "gate_up" else work.flops_down
+    b_dom = work.bytes_gate_up if dom == "gate_up" else work.bytes_down
+    t_dom = stage_ms[dom] * 1e-3
+    ridge = mfma_peak * 1e12 / (acc.PEAK_HBM_GBPS * 1e9)
+    if f_dom / b_dom > ridge:
+        ach, peak, unit, bound = f_dom / t_dom / 1e12, mfma_peak, "TFLOP/s", "mfma"
+    else:
+        ach, peak, unit, bound = b_dom / t_dom / 1e9, acc.PEAK_HBM_GBPS, "GB/s", "hbm"
+    kname = "grouped_gemm_" + dom
+    res["roofline"] = {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                       "frac": round(ach / peak, 4), "traffic": load_traffic(cfg.name, kname), "kernel": kname,
+                       "algorithmic": {"flops": f_dom, "bytes": b_dom}}
+    if not args.layer_only:
+        res["gated_residual"] = (gated_residual(lib, acc, args, cfg, dev, stream, (P, y, pos, tw, y_sh, sl))
+                                 if cfg.act == "bf16" else None)
+        res["weight_audit"] = weight_audit(lib, acc, args, prob, stream) if cfg.wdt == "bf16" else None
+    if args.ep_share:
+        res["ep_share"] = ep_share(lib, acc, args, cfg, dev, stream, prob, offs, sa)
+    return res, prob
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -293,135 +535,64 @@ def main():
 
     import sparse_moe_layer_amd as lib
     from sparse_moe_layer_amd import accounting as acc
-    from sparse_moe_layer_amd.tensors import structs
-    from synthetic import CONFIGS, make_problem
+    from synthetic import CONFIGS
 
-    cfg = CONFIGS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    print(f"[bench] generating {cfg.name} on {torch.cuda.get_device_name(dev)}", file=sys.stderr, flush=True)
-    prob = make_problem(cfg, args.seed, device=dev)
-    T, H, E, k, I, Is = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared
-    R = T * k
-    adt = prob.x.dtype
-    sh = Is > 0
+    print(f"[bench] {torch.cuda.get_device_name(dev)}", file=sys.stderr, flush=True)
     flags = {"auto": 0, "128": lib.MOE_FLAG_GEMM_TILE_128, "256": lib.MOE_FLAG_GEMM_TILE_256}[args.gemm_tile]
     flags |= {"auto": 0, "gemm": lib.MOE_FLAG_FORCE_GEMM, "stream": lib.MOE_FLAG_FORCE_STREAM}[args.path]
-    P, W = structs(prob, flags)
-    ws = lib.workspace(P)
-    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
-    sl = torch.empty(T, dtype=torch.float32, device=dev) if sh else None
-    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    sa = torch.empty(R, dtype=torch.int32, device=dev)
-    pos = torch.empty(R, dtype=torch.int32, device=dev)
-    h = torch.empty((R, I), dtype=adt, device=dev)
-    h_sh = torch.empty((T, Is), dtype=adt, device=dev) if sh else None
-    y = torch.empty((R, H), dtype=adt, device=dev)
-    y_sh = torch.empty((T, H), dtype=adt, device=dev) if sh else None
-    out = torch.empty((T, H), dtype=adt, device=dev)
     stream = torch.cuda.current_stream()
+    cfg = CONFIGS[args.workload]
+    main_res, prob = measure(lib, acc, cfg, args, dev, stream, flags, full=True)
 
-    def step(ev):
-        ev[0].record(stream)
-        lib.moe_route(P, prob.x, prob.w_router, prob.sh_gate_w, ids, tw, sl, ws, stream)
-        ev[1].record(stream)
-        lib.moe_dispatch(P, ids, offs, sa, pos, ws, stream)
-        ev[2].record(stream)
-        lib.moe_expert_gate_up(P, W, prob.x, offs, sa, h, h_sh, ws, stream)
-        ev[3].record(stream)
-        lib.moe_expert_down(P, W, offs, h, h_sh, y, y_sh, ws, stream)
-        ev[4].record(stream)
-        lib.moe_combine(P, y, pos, tw, y_sh, sl, out, stream)
-        ev[5].record(stream)
-
-    # the timed steps: the whole layer, one moe_layer_forward call per step
-    for _ in range(args.warmup):
-        lib.moe_layer_forward(P, W, prob.x, out, None, None, ws, stream)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        lib.moe_layer_forward(P, W, prob.x, out, None, None, ws, stream)
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-
-    # the same layer stage by stage, HIP events on the launch stream between the
-    # entry points: per-stage durations for the roofline of the dominant kernel
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-    for _ in range(max(1, args.warmup)):
-        step(mk())
-    torch.cuda.synchronize()
-    evs = [mk() for _ in range(args.steps)]
-    t2 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    staged_ms = (time.perf_counter() - t2) * 1e3 / args.steps
-    names = ["route", "dispatch", "gate_up", "down", "combine"]
-    stage_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, n in enumerate(names)}
-
-    counts = torch.diff(offs).cpu()
-    touched = int((counts > 0).sum())
-    work = acc.layer_work(T, H, E, k, I, Is, cfg.act, cfg.wdt, touched, cfg.scale_block)
-    mfma_peak = acc.PEAK_BF16_TFLOPS  # every contraction runs on bf16 MFMA (fp8 weights are decoded to bf16)
-
-    # dominant kernel: the longer grouped GEMM phase; its bound from its intensity vs the ridge
-    dom = "gate_up" if stage_ms["gate_up"] >= stage_ms["down"] else "down"
-    f_dom = work.flops_gate_up if dom == "gate_up" else work.flops_down
-    b_dom = work.bytes_gate_up if dom == "gate_up" else work.bytes_down
-    t_dom = stage_ms[dom] * 1e-3
-    ridge = mfma_peak * 1e12 / (acc.PEAK_HBM_GBPS * 1e9)
-    if f_dom / b_dom > ridge:
-        ach, peak, unit, bound = f_dom / t_dom / 1e12, mfma_peak, "TFLOP/s", "mfma"
-    else:
-        ach, peak, unit, bound = b_dom / t_dom / 1e9, acc.PEAK_HBM_GBPS, "GB/s", "hbm"
-    kname = "grouped_gemm_" + dom
-    roof = {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
-            "traffic": load_traffic(args.workload, kname), "kernel": kname,
-            "algorithmic": {"flops": f_dom, "bytes": b_dom}}
-
-    gr = (gated_residual(lib, acc, args, cfg, dev, stream, (P, y, pos, tw, y_sh, sl))
-          if cfg.act == "bf16" else None)
-    audit = weight_audit(lib, acc, args, prob, stream) if cfg.wdt == "bf16" else None
-    ep = None if args.no_ep_share else ep_share(lib, acc, args, cfg, dev, stream, prob, offs, sa)
-
-    t_s = ms_step * 1e-3
+    git_sha, src_sha = source_ids()
     res = {
         "metric": METRIC,
-        "value": round(T / t_s, 1),
+        "value": main_res["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": main_res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if cfg.act == "bf16" else "f32",
         "data": "synthetic (seeded counter-based generator, weights random-init at the pages' shapes)",
-        "config": {"workload": cfg.name, "T": T, "H": H, "E": E, "k": k, "I": I, "I_shared": Is,
-                   "act": cfg.act, "weights": cfg.wdt, "touched_experts": touched,
-                   "max_tokens_per_expert": int(counts.max()), "gemm_tile": args.gemm_tile, "path": args.path},
-        "layer": {"tflops": round(work.flops / t_s / 1e12, 2), "hbm_gbps": round(work.bytes / t_s / 1e9, 1),
-                  "mfma_frac": round(work.flops / t_s / 1e12 / mfma_peak, 4),
-                  "hbm_frac": round(work.bytes / t_s / 1e9 / acc.PEAK_HBM_GBPS, 4),
-                  # the whole layer against its binding roof: t_roof = max(F/P, B/BW)
-                  "bound": "mfma" if work.flops / (mfma_peak * 1e12) >= work.bytes / (acc.PEAK_HBM_GBPS * 1e9)
-                           else "hbm",
-                  "roof_frac": round(max(work.flops / (mfma_peak * 1e12), work.bytes / (acc.PEAK_HBM_GBPS * 1e9))
-                                     / t_s, 4),
-                  "staged_ms": round(staged_ms, 4)},
-        "stages_ms": {n: round(v, 4) for n, v in stage_ms.items()},
-        "roofline": roof,
-        "gated_residual": gr,
-        "weight_audit": audit,
-        "ep_share": ep,
+        "config": dict(main_res["config"], gemm_tile=args.gemm_tile, path=args.path),
+        "cold_ms": main_res["cold_ms"],
+        "layer": main_res["layer"],
+        "stages_ms": main_res["stages_ms"],
+        "roofline": main_res["roofline"],
+        "sclk": main_res["sclk"],
+        "git_sha": git_sha,
+        "source_sha": src_sha,
     }
+    for key in ("gated_residual", "weight_audit", "ep_share"):
+        if key in main_res:
+            res[key] = main_res[key]
     if args.cpu_tokens != 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(prob, args.cpu_tokens)
     else:
         res["cpu_baseline"] = None
+    del prob
+    torch.cuda.empty_cache()
+    # the other workloads, each in the same run, with its own layer-level numbers
+    others = {}
+    for name in [w for w in args.also.split(",") if w and w != args.workload]:
+        r, _ = measure(lib, acc, CONFIGS[name], args, dev, stream, flags, full=False)
+        others[name] = r
+        torch.cuda.empty_cache()
+    if "flash_decode" in others:
+        d = others["flash_decode"]
+        res["decode"] = {"workload": "flash_decode", "ms": d["ms_per_step"], "tokens_per_s": d["tokens_per_s"],
+                         "cold_ms": d["cold_ms"], "hbm_frac": d["layer"]["hbm_frac"],
+                         "hbm_frac_cold_median": d["layer"]["roof_frac_cold_median"],
+                         "target_ms": round(d["layer"]["t_roof_ms"] / 0.7, 4), "stages_ms": d["stages_ms"]}
+    if others:
+        res["workloads"] = others
     print(json.dumps(res), flush=True)
 
 
