@@ -215,13 +215,11 @@ FfnArgs ffn_args(const moe_problem* p, const moe_weights* w, const void* x, cons
   return a;
 }
 
-// MFMA GEMM kernel of the grouped GEMM path: the pipelined direct-load
-// kernel with 256-row tiles once experts average 128 rows or more (the MFMA
-// rate bounds them; a group's last m-tile of at most 128 rows then goes to
-// the 128-row kernel), else the register-staged kernel with 128-row tiles
-// (about a hundred rows per expert: weight streaming bounds them).  The
-// 256-row kernel takes bf16 weights with H, I and I_shared multiples of 32.
-// The caller can pin either kernel for A/B runs.
+// Grouped GEMM path: the persistent direct-load kernel with 256-row tiles
+// once experts average 128 rows or more (the MFMA rate bounds them), else
+// the register-staged kernel with 128-row tiles (about a hundred rows per
+// expert: weight streaming bounds them).  The 256-row tiles take H, I and
+// I_shared multiples of 32.  The caller can pin either tiling for A/B runs.
 bool use_big_tiles(const moe_problem* p, const FfnArgs& a) {
   if (!moe::ffn_dma_supported(a)) return false;
   if (p->flags & MOE_FLAG_GEMM_TILE_128) return false;
@@ -238,11 +236,15 @@ moe_status run_ffn(const moe_problem* p, FfnArgs& a, int phases, void* plan_ws, 
   if (p->act_dtype == MOE_F32) return hip_status(moe::launch_ffn_f32(a, phases, s));
   int32_t* plan = static_cast<int32_t*>(plan_ws);
   const bool big = use_big_tiles(p, a);
-  // A group holds at most T rows, so with T <= kStreamMaxRows no group can
+  // Groups of at most kStreamMaxRows rows stream their weights after the
+  // tiles.  (As ragged 256-row tiles they measured slower: the 2.4T fp8
+  // layer 4.26 against 3.75 ms per step.)
+  const int stream_rows = moe::kStreamMaxRows;
+  // A group holds at most T rows, so with T <= stream_rows no group can
   // reach the GEMM path unless it is forced; with the GEMM path forced no
   // group streams.  Launches that cannot have work are skipped.
   const bool any_gemm = (p->flags & MOE_FLAG_FORCE_GEMM) ||
-                        (!(p->flags & MOE_FLAG_FORCE_STREAM) && p->T > moe::kStreamMaxRows);
+                        (!(p->flags & MOE_FLAG_FORCE_STREAM) && p->T > stream_rows);
   const bool any_stream = !(p->flags & MOE_FLAG_FORCE_GEMM);
   // Every group streaming as one m-block (T <= kStreamMaxRows): the
   // streaming kernels list the groups themselves, with no plan kernel ahead
@@ -250,18 +252,15 @@ moe_status run_ffn(const moe_problem* p, FfnArgs& a, int phases, void* plan_ws, 
   const bool self_plan = !any_gemm && p->T <= moe::kStreamMaxRows;
   if (!self_plan) {
     if (moe::launch_ffn_plan(a.offsets, a.sorted, a.T, a.E, a.k, a.Is > 0 ? 1 : 0, p->flags,
-                             big ? moe::kGemmBigBM : moe::kGemmBM, plan, s) != hipSuccess)
+                             big ? moe::kGemmBigBM : moe::kGemmBM, stream_rows, plan, s) != hipSuccess)
       return MOE_ERR_HIP;
     moe::ffn_bind_plan(a, plan);
   }
   for (int phase = 1; phase <= 2; ++phase) {
     if (!(phases & phase)) continue;
     if (any_gemm) {
-      // 256-row tiles, then the groups' remainders of at most 128 rows in 128-row tiles
-      const hipError_t e = big ? moe::launch_ffn_gemm_dma(a, phase, s) : moe::launch_ffn_gemm(a, phase, s);
+      const hipError_t e = big ? moe::launch_ffn_gemm_big(a, phase, s) : moe::launch_ffn_gemm(a, phase, s);
       if (e != hipSuccess) return MOE_ERR_HIP;
-      if (big && moe::launch_ffn_gemm(a, phase, s, moe::kPlanTiles2Begin, moe::kPlanTiles2End) != hipSuccess)
-        return MOE_ERR_HIP;
     }
     if (any_stream && moe::launch_ffn_stream(a, phase, s, self_plan) != hipSuccess) return MOE_ERR_HIP;
   }

@@ -148,7 +148,7 @@ __global__ __launch_bounds__(NT, BKT == 32 ? 3 : 2) void gemm_kernel(FfnArgs f, 
         a_ptr[i] = ra.x + (int64_t)gr * ra.H;
       } else if (MODE == M_GATEUP) {
         int tok = shared ? gr : f.sorted[gr] / f.k;
-        tok = tok < f.T ? tok : f.T - 1;
+        tok = (unsigned)tok < (unsigned)f.T ? tok : f.T - 1;  // also clamps a negative index
         a_ptr[i] = reinterpret_cast<const bf16*>(f.x) + (int64_t)tok * f.H;
       } else {
         a_ptr[i] = shared ? reinterpret_cast<const bf16*>(f.h_sh) + (int64_t)gr * f.Is
@@ -469,14 +469,12 @@ __device__ int block_excl_scan(int v, int* tmp, int* total) {
 }
 
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* offsets, const int32_t* sorted, int T, int E,
-                                                    int k, int has_shared, uint32_t flags, int bm, int32_t* plan,
-                                                    int max_mt, int max_sb) {
+                                                    int k, int has_shared, uint32_t flags, int bm, int stream_rows,
+                                                    int32_t* plan, int max_mt, int max_sb) {
   __shared__ int tmp[32];
   __shared__ int tot;
-  // with 256-row tiles a group's last m-tile of at most 128 rows goes to a
-  // second list, run by the 128-row kernel: a ragged remainder costs that
-  // kernel about two thirds of what a 256-row tile of it costs
-  const bool two_lists = bm > kGemmBM;
+  // the fused kernels' claim counters start at zero
+  for (int i = threadIdx.x; i < kPlanHeader - kPlanCounters; i += blockDim.x) plan[kPlanCounters + i] = 0;
   int32_t* mt_group = plan + kPlanHeader;
   int32_t* mt_row0 = mt_group + max_mt;
   int32_t* sb_group = mt_row0 + max_mt;
@@ -495,10 +493,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* offsets, cons
     if (n > 0) {
       if (flags & 1u) gemm = true;            // force GEMM
       else if (flags & 2u) gemm = false;      // force streaming
-      else gemm = n > kStreamMaxRows;
+      else gemm = n > stream_rows;
     }
-    const int rem = n % bm;
-    const int cm = !gemm ? 0 : two_lists ? n / bm + (rem > kGemmBM ? 1 : 0) : (n + bm - 1) / bm;
+    const int cm = gemm ? (n + bm - 1) / bm : 0;
     const int cs = (n > 0 && !gemm) ? (n + kStreamBM - 1) / kStreamBM : 0;
     // routed groups first in each list, the shared group (g == E) last: since
     // g ascends with the scan order, this holds automatically.
@@ -519,7 +516,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* offsets, cons
         int tok = 0;
         if (m < nr) {  // sorted is null for the down phase alone, which needs no tokens
           tok = g < E ? (sorted ? sorted[gbase + r0 + m] / k : 0) : r0 + m;
-          tok = tok < T ? tok : T - 1;
+          tok = (unsigned)tok < (unsigned)T ? tok : T - 1;
         }
         sb_tok[sb * kStreamBM + m] = tok;
       }
@@ -531,26 +528,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* offsets, cons
     carry_mt += tm;
     carry_sb += ts;
   }
-  // second list (two_lists only): [plan[4], plan[5]) after the first
-  int carry_small = carry_mt;
-  for (int g0 = 0; two_lists && g0 < G; g0 += 1024) {
-    const int g = g0 + threadIdx.x;
-    int n = 0;
-    if (g < E) n = offsets[g + 1] - offsets[g];
-    else if (g < G) n = T;
-    const bool gemm = n > 0 && ((flags & 1u) || (!(flags & 2u) && n > kStreamMaxRows));
-    const int rem = n % bm;
-    const int cr = gemm && rem > 0 && rem <= kGemmBM ? 1 : 0;
-    const int o = block_excl_scan(cr, tmp, &tot) + carry_small;
-    if (cr) { mt_group[o] = g; mt_row0[o] = n - rem; }
-    carry_small += tot;
-  }
   if (threadIdx.x == 0) {
     plan[0] = carry_mt;
     plan[1] = carry_sb;
     if (!has_shared) { plan[2] = carry_mt; plan[3] = carry_sb; }
-    plan[4] = carry_mt;
-    plan[5] = carry_small;
   }
 }
 
@@ -593,10 +574,10 @@ void ffn_bind_plan(FfnArgs& a, int32_t* plan) {
 }
 
 hipError_t launch_ffn_plan(const int32_t* offsets, const int32_t* sorted, int T, int E, int k, int has_shared,
-                           uint32_t flags, int bm, int32_t* plan, hipStream_t s) {
+                           uint32_t flags, int bm, int stream_rows, int32_t* plan, hipStream_t s) {
   // list capacity is sized for the smallest tile height (kGemmBM <= bm)
   const int mm = max_mtiles(T, E, k, has_shared), ms = max_sblocks(T, E, k, has_shared);
-  plan_kernel<<<1, 1024, 0, s>>>(offsets, sorted, T, E, k, has_shared, flags, bm, plan, mm, ms);
+  plan_kernel<<<1, 1024, 0, s>>>(offsets, sorted, T, E, k, has_shared, flags, bm, stream_rows, plan, mm, ms);
   return hipGetLastError();
 }
 
@@ -631,7 +612,7 @@ hipError_t launch_router_logits_bf16(const void* x, const void* w_router, const 
 }
 
 // Tiled MFMA phase of the expert FFN (phase 1: gate/up + SiLU*mul, 2: down).
-hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s, int list_begin_idx, int list_end_idx) {
+hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s) {
   const bool sh = a.Is > 0;
   const int mm = max_mtiles(a.T, a.E, a.k, sh);
   const int wide = a.I > a.Is ? a.I : a.Is;
@@ -639,11 +620,7 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s, int list_
   const int64_t tiles = (int64_t)mm * ntn;
   const int grid = (int)(tiles < num_cus() * 2 ? (tiles + 7) / 8 * 8 : num_cus() * 2);
   RouterArgs none{};
-  if (a.fp8 && list_begin_idx >= 0) {
-    // an explicit list (128-row remainders): fp8 and shared bf16 tiles mixed
-    if (phase == 1) gemm_kernel<M_GATEUP, true><<<grid, NT, 0, s>>>(a, none, ntn, list_begin_idx, list_end_idx);
-    else gemm_kernel<M_DOWN, true><<<grid, NT, 0, s>>>(a, none, ntn, list_begin_idx, list_end_idx);
-  } else if (a.fp8) {
+  if (a.fp8) {
     // routed tiles [0, plan[2]) decode fp8; the shared expert stays bf16
     if (phase == 1) gemm_kernel<M_GATEUP, true><<<grid, NT, 0, s>>>(a, none, ntn, kPlanStart, kPlanRoutedTiles);
     else gemm_kernel<M_DOWN, true><<<grid, NT, 0, s>>>(a, none, ntn, kPlanStart, kPlanRoutedTiles);
@@ -655,8 +632,8 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s, int list_
     constexpr int per_cu = kBf16FfnBK == 32 ? 3 : 2;
     const int g3 = (int)(tiles < num_cus() * per_cu ? (tiles + 7) / 8 * 8 : num_cus() * per_cu);
     if (phase == 1)
-      gemm_kernel<M_GATEUP, false, 0, kBf16FfnBK><<<g3, NT, 0, s>>>(a, none, ntn, list_begin_idx, list_end_idx);
-    else gemm_kernel<M_DOWN, false, 0, kBf16FfnBK><<<g3, NT, 0, s>>>(a, none, ntn, list_begin_idx, list_end_idx);
+      gemm_kernel<M_GATEUP, false, 0, kBf16FfnBK><<<g3, NT, 0, s>>>(a, none, ntn, kPlanStart, kPlanTiles);
+    else gemm_kernel<M_DOWN, false, 0, kBf16FfnBK><<<g3, NT, 0, s>>>(a, none, ntn, kPlanStart, kPlanTiles);
   }
   return hipGetLastError();
 }

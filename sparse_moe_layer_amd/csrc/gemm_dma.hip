@@ -295,10 +295,224 @@ __device__ __forceinline__ void mainloop_r(f32x16 (&acc)[C::MI][C::NJ], bf16* co
   else mainloop<C, NB, 5 % C::S>(acc, stg, abase, aoff, bbase, boff, nk, wave, o, sc0, sc1);
 }
 
-// m-tiles [plan[begin], plan[end]) of the plan's first list (begin < 0: from 0)
+// One 256 x 256 output tile: m-tile mt (a list entry of the plan: group and
+// first row) x n-tile nt.  stg: the S stage buffers; ssc: fp8 scale table.
+// A tile with fewer rows than BM computes only its M-blocks (a wave with none
+// computes block wm on rows it never stores), and its A loads of 16-row
+// groups past the last row read one 16-byte chunk for all lanes (those LDS
+// rows are never stored).
 template <class C, int MODE>
-__global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArgs f, int n_tiles_n, int super,
-                                                                          int list_begin_idx, int list_end_idx) {
+__device__ __forceinline__ void run_tile(const FfnArgs& f, int mt, int nt, bf16* const* stg, float* ssc, int tid,
+                                         int lane, int wave, const FragOff& fo) {
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int g = f.mt_group[mt];
+  const int r0 = f.mt_row0[mt];
+  const bool shared = g >= f.E;
+  int base = 0, nrows;
+  if (!shared) {
+    base = f.offsets[g];
+    nrows = f.offsets[g + 1] - base - r0;
+  } else {
+    nrows = f.T - r0;
+  }
+  nrows = nrows < C::BM ? nrows : C::BM;
+  const int K = MODE == 1 ? f.H : (shared ? f.Is : f.I);
+  const int Ncols = MODE == 1 ? (shared ? f.Is : f.I) : f.H;
+  const int ncov = MODE == 1 ? C::BN / 2 : C::BN;
+  if (nt * ncov >= Ncols) return;
+
+  // ---- sources of the direct loads of each K step ----
+  // load i of wave w fills rows (NW*i + w)*RPL .. +RPL of its part; lane l
+  // lands at row +l/(BK/8), position l%(BK/8), so it fetches the global
+  // chunk that belongs there: position ^ swz(row).  Bases are wave-uniform
+  // (SGPRs); lanes carry 32-bit element offsets.
+  constexpr int LPR = C::BK / 8;  // lanes per row
+  const int lrow = lane / LPR;
+  const int lpos = lane % LPR;
+  const bf16* abase;
+  if (MODE == 1) abase = reinterpret_cast<const bf16*>(f.x);
+  else abase = shared ? reinterpret_cast<const bf16*>(f.h_sh) : reinterpret_cast<const bf16*>(f.h);
+  uint32_t aoff[C::LA], boff[C::LB];
+  const bf16* bbase[C::LB];
+#pragma unroll
+  for (int i = 0; i < C::LA; ++i) {
+    const int row = (C::NW * i + wave) * C::RPL + lrow;
+    // a load whose rows all lie past the tile's: every lane reads the same
+    // 16 bytes (one cache line request instead of sixteen; the loads stay
+    // unconditional, so the compiler's wait counts stay exact)
+    const bool dead = (C::NW * i + wave) * C::RPL >= nrows;
+    const int gchunk = dead ? 0 : lpos ^ swz<C::BK>(row);
+    const int rr = dead ? nrows - 1 : (row < nrows ? row : nrows - 1);
+    const int gr = base + r0 + rr;
+    if (MODE == 1) {
+      int tok = shared ? gr : f.sorted[gr] / f.k;
+      tok = (unsigned)tok < (unsigned)f.T ? tok : f.T - 1;  // also clamps a negative index
+      aoff[i] = (uint32_t)tok * (uint32_t)f.H + gchunk * 8;
+    } else {
+      aoff[i] = (uint32_t)gr * (uint32_t)K + gchunk * 8;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < C::LB; ++i) {
+    if constexpr (C::F8) {
+      // load i of wave w fills B rows (NW*i + w)*32 .. +32 as [chunk][row]:
+      // lane l takes row +l%32, 16-byte chunk l/32 of the 32-code K slice
+      const int grow0 = (C::NW * i + wave) * C::RPL8;
+      const int n = grow0 + (lane & 31);
+      const int ch = lane >> 5;
+      int col;
+      const uint8_t* mat;
+      if (MODE == 1) {
+        const bool up = (grow0 % C::CW) >= C::CW / 2;
+        col = nt * (C::BN / 2) + (n / C::CW) * (C::CW / 2) + (n % (C::CW / 2));
+        mat = reinterpret_cast<const uint8_t*>(up ? f.wu : f.wg) + (int64_t)g * (up ? f.su : f.sg);
+      } else {
+        col = nt * C::BN + n;
+        mat = reinterpret_cast<const uint8_t*>(f.wd) + (int64_t)g * f.sd;
+      }
+      col = col < Ncols ? col : Ncols - 1;
+      bbase[i] = reinterpret_cast<const bf16*>(mat);
+      boff[i] = (uint32_t)col * (uint32_t)K + ch * 16;
+    } else {
+      const int grow0 = (C::NW * i + wave) * C::RPL;  // wave-uniform first row of the load
+      const int n = grow0 + lrow;                       // B tile row
+      const int gchunk = lpos ^ swz<C::BK>(n);
+      int col;
+      if (MODE == 1) {
+        // wave column wc (CW rows) holds CW/2 gate rows, then the up rows of
+        // the same CW/2 hidden columns
+        const bool up = (grow0 % C::CW) >= C::CW / 2;
+        col = nt * (C::BN / 2) + (n / C::CW) * (C::CW / 2) + (n % (C::CW / 2));
+        bbase[i] = shared ? reinterpret_cast<const bf16*>(up ? f.shu : f.shg)
+                          : reinterpret_cast<const bf16*>(up ? f.wu : f.wg) + (int64_t)g * (up ? f.su : f.sg);
+      } else {
+        col = nt * C::BN + n;
+        bbase[i] = shared ? reinterpret_cast<const bf16*>(f.shd) : reinterpret_cast<const bf16*>(f.wd) + (int64_t)g * f.sd;
+      }
+      col = col < Ncols ? col : Ncols - 1;
+      boff[i] = (uint32_t)col * (uint32_t)K + gchunk * 8;
+    }
+  }
+
+  // fp8: the tile's block scales, K block kb of row sel at ssc[sel*nkb + kb]
+  // (gate/up: sel 0 gate, 1 up, of hidden block nt; down: W_down row
+  // blocks 2nt and 2nt+1, the second clamped at the last)
+  const float* sc0 = nullptr;
+  const float* sc1 = nullptr;
+  if constexpr (C::F8) {
+    const int nkb = K / 128;
+    for (int t = tid; t < 2 * nkb; t += C::NT) {
+      const int sel = t / nkb, kb = t - sel * nkb;
+      float v;
+      if (MODE == 1) {
+        v = (sel ? f.scu : f.scg)[((int64_t)g * (f.I / 128) + nt) * nkb + kb];
+      } else {
+        int rb = 2 * nt + sel;
+        rb = rb < f.H / 128 ? rb : f.H / 128 - 1;
+        v = f.scd[((int64_t)g * (f.H / 128) + rb) * nkb + kb];
+      }
+      ssc[t] = v;
+    }
+    if (MODE == 1) {
+      sc0 = ssc;
+      sc1 = ssc + nkb;
+    } else {
+      sc0 = sc1 = ssc + (wn * C::CW / 128) * nkb;
+    }
+  }
+
+  f32x16 acc[C::MI][C::NJ];
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  // M-blocks of 32 rows this wave computes (blocks wm, wm+WM, ... below nrows)
+  const int nblk_tile = (nrows + 31) / 32;
+  const int nb = (nblk_tile - wm + C::WM - 1) / C::WM;
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // previous tile's loads and stores settled
+  const int nk = K / C::BK;
+  if constexpr (C::MI >= 4) {
+    if (nb >= 4) mainloop_r<C, 4>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo, sc0, sc1);
+    else if (nb == 3) mainloop_r<C, 3>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo, sc0, sc1);
+    else if (nb == 2) mainloop_r<C, 2>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo, sc0, sc1);
+    else mainloop_r<C, 1>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo, sc0, sc1);
+  } else {
+    if (nb >= 2) mainloop_r<C, 2>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo, sc0, sc1);
+    else mainloop_r<C, 1>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo, sc0, sc1);
+  }
+
+  // ---- epilogue through LDS ----
+  // The tile leaves in M bands of WM*32 rows: band ii (M-blocks WM*ii ..
+  // WM*ii + WM-1) goes, as bf16 (gate/up: SiLU(g)*u), into the stage
+  // buffers (BPS bands each), then every thread stores whole 16-byte row
+  // chunks.  C lane layout of a
+  // 32x32 block: col = lane%32, row 8*(v/4) + 4*(lane/32) + v%4.  Chunk c of
+  // band row r sits at c ^ (4 * ((r >> 2) & 1)), so the two half-waves'
+  // rows (4 apart) write different banks.
+  constexpr int CCOLS = MODE == 1 ? C::BN / 2 : C::BN;  // output columns of the tile
+  constexpr int CPR = CCOLS / 8;                        // 16-byte chunks per row
+  constexpr int BAND = C::WM * 32;
+  constexpr int BPS = C::STAGE / (BAND * CCOLS);        // bands per stage buffer
+  static_assert(BPS >= 1 && C::MI <= C::S * BPS && CPR >= 8, "epilogue staging");
+  auto cpos = [&](int r, int col) { return r * CCOLS + ((((col >> 3) ^ (((r >> 2) & 1) << 2))) << 3) + (col & 7); };
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // trailing (redundant) direct loads have landed
+  block_sync();                              // every wave is done reading the stage buffers
+#pragma unroll
+  for (int ii = 0; ii < C::MI; ++ii) {
+    bf16* ct = stg[ii / BPS] + (ii % BPS) * BAND * CCOLS;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if constexpr (MODE == 1) {
+#pragma unroll
+        for (int jj = 0; jj < C::NJ / 2; ++jj)
+          ct[cpos(r, wn * (C::CW / 2) + jj * 32 + (lane & 31))] =
+              f2bf(silu(acc[ii][jj][v]) * acc[ii][jj + C::NJ / 2][v]);
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < C::NJ; ++jj) ct[cpos(r, wn * C::CW + jj * 32 + (lane & 31))] = f2bf(acc[ii][jj][v]);
+      }
+    }
+  }
+  block_sync();
+  bf16* obase;
+  int ld;
+  if (MODE == 1) {
+    obase = shared ? reinterpret_cast<bf16*>(f.h_sh) : reinterpret_cast<bf16*>(f.h);
+    ld = shared ? f.Is : f.I;
+  } else {
+    obase = shared ? reinterpret_cast<bf16*>(f.y_sh) : reinterpret_cast<bf16*>(f.y);
+    ld = f.H;
+  }
+#pragma unroll
+  for (int ii = 0; ii < C::MI; ++ii) {
+    const bf16* ct = stg[ii / BPS] + (ii % BPS) * BAND * CCOLS;
+    for (int q = tid; q < BAND * CPR; q += C::NT) {
+      const int r = q / CPR, c = q % CPR;
+      const int trow = ii * BAND + r;  // band ii holds tile rows ii*BAND ..
+      const int col = nt * CCOLS + c * 8;
+      if (trow < nrows && col < Ncols)
+        st16(obase + (int64_t)(base + r0 + trow) * ld + col, ld16(ct + cpos(r, c * 8)));
+    }
+  }
+}
+
+// The persistent phase kernel: the phase's GEMM tiles (m-tiles
+// [plan[tb], plan[te]) x n-tiles, ragged last m-tiles included), dealt to
+// XCDs in the static order of supertiles of `super` m-tiles x all n-tiles:
+// workgroup i runs on XCD i % 8, and XCD x takes tiles [x * chunk, (x+1) *
+// chunk) of every round of G tiles (chunk = G / 8), so the tiles it runs at
+// the same time share A and weight slices in its L2.  Its workgroups claim
+// those tiles in order through the XCD's counter, so a workgroup that drew a
+// ragged (cheaper) tile takes the next one sooner; a workgroup whose XCD has
+// run out moves on to the next XCD's counter.  counters: 8 ints, zero at
+// launch.
+template <class C, int MODE>
+__global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void ffn_tiles_kernel(FfnArgs f, int n_tiles_n, int super,
+                                                                           int tb, int te, int32_t* counters) {
   __shared__ __attribute__((aligned(1024))) bf16 s0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) bf16 s1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) bf16 s2[C::S > 2 ? C::STAGE : 8];
@@ -306,219 +520,54 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void dma_gemm_kernel(FfnArg
   __shared__ __attribute__((aligned(1024))) bf16 s4[C::S > 4 ? C::STAGE : 8];
   __shared__ __attribute__((aligned(1024))) bf16 s5[C::S > 5 ? C::STAGE : 8];
   __shared__ float ssc[C::F8 ? 256 : 1];  // fp8: two rows of K-block scales
+  __shared__ int claim[2];
+  // separate arrays: the compiler then knows that a fragment read from one
+  // buffer does not wait on the direct loads in flight into the others
   bf16* const stg[6] = {s0, s1, s2, s3, s4, s5};
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / C::WN, wn = wave % C::WN;
-  const FragOff fo = frag_offsets<C>(wm, wn, lane);
+  const FragOff fo = frag_offsets<C>(wave / C::WN, wave % C::WN, lane);
 
-  // m-tiles: routed groups, then the shared expert (fp8: routed ones only)
-  const int mt_first = list_begin_idx == kPlanStart ? 0 : f.plan[list_begin_idx];
-  const int MT = f.plan[list_end_idx] - mt_first;
+  const int mt_first = tb == kPlanStart ? 0 : f.plan[tb];
+  const int MT = f.plan[te] - mt_first;
   const int total = MT * n_tiles_n;
   const int G = gridDim.x;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int chunk = G >> 3;
+  auto xcd_tiles = [&](int x) {
+    return (total / G) * chunk + min(max(total % G - x * chunk, 0), chunk);
+  };
 
-  for (int it = 0;; ++it) {
-    const int t = it * G + xcd * (G >> 3) + slot;
-    if (t >= total) break;
+  int victim = blockIdx.x & 7;  // the XCD whose counter this workgroup claims from
+  int tried = 0;
+  for (;;) {
+    if (tid == 0) {
+      int xv = -1, c = 0;
+      while (tried < 8) {
+        const int tx = xcd_tiles(victim);
+        if (tx > 0) {
+          c = atomicAdd(&counters[victim], 1);
+          if (c < tx) {
+            xv = victim;
+            break;
+          }
+        }
+        victim = (victim + 1) & 7;
+        ++tried;
+      }
+      claim[0] = xv;
+      claim[1] = c;
+    }
+    __syncthreads();
+    const int xv = claim[0], c = claim[1];
+    __syncthreads();  // claim[] may be rewritten for the next tile
+    if (xv < 0) break;
+    const int t = (c / chunk) * G + xv * chunk + c % chunk;
     // supertile order: `super` m-tiles x all n-tiles, m fastest
     const int sbase = (t / (super * n_tiles_n)) * super;
     const int grp = MT - sbase < super ? MT - sbase : super;
     const int r = t - sbase * n_tiles_n;
-    const int nt = r / grp;
-    const int mt = mt_first + sbase + r % grp;
-
-    const int g = f.mt_group[mt];
-    const int r0 = f.mt_row0[mt];
-    const bool shared = g >= f.E;
-    int base = 0, nrows;
-    if (!shared) {
-      base = f.offsets[g];
-      nrows = f.offsets[g + 1] - base - r0;
-    } else {
-      nrows = f.T - r0;
-    }
-    nrows = nrows < C::BM ? nrows : C::BM;
-    const int K = MODE == 1 ? f.H : (shared ? f.Is : f.I);
-    const int Ncols = MODE == 1 ? (shared ? f.Is : f.I) : f.H;
-    const int ncov = MODE == 1 ? C::BN / 2 : C::BN;
-    if (nt * ncov >= Ncols) continue;
-
-    // ---- sources of the direct loads of each K step ----
-    // load i of wave w fills rows (NW*i + w)*RPL .. +RPL of its part; lane l
-    // lands at row +l/(BK/8), position l%(BK/8), so it fetches the global
-    // chunk that belongs there: position ^ swz(row).  Bases are wave-uniform
-    // (SGPRs); lanes carry 32-bit element offsets.
-    constexpr int LPR = C::BK / 8;  // lanes per row
-    const int lrow = lane / LPR;
-    const int lpos = lane % LPR;
-    const bf16* abase;
-    if (MODE == 1) abase = reinterpret_cast<const bf16*>(f.x);
-    else abase = shared ? reinterpret_cast<const bf16*>(f.h_sh) : reinterpret_cast<const bf16*>(f.h);
-    uint32_t aoff[C::LA], boff[C::LB];
-    const bf16* bbase[C::LB];
-#pragma unroll
-    for (int i = 0; i < C::LA; ++i) {
-      const int row = (C::NW * i + wave) * C::RPL + lrow;
-      const int gchunk = lpos ^ swz<C::BK>(row);
-      const int rr = row < nrows ? row : nrows - 1;
-      const int gr = base + r0 + rr;
-      if (MODE == 1) {
-        int tok = shared ? gr : f.sorted[gr] / f.k;
-        tok = tok < f.T ? tok : f.T - 1;
-        aoff[i] = (uint32_t)tok * (uint32_t)f.H + gchunk * 8;
-      } else {
-        aoff[i] = (uint32_t)gr * (uint32_t)K + gchunk * 8;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::LB; ++i) {
-      if constexpr (C::F8) {
-        // load i of wave w fills B rows (NW*i + w)*32 .. +32 as [chunk][row]:
-        // lane l takes row +l%32, 16-byte chunk l/32 of the 32-code K slice
-        const int grow0 = (C::NW * i + wave) * C::RPL8;
-        const int n = grow0 + (lane & 31);
-        const int ch = lane >> 5;
-        int col;
-        const uint8_t* mat;
-        if (MODE == 1) {
-          const bool up = (grow0 % C::CW) >= C::CW / 2;
-          col = nt * (C::BN / 2) + (n / C::CW) * (C::CW / 2) + (n % (C::CW / 2));
-          mat = reinterpret_cast<const uint8_t*>(up ? f.wu : f.wg) + (int64_t)g * (up ? f.su : f.sg);
-        } else {
-          col = nt * C::BN + n;
-          mat = reinterpret_cast<const uint8_t*>(f.wd) + (int64_t)g * f.sd;
-        }
-        col = col < Ncols ? col : Ncols - 1;
-        bbase[i] = reinterpret_cast<const bf16*>(mat);
-        boff[i] = (uint32_t)col * (uint32_t)K + ch * 16;
-      } else {
-        const int grow0 = (C::NW * i + wave) * C::RPL;  // wave-uniform first row of the load
-        const int n = grow0 + lrow;                       // B tile row
-        const int gchunk = lpos ^ swz<C::BK>(n);
-        int col;
-        if (MODE == 1) {
-          // wave column wc (CW rows) holds CW/2 gate rows, then the up rows of
-          // the same CW/2 hidden columns
-          const bool up = (grow0 % C::CW) >= C::CW / 2;
-          col = nt * (C::BN / 2) + (n / C::CW) * (C::CW / 2) + (n % (C::CW / 2));
-          bbase[i] = shared ? reinterpret_cast<const bf16*>(up ? f.shu : f.shg)
-                            : reinterpret_cast<const bf16*>(up ? f.wu : f.wg) + (int64_t)g * (up ? f.su : f.sg);
-        } else {
-          col = nt * C::BN + n;
-          bbase[i] = shared ? reinterpret_cast<const bf16*>(f.shd) : reinterpret_cast<const bf16*>(f.wd) + (int64_t)g * f.sd;
-        }
-        col = col < Ncols ? col : Ncols - 1;
-        boff[i] = (uint32_t)col * (uint32_t)K + gchunk * 8;
-      }
-    }
-
-    // fp8: the tile's block scales, K block kb of row sel at ssc[sel*nkb + kb]
-    // (gate/up: sel 0 gate, 1 up, of hidden block nt; down: W_down row
-    // blocks 2nt and 2nt+1, the second clamped at the last)
-    const float* sc0 = nullptr;
-    const float* sc1 = nullptr;
-    if constexpr (C::F8) {
-      const int nkb = K / 128;
-      for (int t = tid; t < 2 * nkb; t += C::NT) {
-        const int sel = t / nkb, kb = t - sel * nkb;
-        float v;
-        if (MODE == 1) {
-          v = (sel ? f.scu : f.scg)[((int64_t)g * (f.I / 128) + nt) * nkb + kb];
-        } else {
-          int rb = 2 * nt + sel;
-          rb = rb < f.H / 128 ? rb : f.H / 128 - 1;
-          v = f.scd[((int64_t)g * (f.H / 128) + rb) * nkb + kb];
-        }
-        ssc[t] = v;
-      }
-      if (MODE == 1) {
-        sc0 = ssc;
-        sc1 = ssc + nkb;
-      } else {
-        sc0 = sc1 = ssc + (wn * C::CW / 128) * nkb;
-      }
-    }
-
-    f32x16 acc[C::MI][C::NJ];
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-      for (int j = 0; j < C::NJ; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    // M-blocks of 32 rows this wave computes (blocks wm, wm+WM, ... below nrows)
-    const int nblk_tile = (nrows + 31) / 32;
-    const int nb = (nblk_tile - wm + C::WM - 1) / C::WM;
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // previous tile's loads and stores settled
-    const int nk = K / C::BK;
-    if constexpr (C::MI >= 4) {
-      if (nb >= 4) mainloop_r<C, 4>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo, sc0, sc1);
-      else if (nb == 3) mainloop_r<C, 3>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo, sc0, sc1);
-      else if (nb == 2) mainloop_r<C, 2>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo, sc0, sc1);
-      else mainloop_r<C, 1>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo, sc0, sc1);
-    } else {
-      if (nb >= 2) mainloop_r<C, 2>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo, sc0, sc1);
-      else mainloop_r<C, 1>(acc, stg, abase, aoff, bbase, boff, nk, wave, fo, sc0, sc1);
-    }
-
-    // ---- epilogue through LDS ----
-    // The tile leaves in M bands of WM*32 rows: band ii (M-blocks WM*ii ..
-    // WM*ii + WM-1) goes, as bf16 (gate/up: SiLU(g)*u), into the stage
-    // buffers (BPS bands each), then every thread stores whole 16-byte row
-    // chunks.  C lane layout of a
-    // 32x32 block: col = lane%32, row 8*(v/4) + 4*(lane/32) + v%4.  Chunk c of
-    // band row r sits at c ^ (4 * ((r >> 2) & 1)), so the two half-waves'
-    // rows (4 apart) write different banks.
-    constexpr int CCOLS = MODE == 1 ? C::BN / 2 : C::BN;  // output columns of the tile
-    constexpr int CPR = CCOLS / 8;                        // 16-byte chunks per row
-    constexpr int BAND = C::WM * 32;
-    constexpr int BPS = C::STAGE / (BAND * CCOLS);        // bands per stage buffer
-    static_assert(BPS >= 1 && C::MI <= C::S * BPS && CPR >= 8, "epilogue staging");
-    auto cpos = [&](int r, int col) { return r * CCOLS + ((((col >> 3) ^ (((r >> 2) & 1) << 2))) << 3) + (col & 7); };
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // trailing (redundant) direct loads have landed
-    block_sync();                              // every wave is done reading the stage buffers
-#pragma unroll
-    for (int ii = 0; ii < C::MI; ++ii) {
-      bf16* ct = stg[ii / BPS] + (ii % BPS) * BAND * CCOLS;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if constexpr (MODE == 1) {
-#pragma unroll
-          for (int jj = 0; jj < C::NJ / 2; ++jj)
-            ct[cpos(r, wn * (C::CW / 2) + jj * 32 + (lane & 31))] =
-                f2bf(silu(acc[ii][jj][v]) * acc[ii][jj + C::NJ / 2][v]);
-        } else {
-#pragma unroll
-          for (int jj = 0; jj < C::NJ; ++jj) ct[cpos(r, wn * C::CW + jj * 32 + (lane & 31))] = f2bf(acc[ii][jj][v]);
-        }
-      }
-    }
-    block_sync();
-    bf16* obase;
-    int ld;
-    if (MODE == 1) {
-      obase = shared ? reinterpret_cast<bf16*>(f.h_sh) : reinterpret_cast<bf16*>(f.h);
-      ld = shared ? f.Is : f.I;
-    } else {
-      obase = shared ? reinterpret_cast<bf16*>(f.y_sh) : reinterpret_cast<bf16*>(f.y);
-      ld = f.H;
-    }
-#pragma unroll
-    for (int ii = 0; ii < C::MI; ++ii) {
-      const bf16* ct = stg[ii / BPS] + (ii % BPS) * BAND * CCOLS;
-      for (int q = tid; q < BAND * CPR; q += C::NT) {
-        const int r = q / CPR, c = q % CPR;
-        const int trow = ii * BAND + r;  // band ii holds tile rows ii*BAND ..
-        const int col = nt * CCOLS + c * 8;
-        if (trow < nrows && col < Ncols)
-          st16(obase + (int64_t)(base + r0 + trow) * ld + col, ld16(ct + cpos(r, c * 8)));
-      }
-    }
+    run_tile<C, MODE>(f, mt_first + sbase + r % grp, r / grp, stg, ssc, tid, lane, wave, fo);
   }
 }
 
@@ -534,18 +583,21 @@ int cu_count() {
   return cus;
 }
 
+// One launch of a phase over the m-tiles [plan[tb], plan[te]), with the given
+// block of eight claim counters.
 template <class C>
-hipError_t launch(const FfnArgs& a, int phase, hipStream_t s, int list_begin_idx, int list_end_idx) {
+hipError_t launch(const FfnArgs& a, int phase, hipStream_t s, int tb, int te, int ctr_block) {
   const int wide = a.I > a.Is ? a.I : a.Is;
   const int ntn = phase == 1 ? (wide + C::BN / 2 - 1) / (C::BN / 2) : (a.H + C::BN - 1) / C::BN;
   const int grid = (cu_count() * C::WG_PER_CU + 7) / 8 * 8;  // resident workgroups, a multiple of 8 XCDs
-  // Each XCD takes grid/8 consecutive tiles: supertiles of 8 m-tiles, so an
-  // expert's weight slice serves up to 8 of its m-tiles from L2.  (Two
-  // m-tiles x all n-tiles per XCD, which fetches each A slice once, measured
-  // slower on the 8192-token skewed layer.)
+  // Each XCD takes grid/8 consecutive tiles of a round: supertiles of 8
+  // m-tiles, so an expert's weight slice serves up to 8 of its m-tiles from
+  // L2.  (Two m-tiles x all n-tiles per XCD, which fetches each A slice once,
+  // measured slower on the 8192-token skewed layer.)
   const int super = 8;
-  if (phase == 1) dma_gemm_kernel<C, 1><<<grid, C::NT, 0, s>>>(a, ntn, super, list_begin_idx, list_end_idx);
-  else dma_gemm_kernel<C, 2><<<grid, C::NT, 0, s>>>(a, ntn, super, list_begin_idx, list_end_idx);
+  int32_t* ctr = const_cast<int32_t*>(a.plan) + kPlanCounters + (ctr_block * 2 + phase - 1) * 8;
+  if (phase == 1) ffn_tiles_kernel<C, 1><<<grid, C::NT, 0, s>>>(a, ntn, super, tb, te, ctr);
+  else ffn_tiles_kernel<C, 2><<<grid, C::NT, 0, s>>>(a, ntn, super, tb, te, ctr);
   return hipGetLastError();
 }
 
@@ -559,12 +611,12 @@ bool ffn_dma_supported(const FfnArgs& a) {
   return a.H % k == 0 && a.I % k == 0;
 }
 
-hipError_t launch_ffn_gemm_dma(const FfnArgs& a, int phase, hipStream_t s) {
-  if (!a.fp8) return launch<BigCfg>(a, phase, s, kPlanStart, kPlanTiles);
-  // fp8 layers: routed m-tiles [0, plan[2]) decode codes, the shared
-  // expert's [plan[2], plan[0]) are bf16
-  hipError_t e = launch<BigCfg8>(a, phase, s, kPlanStart, kPlanRoutedTiles);
-  if (e == hipSuccess && a.Is > 0) e = launch<BigCfg>(a, phase, s, kPlanRoutedTiles, kPlanTiles);
+hipError_t launch_ffn_gemm_big(const FfnArgs& a, int phase, hipStream_t s) {
+  if (!a.fp8) return launch<BigCfg>(a, phase, s, kPlanStart, kPlanTiles, 0);
+  // fp8 layers: the routed groups' tiles decode codes; the shared expert's
+  // [plan[2], plan[0]) tiles are bf16
+  hipError_t e = launch<BigCfg8>(a, phase, s, kPlanStart, kPlanRoutedTiles, 0);
+  if (e == hipSuccess && a.Is > 0) e = launch<BigCfg>(a, phase, s, kPlanRoutedTiles, kPlanTiles, 1);
   return e;
 }
 

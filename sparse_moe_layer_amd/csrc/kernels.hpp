@@ -14,20 +14,20 @@ constexpr int kGemmBM = 128;
 constexpr int kGemmBigBM = 256;
 constexpr int kStreamBM = 16;
 constexpr int kMaxExperts = 1024;
-// plan ints ahead of the work lists: [0] m-tiles of the first list, [1] stream
-// m-blocks, [2] / [3] where the shared expert's m-tiles / m-blocks begin,
-// [4, 5) the second m-tile list (128-row remainders of 256-row tiling)
-constexpr int kPlanHeader = 8;
+// plan ints ahead of the work lists: [0] m-tiles, [1] stream m-blocks,
+// [2] / [3] where the shared expert's m-tiles / m-blocks begin, then the
+// fused kernel's claim counters: kPlanCounters + (launch * 2 + phase - 1) * 8,
+// eight per XCD-indexed counter block, zeroed by the plan kernel
+constexpr int kPlanCounters = 8;
+constexpr int kPlanHeader = kPlanCounters + 4 * 8;
 // Positions in the plan header, as the kernels' list bounds: a kernel runs
 // the entries [plan[begin], plan[end]) of its list, begin kPlanStart meaning 0.
 enum PlanPos : int {
   kPlanStart = -1,
-  kPlanTiles = 0,          // end of the first m-tile list
+  kPlanTiles = 0,          // end of the m-tile list
   kPlanBlocks = 1,         // end of the stream m-block list
   kPlanRoutedTiles = 2,    // end of the routed groups' m-tiles (the shared expert's follow)
   kPlanRoutedBlocks = 3,   // end of the routed groups' m-blocks (the shared expert's follow)
-  kPlanTiles2Begin = 4,    // the second m-tile list
-  kPlanTiles2End = 5,
 };
 // An expert with at most this many rows streams its weights (small-M path).
 constexpr int kStreamMaxRows = 16;
@@ -82,17 +82,19 @@ hipError_t launch_topk(const float* partial, int nsplit, int ldl, int T, int E, 
 size_t dispatch_ws_ints(int64_t T, int64_t E);
 hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* offsets,
                            int32_t* sorted, int32_t* pos, int32_t* ws, hipStream_t s);
+// Groups of more than stream_rows rows (and none with MOE_FLAG_FORCE_STREAM,
+// all with MOE_FLAG_FORCE_GEMM) become m-tiles of bm rows, the rest 16-row
+// streaming m-blocks.
 hipError_t launch_ffn_plan(const int32_t* offsets, const int32_t* sorted, int T, int E, int k, int has_shared,
-                           uint32_t flags, int bm, int32_t* plan_ws, hipStream_t s);
+                           uint32_t flags, int bm, int stream_rows, int32_t* plan_ws, hipStream_t s);
 void ffn_bind_plan(FfnArgs& a, int32_t* plan_ws);
-// phase 1 gate/up, 2 down; bf16 tiles run the m-tiles [plan[begin], plan[end])
-// (begin < 0: from 0), fp8 tiles the whole first list
-hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s, int list_begin_idx = kPlanStart,
-                           int list_end_idx = kPlanTiles);
-// Pipelined direct-load MFMA GEMM with 256-row tiles (bf16 weights, H, I,
-// I_shared multiples of 32).
+// phase 1 gate/up, 2 down: the 128-row MFMA tiles over the m-tile list
+hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s);
+// Persistent direct-load MFMA GEMM with 256-row tiles for layers with
+// hundreds of rows per expert (ragged last m-tiles included; bf16 weights
+// need H, I and I_shared multiples of 32).
 bool ffn_dma_supported(const FfnArgs& a);
-hipError_t launch_ffn_gemm_dma(const FfnArgs& a, int phase, hipStream_t s);
+hipError_t launch_ffn_gemm_big(const FfnArgs& a, int phase, hipStream_t s);
 // phase 1 gate/up, 2 down.  self_plan: T <= kStreamMaxRows and no plan kernel
 // ran; the kernels list the touched groups from the offsets themselves.
 hipError_t launch_ffn_stream(const FfnArgs& a, int phase, hipStream_t s, bool self_plan = false);
