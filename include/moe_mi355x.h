@@ -224,6 +224,22 @@ moe_status moe_layer_forward(const moe_problem* p, const moe_weights* w, const v
                              void* out, int32_t* topk_ids, float* topk_w,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* moe_layer_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops and harnesses that forbid
+ * hipMalloc): the same kernels, with the workspace in a device array inside
+ * the library instead of the ws argument.  It calls no allocating routine.
+ *   Problems whose moe_workspace_bytes(p) exceeds MOE_NOALLOC_SCRATCH_BYTES
+ *   (32 MiB: decode batches and prefill chunks of a few hundred tokens at the
+ *   2.4T shape) return MOE_ERR_WORKSPACE before any launch.
+ *   Each GPU holds one copy of the array for the life of the process, shared
+ *   by every call on that GPU: calls that overlap on one GPU (different
+ *   streams or threads) race on it and must be serialised by the caller.
+ *   Nothing in it needs to start at zero; every call writes what it reads.
+ * Other arguments, outputs and errors as moe_layer_forward.               */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_layer_forward_noalloc(const moe_problem* p, const moe_weights* w, const void* x,
+                                     void* out, int32_t* topk_ids, float* topk_w, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Gated residual around the layer (Qwen3.8-Flash-Next study, "Gated residual:
  * four streams, one sublayer input"): the persistent residual is four

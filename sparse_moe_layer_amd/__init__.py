@@ -13,7 +13,8 @@ from typing import Optional
 import torch
 
 from ._lib import (LIB, MOE_BF16, MOE_F32, MOE_FLAG_FORCE_GEMM, MOE_FLAG_FORCE_STREAM,  # noqa: F401
-                   MOE_FLAG_GEMM_TILE_128, MOE_FLAG_GEMM_TILE_256, MOE_FLAG_PAGE_ROUTING, MOE_FP8_E4M3FN, MOE_OK, EXPORTS, moe_audit_stats, moe_gr_weights, moe_problem,
+                   MOE_FLAG_GEMM_TILE_128, MOE_FLAG_GEMM_TILE_256, MOE_FLAG_PAGE_ROUTING, MOE_FP8_E4M3FN,
+                   MOE_NOALLOC_SCRATCH_BYTES, MOE_OK, EXPORTS, moe_audit_stats, moe_gr_weights, moe_problem,
                    moe_weights)
 
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3FN}
@@ -109,6 +110,11 @@ def moe_combine(p, y, assign_pos, topk_w, y_shared, shared_logit, out, stream=No
 def moe_layer_forward(p, w: moe_weights, x, out, topk_ids, topk_w, ws, stream=None):
     _check(LIB.moe_layer_forward(ctypes.byref(p), ctypes.byref(w), _ptr(x), _ptr(out), _ptr(topk_ids),
                                  _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream)), "moe_layer_forward")
+
+
+def moe_layer_forward_noalloc(p, w: moe_weights, x, out, topk_ids, topk_w, stream=None):
+    _check(LIB.moe_layer_forward_noalloc(ctypes.byref(p), ctypes.byref(w), _ptr(x), _ptr(out), _ptr(topk_ids),
+                                         _ptr(topk_w), _stream(stream)), "moe_layer_forward_noalloc")
 
 
 def gr_weights(norm_w, w_read, w_up, rank: int, eps: float = 1e-6) -> moe_gr_weights:

@@ -282,6 +282,38 @@ moe_status do_ffn(const moe_problem* p, const moe_weights* w, const void* x, con
 
 }  // namespace
 
+namespace moe {
+
+moe_status layer_forward_checks(const moe_problem* p, const moe_weights* w, const void* x, const void* out) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (p->T == 0) return MOE_OK;  // empty batch: nothing to read or write
+  if ((st = check_weights(p, w, true, true)) != MOE_OK) return st;
+  if (!x || !out) return MOE_ERR_NULL;
+  if (!al16(x) || !al16(out)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+moe_status layer_forward_run(const moe_problem* p, const moe_weights* w, const void* x, void* out,
+                             int32_t* topk_ids, float* topk_w, void* ws, hipStream_t s) {
+  moe_status st;
+  LayerWs L = layer_layout(p, ws);
+  int32_t* ids = topk_ids ? topk_ids : L.ids;
+  float* tw = topk_w ? topk_w : L.w;
+  const bool sh = p->I_shared > 0;
+  if ((st = do_route(p, x, w->w_router, sh ? w->sh_gate_w : nullptr, ids, tw, sh ? L.sl : nullptr, L.stage, s)) !=
+      MOE_OK)
+    return st;
+  if ((st = hip_status(moe::launch_dispatch(ids, (int)p->T, (int)p->E, (int)p->k, L.offsets, L.sorted, L.pos,
+                                            static_cast<int32_t*>(L.stage), s))) != MOE_OK)
+    return st;
+  if ((st = do_ffn(p, w, x, L.offsets, L.sorted, L.y, sh ? L.y_sh : nullptr, L.stage, s)) != MOE_OK) return st;
+  return hip_status(moe::launch_combine(L.y, L.pos, tw, sh ? L.y_sh : nullptr, sh ? L.sl : nullptr, out, (int)p->T,
+                                        (int)p->H, (int)p->k, p->act_dtype == MOE_F32 ? 1 : 0, s));
+}
+
+}  // namespace moe
+
 extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
@@ -392,27 +424,10 @@ moe_status moe_combine(const moe_problem* p, const void* y, const int32_t* assig
 
 moe_status moe_layer_forward(const moe_problem* p, const moe_weights* w, const void* x, void* out,
                              int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
-  moe_status st = check_problem(p);
-  if (st != MOE_OK) return st;
-  if (p->T == 0) return MOE_OK;  // empty batch: nothing to read or write
-  if ((st = check_weights(p, w, true, true)) != MOE_OK) return st;
-  if (!x || !out) return MOE_ERR_NULL;
-  if (!al16(x) || !al16(out)) return MOE_ERR_ALIGN;
+  moe_status st = moe::layer_forward_checks(p, w, x, out);
+  if (st != MOE_OK || p->T == 0) return st;
   if ((st = check_ws(p, ws, ws_bytes)) != MOE_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  LayerWs L = layer_layout(p, ws);
-  int32_t* ids = topk_ids ? topk_ids : L.ids;
-  float* tw = topk_w ? topk_w : L.w;
-  const bool sh = p->I_shared > 0;
-  if ((st = do_route(p, x, w->w_router, sh ? w->sh_gate_w : nullptr, ids, tw, sh ? L.sl : nullptr, L.stage, s)) !=
-      MOE_OK)
-    return st;
-  if ((st = hip_status(moe::launch_dispatch(ids, (int)p->T, (int)p->E, (int)p->k, L.offsets, L.sorted, L.pos,
-                                            static_cast<int32_t*>(L.stage), s))) != MOE_OK)
-    return st;
-  if ((st = do_ffn(p, w, x, L.offsets, L.sorted, L.y, sh ? L.y_sh : nullptr, L.stage, s)) != MOE_OK) return st;
-  return hip_status(moe::launch_combine(L.y, L.pos, tw, sh ? L.y_sh : nullptr, sh ? L.sl : nullptr, out, (int)p->T,
-                                        (int)p->H, (int)p->k, p->act_dtype == MOE_F32 ? 1 : 0, s));
+  return moe::layer_forward_run(p, w, x, out, topk_ids, topk_w, ws, (hipStream_t)stream);
 }
 
 

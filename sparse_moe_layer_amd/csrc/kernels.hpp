@@ -108,6 +108,13 @@ hipError_t launch_combine_gr_write(const void* y, const int32_t* pos, const floa
                                    const float* shared_logit, void* out, const void* resid, const float* gate,
                                    void* resid_out, int T, int H, int k, hipStream_t s);
 
+// The whole layer behind moe_layer_forward: argument checks (MOE_OK also
+// for an empty batch, which needs no run), then the launches on workspace
+// ws of moe_workspace_bytes(p) bytes (no workspace check).
+moe_status layer_forward_checks(const moe_problem* p, const moe_weights* w, const void* x, const void* out);
+moe_status layer_forward_run(const moe_problem* p, const moe_weights* w, const void* x, void* out,
+                             int32_t* topk_ids, float* topk_w, void* ws, hipStream_t s);
+
 // Gated residual read / write (bf16).
 // Expert-weight audit (bf16): histograms of the bit patterns per slice and
 // over the tensor, then the exact statistics of each.

@@ -132,6 +132,17 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert L.moe_layer_forward(ctypes.byref(p0), ctypes.byref(
         _lib.moe_weights(fake, fake, fake, fake, 0, 0, 0, None, None, None, None, None, None, None)),
         fake, fake, None, None, fake, lib.moe_workspace_bytes(p0), None) == OK
+    # the allocation-free layer call: same checks, and problems whose workspace
+    # exceeds its device array are refused before any launch
+    wf = _lib.moe_weights(fake, fake, fake, fake, 0, 0, 0, None, None, None, None, None, None, None)
+    NA = L.moe_layer_forward_noalloc
+    assert NA(P, ctypes.byref(wf), None, fake, None, None, None) == _lib.MOE_ERR_NULL
+    assert NA(P, ctypes.byref(wf), fake + 8, fake, None, None, None) == _lib.MOE_ERR_ALIGN
+    big = lib.problem(4096, 2560, 512, 10, 640, 640)
+    assert lib.moe_workspace_bytes(big) > _lib.MOE_NOALLOC_SCRATCH_BYTES
+    wb = _lib.moe_weights(fake, fake, fake, fake, 0, 0, 0, None, None, None, fake, fake, fake, fake)
+    assert NA(ctypes.byref(big), ctypes.byref(wb), fake, fake, None, None, None) == _lib.MOE_ERR_WORKSPACE
+    assert NA(ctypes.byref(p0), ctypes.byref(wf), fake, fake, None, None, None) == OK
 
 
 def test_gated_residual_entry_points_validate_before_any_launch():
