@@ -305,7 +305,7 @@ moe_status layer_forward_run(const moe_problem* p, const moe_weights* w, const v
       MOE_OK)
     return st;
   if ((st = hip_status(moe::launch_dispatch(ids, (int)p->T, (int)p->E, (int)p->k, L.offsets, L.sorted, L.pos,
-                                            static_cast<int32_t*>(L.stage), s))) != MOE_OK)
+                                            static_cast<int32_t*>(L.stage), s, /*distinct=*/true))) != MOE_OK)
     return st;
   if ((st = do_ffn(p, w, x, L.offsets, L.sorted, L.y, sh ? L.y_sh : nullptr, L.stage, s)) != MOE_OK) return st;
   return hip_status(moe::launch_combine(L.y, L.pos, tw, sh ? L.y_sh : nullptr, sh ? L.sl : nullptr, out, (int)p->T,

@@ -14,10 +14,11 @@
 //              same token with the same expert, and the last such lane
 //              advances the cursor by the group's size, so positions come
 //              out ascending in a within every expert (stable).
-// The router never repeats an expert within a token, but moe_dispatch takes
-// caller ids: a repeated id still gets its own slot (ordered by j), and ids
-// outside [0, E) are clamped into range, so sorted_assign is always a
-// permutation of [0, R) and assign_pos its inverse.
+// The router never repeats an expert within a token (the layer call's
+// dispatch skips the check), but moe_dispatch takes caller ids: a repeated id
+// still gets its own slot (ordered by j), and ids outside [0, E) are clamped
+// into range, so sorted_assign is always a permutation of [0, R) and
+// assign_pos its inverse.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -55,6 +56,7 @@ __device__ __forceinline__ TokenRank token_rank(int e, int lane, int k) {
 // never repeats one, and then each lane takes p = cur[e], cur[e] = p + 1.
 // Otherwise every lane adds its rank among the token's lanes with the same
 // expert, and the last of them advances the cursor by the group's size.
+template <bool CHECK>
 __device__ __forceinline__ void scatter_tokens(const int32_t* __restrict__ ids, int t0, int nt, int E, int k,
                                                int lane, int* cur, int* mark, int32_t* __restrict__ sorted,
                                                int32_t* __restrict__ pos) {
@@ -67,11 +69,14 @@ __device__ __forceinline__ void scatter_tokens(const int32_t* __restrict__ ids, 
     if (i < nt) {
       const int e = ev[i];
       const bool mine = lane < k;
-      // volatile: the read must observe the write instruction's winner, not
-      // this lane's own stored value
-      volatile int* mk = mark;
-      if (mine) mk[e] = lane;
-      const bool rep = mine && mk[e] != lane;
+      bool rep = false;
+      if constexpr (CHECK) {
+        // volatile: the read must observe the write instruction's winner, not
+        // this lane's own stored value
+        volatile int* mk = mark;
+        if (mine) mk[e] = lane;
+        rep = mine && mk[e] != lane;
+      }
       const int64_t a = (int64_t)(t0 + i) * k + lane;
       if (__ballot(rep) == 0) {
         if (mine) {
@@ -154,6 +159,7 @@ __global__ __launch_bounds__(1024) void chunk_scan_kernel(int32_t* __restrict__ 
 // expert offsets (every block redoes this small scan; block 0 publishes
 // them), then walks its tokens in order: lane j of a token takes its
 // expert's cursor plus its rank among the token's lanes with that expert.
+template <bool CHECK>
 __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
                                                      const int32_t* __restrict__ chunk_prefix,
                                                      const int32_t* __restrict__ totals,
@@ -185,12 +191,13 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
   __syncthreads();
   const int t0 = blockIdx.x * CH;
   const int nt = T - t0 < CH ? T - t0 : CH;
-  scatter_tokens(ids, t0, nt, E, k, lane, cur, cur + E, sorted, pos);
+  scatter_tokens<CHECK>(ids, t0, nt, E, k, lane, cur, cur + E, sorted, pos);
 }
 
 // Whole dispatch of a batch of at most CH tokens in one 1024-thread
 // workgroup (decode): LDS counts, workgroup scan into expert_offsets, then
 // wave 0 walks the tokens in order as in scatter_kernel.
+template <bool CHECK>
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ sorted, int32_t* __restrict__ pos) {
@@ -231,7 +238,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
   }
   if (tid == 0) offsets[E] = R;
   __syncthreads();
-  if (w == 0) scatter_tokens(ids, 0, T, E, k, lane, cur, mark, sorted, pos);
+  if (w == 0) scatter_tokens<CHECK>(ids, 0, T, E, k, lane, cur, mark, sorted, pos);
 }
 
 }  // namespace
@@ -239,16 +246,18 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
 size_t dispatch_ws_ints(int64_t T, int64_t E) { return (size_t)((T + CH - 1) / CH) * (size_t)E + (size_t)E; }
 
 hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* offsets, int32_t* sorted,
-                           int32_t* pos, int32_t* ws, hipStream_t s) {
+                           int32_t* pos, int32_t* ws, hipStream_t s, bool distinct) {
   if (T <= CH) {
-    dispatch_small_kernel<<<1, 1024, 0, s>>>(ids, T, E, k, offsets, sorted, pos);
+    if (distinct) dispatch_small_kernel<false><<<1, 1024, 0, s>>>(ids, T, E, k, offsets, sorted, pos);
+    else dispatch_small_kernel<true><<<1, 1024, 0, s>>>(ids, T, E, k, offsets, sorted, pos);
     return hipGetLastError();
   }
   const int nch = (T + CH - 1) / CH;
   int32_t* totals = ws + (size_t)nch * E;
   count_kernel<<<nch, 256, E * sizeof(int), s>>>(ids, T, E, k, ws);
   chunk_scan_kernel<<<(E + 63) / 64, 1024, 0, s>>>(ws, nch, E, totals);
-  scatter_kernel<<<nch, 64, 2 * E * sizeof(int), s>>>(ids, T, E, k, ws, totals, offsets, sorted, pos);
+  if (distinct) scatter_kernel<false><<<nch, 64, 2 * E * sizeof(int), s>>>(ids, T, E, k, ws, totals, offsets, sorted, pos);
+  else scatter_kernel<true><<<nch, 64, 2 * E * sizeof(int), s>>>(ids, T, E, k, ws, totals, offsets, sorted, pos);
   return hipGetLastError();
 }
 

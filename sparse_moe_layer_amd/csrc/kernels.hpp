@@ -80,8 +80,10 @@ hipError_t launch_router_logits_f32(const float* x, const float* w_router, const
 hipError_t launch_topk(const float* partial, int nsplit, int ldl, int T, int E, int k, int has_sg, bool page,
                        int32_t* ids, float* w, float* shared_logit, hipStream_t s);
 size_t dispatch_ws_ints(int64_t T, int64_t E);
+// distinct: the ids come from the router, which never repeats an expert
+// within a token (skips the per-token check for repeats).
 hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* offsets,
-                           int32_t* sorted, int32_t* pos, int32_t* ws, hipStream_t s);
+                           int32_t* sorted, int32_t* pos, int32_t* ws, hipStream_t s, bool distinct = false);
 // Groups of more than stream_rows rows (and none with MOE_FLAG_FORCE_STREAM,
 // all with MOE_FLAG_FORCE_GEMM) become m-tiles of bm rows, the rest 16-row
 // streaming m-blocks.
