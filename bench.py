@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--no-ep-share", action="store_true", help="accepted for older commands (the default)")
     ap.add_argument("--layer-only", action="store_true",
                     help="skip the gated-residual and weight-audit rows (kernel traces of the layer alone)")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="only time moe_hbm_read_probe (one pass over 4 GiB, 16 B per lane) and print its rate")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scale factor for HBM byte counters)")
     return ap.parse_args()
@@ -77,6 +79,31 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+
+
+def stream_ceiling(lib, stream, nbytes=4 << 30, launches=20):
+    """Practical HBM read ceiling: the rate of a kernel that only reads, with the
+    streaming kernels' access shape, over a buffer far larger than the 256 MB
+    last-level cache.  Timed with HIP events on the stream it is launched on."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(3)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            lib.moe_hbm_read_probe(src, sink, stream)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+        for a, b in evs:
+            a.record(stream)
+            lib.moe_hbm_read_probe(src, sink, stream)
+            b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    del src
+    torch.cuda.empty_cache()
+    gbs = [nbytes / (m * 1e-3) / 1e9 for m in ms]
+    return {"kernel": "hbm_read_probe_kernel", "bytes": nbytes, "launches": launches,
+            "ms_median": round(pct(ms, 0.5), 4), "gbs_median": round(pct(gbs, 0.5), 1),
+            "gbs_best": round(max(gbs), 1), "frac_of_8tbs": round(pct(gbs, 0.5) / 8000.0, 4)}
 
 
 def kernel_source_sha():
@@ -540,6 +567,9 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     print(f"[bench] {torch.cuda.get_device_name(dev)}", file=sys.stderr, flush=True)
+    if args.stream_ceiling:
+        print(json.dumps({"stream_ceiling": stream_ceiling(lib, torch.cuda.current_stream())}), flush=True)
+        return
     flags = {"auto": 0, "128": lib.MOE_FLAG_GEMM_TILE_128, "256": lib.MOE_FLAG_GEMM_TILE_256}[args.gemm_tile]
     flags |= {"auto": 0, "gemm": lib.MOE_FLAG_FORCE_GEMM, "stream": lib.MOE_FLAG_FORCE_STREAM}[args.path]
     stream = torch.cuda.current_stream()
@@ -593,6 +623,7 @@ def main():
                          "target_ms": round(d["layer"]["t_roof_ms"] / 0.7, 4), "stages_ms": d["stages_ms"]}
     if others:
         res["workloads"] = others
+    res["stream_ceiling"] = stream_ceiling(lib, stream)
     print(json.dumps(res), flush=True)
 
 

@@ -326,6 +326,16 @@ size_t moe_audit_workspace_bytes(int64_t slices);
 moe_status moe_weight_audit(const void* w, int32_t dtype, int64_t slices, int64_t n, int64_t slice_stride,
                             moe_audit_stats* stats, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Measurement helper (not a step of the layer): reads `bytes` of device
+ * memory at src once, 16 bytes per lane over contiguous runs with eight loads
+ * in flight per lane, and writes nothing (sink: a device uint32, written only
+ * in a case that does not arise in practice).  Its rate is the practical HBM
+ * read ceiling that the streaming stages' rates are compared with.  src
+ * 16-byte aligned and bytes a multiple of 16 (MOE_ERR_ALIGN).
+ * --------------------------------------------------------------------------- */
+moe_status moe_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -112,6 +112,11 @@ def moe_layer_forward(p, w: moe_weights, x, out, topk_ids, topk_w, ws, stream=No
                                  _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream)), "moe_layer_forward")
 
 
+def moe_hbm_read_probe(src, sink, stream=None):
+    _check(LIB.moe_hbm_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)),
+           "moe_hbm_read_probe")
+
+
 def moe_layer_forward_noalloc(p, w: moe_weights, x, out, topk_ids, topk_w, stream=None):
     _check(LIB.moe_layer_forward_noalloc(ctypes.byref(p), ctypes.byref(w), _ptr(x), _ptr(out), _ptr(topk_ids),
                                          _ptr(topk_w), _stream(stream)), "moe_layer_forward_noalloc")
