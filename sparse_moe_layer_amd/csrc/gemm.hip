@@ -585,7 +585,8 @@ int router_gemm_split(int T, int H, int E) {
   // as many (m, n, K-chunk) tiles as fit in one round of resident workgroups
   // (two per CU): a split that spills a few tiles into a second round
   // doubles the kernel's time.  Chunks are whole 64-wide K steps.
-  const int tiles = ((T + BM - 1) / BM) * ((E + 1 + BN - 1) / BN);
+  int tiles = ((T + BM - 1) / BM) * ((E + 1 + BN - 1) / BN);
+  tiles = tiles < 1 ? 1 : tiles;  // an empty batch still sizes one split
   int ns = (2 * num_cus()) / tiles;
   const int maxs = H / (4 * BK) > 0 ? H / (4 * BK) : 1;
   ns = ns < 1 ? 1 : (ns > maxs ? maxs : ns);
