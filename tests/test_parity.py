@@ -128,16 +128,89 @@ def sample_tokens(T, n, seed=0):
     return np.array(sorted(pick))
 
 
+# Rows per expert group at or below which a group streams its weights instead
+# of taking GEMM tiles, and the two m-tile heights of the GEMM kernels.
+STREAM_ROWS = 16
+TILE_ROWS = (128, 256)
+
+
+def tile_class_tokens(g, cfg, per_class=2):
+    """Tokens whose rows land in every kind of tile the expert GEMMs form.
+
+    From the (already bit-exact) expert offsets and permutation: per expert
+    group of n rows, rows at the edges of full m-tiles of either height, the
+    first and last rows of a ragged last m-tile (after full tiles, alone, and
+    one row long), and rows of groups that stream (n <= STREAM_ROWS, one row
+    long included).  Shared-expert rows are the tokens themselves, so token
+    indices at m-tile edges cover its tiles.  Every sampled row is compared
+    over all output columns, which covers every n-tile of both phases.
+    Returns (tokens, {class: [(expert, row in group, token), ...]})."""
+    offs, sa, k = g["offsets"], g["sorted"], cfg.k
+    n = np.diff(offs)
+    order = np.argsort(-n, kind="stable")          # hottest groups first
+    classes = {}
+
+    def add(cls, e, r):
+        lst = classes.setdefault(cls, [])
+        if len(lst) < per_class and r < n[e]:
+            lst.append((int(e), int(r), int(sa[offs[e] + r]) // k))
+
+    for e in order:
+        ne = int(n[e])
+        if ne == 0:
+            continue
+        if ne <= STREAM_ROWS:
+            add("stream" if ne > 1 else "stream_1row", e, ne - 1)
+            add("stream_first", e, 0)
+            continue
+        for bm in TILE_ROWS:
+            full, rem = divmod(ne, bm)
+            if full:
+                add(f"full{bm}_edges", e, 0)
+                add(f"full{bm}_edges", e, bm - 1)
+                if full > 1:
+                    add(f"full{bm}_inner", e, bm)
+            if rem:
+                where = "after_full" if full else "alone"
+                add(f"ragged{bm}_{where}_first", e, full * bm)
+                add(f"ragged{bm}_{where}_last", e, ne - 1)
+                if rem == 1:
+                    add(f"ragged{bm}_1row", e, ne - 1)
+    toks = {0, cfg.T - 1}
+    if cfg.I_shared > 0:
+        for bm in TILE_ROWS:
+            toks |= {t for t in (bm - 1, bm, cfg.T - (cfg.T % bm or bm)) if 0 <= t < cfg.T}
+    for lst in classes.values():
+        toks |= {t for _, _, t in lst}
+    return np.array(sorted(toks)), classes
+
+
 # ----------------------------------------------------------------------------
 # The five workloads at full size
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("name,n_tok", [("toy_fp32", None), ("flash_decode", None), ("flash_prefill", 48),
-                                        ("max_fp8", 12), ("max_prefill", 12)])
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("name,n_tok", [("toy_fp32", None), ("flash_decode", None), ("flash_prefill", 8),
+                                        ("max_fp8", 4), ("max_prefill", 4)])
 def test_workload_parity(name, n_tok):
+    """Small workloads everywhere; full-size ones on tokens chosen to put a
+    row in every tile class of both GEMM phases, plus a few drawn at random."""
     cfg = CONFIGS[name]
     p = gpu_problem(cfg)
     g = run_stages(p)
-    check(p, g, None if n_tok is None else sample_tokens(cfg.T, n_tok))
+    if n_tok is None:
+        check(p, g)
+    else:
+        toks, classes = tile_class_tokens(g, cfg, per_class=1)
+        for cls, lst in sorted(classes.items()):
+            print(f"[coverage] {name} {cls}: " + ", ".join(f"e{e} row {r} -> t{t}" for e, r, t in lst), flush=True)
+        assert any(c.startswith("ragged") for c in classes), "no ragged m-tile sampled"
+        if cfg.zipf_s:
+            # the skewed batches hold full 256-row tiles, ragged tails and streamed groups
+            assert any(c.startswith("full256") for c in classes), "no full 256-row tile sampled"
+            assert any(c.startswith("stream") for c in classes), "no streamed group sampled"
+        toks = np.union1d(toks, sample_tokens(cfg.T, n_tok))
+        print(f"[coverage] {name}: {len(classes)} classes, {len(toks)} tokens", flush=True)
+        check(p, g, toks)
     del p
     torch.cuda.empty_cache()
 
