@@ -51,7 +51,7 @@ StageSizes stage_sizes(const moe_problem* p) {
   StageSizes s{};
   const size_t T = (size_t)p->T, E = (size_t)p->E, k = (size_t)p->k;
   const size_t R = T * k;
-  s.route = up((size_t)route_plan(p).nsplit * T * (E + 1) * 4);
+  s.route = up((size_t)route_plan(p).nsplit * T * (E + 1) * 4) + kAlign;  // partials, then one counter
   s.dispatch = up(moe::dispatch_ws_ints(p->T, p->E) * 4);
   s.ffn = up(moe::ffn_plan_ints(p->T, p->E, p->k, p->I_shared > 0) * 4) + up(R * (size_t)p->I * act_bytes(p)) +
           up(T * (size_t)p->I_shared * act_bytes(p));
@@ -167,24 +167,42 @@ inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : M
 // ---------------------------------------------------------------------------
 // stage bodies (arguments already validated)
 // ---------------------------------------------------------------------------
+// Where the layer call's small batches (T <= kSmallBatch) take the dispatch
+// from the top-k kernel itself.  Such a batch always routes with the
+// streaming (or fp32) router, whose launch zeroes the top-k counter.
+static_assert(moe::kSmallBatch <= moe::kStreamMaxRows, "small batches take the streaming router");
+struct DispatchOut {
+  int32_t* offsets;
+  int32_t* sorted;
+  int32_t* pos;
+};
+
 moe_status do_route(const moe_problem* p, const void* x, const void* w_router, const void* sh_gate_w,
-                    int32_t* ids, float* w, float* sl, void* stage, hipStream_t s) {
+                    int32_t* ids, float* w, float* sl, void* stage, hipStream_t s,
+                    const DispatchOut* d = nullptr) {
   const int T = (int)p->T, H = (int)p->H, E = (int)p->E, k = (int)p->k;
   const void* wsg = (sh_gate_w && sl) ? sh_gate_w : nullptr;
   float* partial = static_cast<float*>(stage);
   const RoutePlan rp = route_plan(p);
+  // the fused small-batch top-k's counter, after the partial logits; the
+  // router launch zeroes it
+  const bool fused = d && T <= moe::kSmallBatch;
+  int32_t* counter = reinterpret_cast<int32_t*>(static_cast<char*>(stage) +
+                                                up((size_t)rp.nsplit * T * (E + 1) * 4));
   hipError_t e;
   if (p->act_dtype == MOE_F32)
     e = moe::launch_router_logits_f32(static_cast<const float*>(x), static_cast<const float*>(w_router),
-                                      static_cast<const float*>(wsg), partial, T, H, E, s);
+                                      static_cast<const float*>(wsg), partial, T, H, E, s, fused ? counter : nullptr);
   else if (rp.stream)
-    e = moe::launch_router_stream(x, w_router, wsg, partial, T, H, E, rp.nsplit, s);
+    e = moe::launch_router_stream(x, w_router, wsg, partial, T, H, E, rp.nsplit, s, fused ? counter : nullptr);
   else
     e = moe::launch_router_logits_bf16(x, w_router, wsg, partial, T, H, E, rp.nsplit, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(
-      moe::launch_topk(partial, rp.nsplit, E + (wsg ? 1 : 0), T, E, k, wsg ? 1 : 0,
-                       p->act_dtype == MOE_BF16 && (p->flags & MOE_FLAG_PAGE_ROUTING), ids, w, sl, s));
+  const bool page = p->act_dtype == MOE_BF16 && (p->flags & MOE_FLAG_PAGE_ROUTING);
+  if (fused)
+    return hip_status(moe::launch_topk_dispatch_small(partial, rp.nsplit, E + (wsg ? 1 : 0), T, E, k, wsg ? 1 : 0,
+                                                      page, ids, w, sl, d->offsets, d->sorted, d->pos, counter, s));
+  return hip_status(moe::launch_topk(partial, rp.nsplit, E + (wsg ? 1 : 0), T, E, k, wsg ? 1 : 0, page, ids, w, sl, s));
 }
 
 FfnArgs ffn_args(const moe_problem* p, const moe_weights* w, const void* x, const int32_t* offsets,
@@ -301,11 +319,15 @@ moe_status layer_forward_run(const moe_problem* p, const moe_weights* w, const v
   int32_t* ids = topk_ids ? topk_ids : L.ids;
   float* tw = topk_w ? topk_w : L.w;
   const bool sh = p->I_shared > 0;
-  if ((st = do_route(p, x, w->w_router, sh ? w->sh_gate_w : nullptr, ids, tw, sh ? L.sl : nullptr, L.stage, s)) !=
-      MOE_OK)
+  // a small batch's dispatch comes out of the top-k workgroup
+  const bool small = p->T <= moe::kSmallBatch;
+  const DispatchOut d{L.offsets, L.sorted, L.pos};
+  if ((st = do_route(p, x, w->w_router, sh ? w->sh_gate_w : nullptr, ids, tw, sh ? L.sl : nullptr, L.stage, s,
+                     small ? &d : nullptr)) != MOE_OK)
     return st;
-  if ((st = hip_status(moe::launch_dispatch(ids, (int)p->T, (int)p->E, (int)p->k, L.offsets, L.sorted, L.pos,
-                                            static_cast<int32_t*>(L.stage), s, /*distinct=*/true))) != MOE_OK)
+  if (!small && (st = hip_status(moe::launch_dispatch(ids, (int)p->T, (int)p->E, (int)p->k, L.offsets, L.sorted,
+                                                      L.pos, static_cast<int32_t*>(L.stage), s,
+                                                      /*distinct=*/true))) != MOE_OK)
     return st;
   if ((st = do_ffn(p, w, x, L.offsets, L.sorted, L.y, sh ? L.y_sh : nullptr, L.stage, s)) != MOE_OK) return st;
   return hip_status(moe::launch_combine(L.y, L.pos, tw, sh ? L.y_sh : nullptr, sh ? L.sl : nullptr, out, (int)p->T,

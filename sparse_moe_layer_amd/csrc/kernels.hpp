@@ -14,6 +14,9 @@ constexpr int kGemmBM = 128;
 constexpr int kGemmBigBM = 256;
 constexpr int kStreamBM = 16;
 constexpr int kMaxExperts = 1024;
+// Batches of at most this many tokens route and dispatch in one workgroup
+// (a wave per token).
+constexpr int kSmallBatch = 16;
 // plan ints ahead of the work lists: [0] m-tiles, [1] stream m-blocks,
 // [2] / [3] where the shared expert's m-tiles / m-blocks begin, then the
 // fused kernel's claim counters: kPlanCounters + (launch * 2 + phase - 1) * 8,
@@ -71,10 +74,13 @@ hipError_t launch_router_logits_bf16(const void* x, const void* w_router, const 
                                      bool gated_residual = false);
 // nsplit = router_stream_split(H) K chunks, each its own partial logits.
 int router_stream_split(int H);
+// zero_word (may be null): an int the launch sets to zero for the kernel
+// that follows it (the small-batch top-k counter).
 hipError_t launch_router_stream(const void* x, const void* w_router, const void* w_sg, float* logits, int T,
-                                int H, int E, int nsplit, hipStream_t s);
+                                int H, int E, int nsplit, hipStream_t s, int32_t* zero_word = nullptr);
 hipError_t launch_router_logits_f32(const float* x, const float* w_router, const float* w_sg,
-                                    float* logits, int T, int H, int E, hipStream_t s);
+                                    float* logits, int T, int H, int E, hipStream_t s,
+                                    int32_t* zero_word = nullptr);
 // page: round the logits to bf16 before the top-k and the mixing weights to
 // bf16 after renormalising (the page's routing numerics for bf16 layers).
 hipError_t launch_topk(const float* partial, int nsplit, int ldl, int T, int E, int k, int has_sg, bool page,
@@ -82,6 +88,12 @@ hipError_t launch_topk(const float* partial, int nsplit, int ldl, int T, int E, 
 size_t dispatch_ws_ints(int64_t T, int64_t E);
 // distinct: the ids come from the router, which never repeats an expert
 // within a token (skips the per-token check for repeats).
+// Top-k and dispatch in one kernel for 1 <= T <= kSmallBatch (same outputs
+// as launch_topk followed by launch_dispatch).  counter: one int, zero at
+// launch (the router launch zeroes it), left at zero.
+hipError_t launch_topk_dispatch_small(const float* partial, int nsplit, int ldl, int T, int E, int k, int has_sg,
+                                     bool page, int32_t* ids, float* w, float* shared_logit, int32_t* offsets,
+                                     int32_t* sorted, int32_t* pos, int32_t* counter, hipStream_t s);
 hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* offsets,
                            int32_t* sorted, int32_t* pos, int32_t* ws, hipStream_t s, bool distinct = false);
 // Groups of more than stream_rows rows (and none with MOE_FLAG_FORCE_STREAM,

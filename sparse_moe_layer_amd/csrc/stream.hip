@@ -150,7 +150,9 @@ __global__ __launch_bounds__(RW * 64) void router_stream_kernel(const bf16* __re
                                                                 const bf16* __restrict__ wr,
                                                                 const bf16* __restrict__ wsg,
                                                                 float* __restrict__ logits, int T, int H, int E,
-                                                                int N, int kchunk) {
+                                                                int N, int kchunk, int32_t* zero_word) {
+  // a word the next kernel in the chain needs at zero (or null)
+  if (zero_word && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *zero_word = 0;
   __shared__ f32x4 part[RW][64];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -206,14 +208,14 @@ int router_stream_split(int H) {
 }
 
 hipError_t launch_router_stream(const void* x, const void* w_router, const void* w_sg, float* logits, int T, int H,
-                                int E, int nsplit, hipStream_t s) {
+                                int E, int nsplit, hipStream_t s, int32_t* zero_word) {
   const int N = E + (w_sg ? 1 : 0);
   int kchunk = (H + RW * nsplit - 1) / (RW * nsplit);
   kchunk = (kchunk + KSTEP - 1) / KSTEP * KSTEP;
   router_stream_kernel<<<dim3((N + 15) / 16, nsplit), RW * 64, 0, s>>>(reinterpret_cast<const bf16*>(x),
                                                          reinterpret_cast<const bf16*>(w_router),
                                                          reinterpret_cast<const bf16*>(w_sg), logits, T, H, E, N,
-                                                         kchunk);
+                                                         kchunk, zero_word);
   return hipGetLastError();
 }
 

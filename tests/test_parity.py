@@ -74,7 +74,8 @@ def run_stages(p, flags=0):
                        y2.view(torch.int16) if y2.dtype == torch.bfloat16 else y2), "split GEMM phases differ"
     if sh:
         assert torch.equal(ysh.float(), y2_sh.float()), "split GEMM phases differ (shared)"
-    # the one-call layer runs the same kernels: same bits as the stage calls
+    # the one-call layer gives the same bits as the stage calls (a small
+    # batch's top-k and dispatch run as one kernel there)
     assert torch.equal(ids2, ids) and torch.equal(w2, w), "layer call routing differs"
     assert torch.equal(out2.float(), out.float()), "layer call output differs"
     return dict(ids=f(ids), w=f(w), sl=f(sl), offsets=f(offs), sorted=f(sa), pos=f(pos), y=f(y), ysh=f(ysh),
@@ -320,6 +321,18 @@ def test_decode_batch_max_experts():
     p = gpu_problem(cfg, 16)
     g = run_stages(p)
     assert np.count_nonzero(np.diff(g["offsets"])[768:]) > 0  # touched groups in the last chunk
+    check(p, g)
+
+
+@pytest.mark.parametrize("T,E,k,H,Is", [(1, 40, 3, 256, 0), (7, 100, 10, 512, 64), (16, 64, 64, 128, 128),
+                                         (16, 512, 10, 136, 64), (12, 1000, 8, 2560, 640)])
+def test_small_batch_fused_route_and_dispatch(T, E, k, H, Is):
+    # T <= 16: the layer call's top-k and dispatch run as one kernel (k = 64
+    # gives R = 1024 assignments, the most it takes); same bits as the
+    # separate top-k and dispatch kernels of the stage calls
+    cfg = CONFIGS["flash_decode"].with_(name=f"small_T{T}_E{E}_k{k}", T=T, H=H, E=E, k=k, I=64, I_shared=Is)
+    p = gpu_problem(cfg, 21 + T)
+    g = run_stages(p)
     check(p, g)
 
 
