@@ -108,7 +108,7 @@ def stream_ceiling(lib, stream, nbytes=4 << 30, launches=20):
 
 def kernel_source_sha():
     h = hashlib.sha256()
-    for f in ("gemm.hip", "gemm_dma.hip", "stream.hip", "common.hpp"):
+    for f in ("gemm.hip", "gemm_dma.hip", "stream.hip", "stream_item.hpp", "common.hpp", "kernels.hpp"):
         h.update(open(os.path.join(ROOT, "sparse_moe_layer_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

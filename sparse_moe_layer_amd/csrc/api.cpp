@@ -7,6 +7,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.hpp"
 
@@ -249,8 +250,53 @@ bool use_big_tiles(const moe_problem* p, const FfnArgs& a) {
   return p->T * p->k >= (a.fp8 ? 32 : 128) * p->E;
 }
 
+// A second stream per device (default priority) and two events, so that
+// the MFMA-bound tile launches and the HBM-bound streaming launches of one
+// FFN call run side by side: fork after the plan kernel, join before the
+// call returns.  Created on first use; a device where that fails runs the
+// launches in order on the caller's stream.  The mutex keeps each fork's
+// record/wait pairs and the launches between them from interleaving with
+// another host thread's.
+struct Aux {
+  hipStream_t s2 = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+constexpr int kMaxDevices = 64;
+Aux g_aux[kMaxDevices];
+std::mutex g_aux_init;
+
+Aux* aux_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_aux_init);
+  Aux& x = g_aux[dev];
+  if (!x.s2) {
+    hipStream_t st = nullptr;
+    hipEvent_t a = nullptr, b = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
+      if (a) (void)hipEventDestroy(a);
+      (void)hipStreamDestroy(st);
+      return nullptr;
+    }
+    x.fork = a;
+    x.join = b;
+    x.s2 = st;
+  }
+  return &x;
+}
+
+// Workgroups of the persistent tile grid left to a streaming launch that
+// runs beside it (4 per XCD): the tiles are partly bound by the chip's
+// power, so they lose less than the CUs' share, and the streams' HBM reads
+// overlap them.
+constexpr int kStreamReserve = 32;
+
 // phases: bit 0 gate/up, bit 1 down.  The plan kernel runs first (bf16/fp8).
-moe_status run_ffn(const moe_problem* p, FfnArgs& a, int phases, void* plan_ws, hipStream_t s) {
+// fork_ok: the streaming launches may run on the device's second stream.
+moe_status run_ffn(const moe_problem* p, FfnArgs& a, int phases, void* plan_ws, hipStream_t s, bool fork_ok) {
   if (p->act_dtype == MOE_F32) return hip_status(moe::launch_ffn_f32(a, phases, s));
   int32_t* plan = static_cast<int32_t*>(plan_ws);
   const bool big = use_big_tiles(p, a);
@@ -274,19 +320,38 @@ moe_status run_ffn(const moe_problem* p, FfnArgs& a, int phases, void* plan_ws, 
       return MOE_ERR_HIP;
     moe::ffn_bind_plan(a, plan);
   }
-  for (int phase = 1; phase <= 2; ++phase) {
-    if (!(phases & phase)) continue;
-    if (any_gemm) {
-      const hipError_t e = big ? moe::launch_ffn_gemm_big(a, phase, s) : moe::launch_ffn_gemm(a, phase, s);
-      if (e != hipSuccess) return MOE_ERR_HIP;
+  // the 256-row tiles and the streaming groups side by side
+  Aux* x = (fork_ok && big && any_gemm && any_stream && !self_plan) ? aux_stream() : nullptr;
+  if (!x) {
+    for (int phase = 1; phase <= 2; ++phase) {
+      if (!(phases & phase)) continue;
+      if (any_gemm) {
+        const hipError_t e = big ? moe::launch_ffn_gemm_big(a, phase, s) : moe::launch_ffn_gemm(a, phase, s);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+      }
+      if (any_stream && moe::launch_ffn_stream(a, phase, s, self_plan) != hipSuccess) return MOE_ERR_HIP;
     }
-    if (any_stream && moe::launch_ffn_stream(a, phase, s, self_plan) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
   }
-  return MOE_OK;
+  std::lock_guard<std::mutex> lk(x->mu);
+  if (hipEventRecord(x->fork, s) != hipSuccess || hipStreamWaitEvent(x->s2, x->fork, 0) != hipSuccess)
+    return MOE_ERR_HIP;
+  moe_status st = MOE_OK;
+  for (int phase = 1; phase <= 2 && st == MOE_OK; ++phase) {
+    if (!(phases & phase)) continue;
+    if (moe::launch_ffn_gemm_big(a, phase, s, kStreamReserve) != hipSuccess ||
+        moe::launch_ffn_stream(a, phase, x->s2, false) != hipSuccess)
+      st = MOE_ERR_HIP;
+  }
+  // the join is recorded even after a failed launch, so the caller's stream
+  // never runs ahead of the second stream's work
+  if (hipEventRecord(x->join, x->s2) != hipSuccess || hipStreamWaitEvent(s, x->join, 0) != hipSuccess)
+    return MOE_ERR_HIP;
+  return st;
 }
 
 moe_status do_ffn(const moe_problem* p, const moe_weights* w, const void* x, const int32_t* offsets,
-                  const int32_t* sorted, void* y, void* y_sh, void* stage, hipStream_t s) {
+                  const int32_t* sorted, void* y, void* y_sh, void* stage, hipStream_t s, bool fork_ok = true) {
   FfnArgs a = ffn_args(p, w, x, offsets, sorted, y_sh != nullptr);
   a.y = y;
   a.y_sh = a.Is ? y_sh : nullptr;
@@ -295,7 +360,7 @@ moe_status do_ffn(const moe_problem* p, const moe_weights* w, const void* x, con
   const size_t plan_bytes = up(moe::ffn_plan_ints(p->T, p->E, p->k, a.Is > 0) * 4);
   a.h = b + plan_bytes;
   a.h_sh = b + plan_bytes + up((size_t)p->T * p->k * p->I * act_bytes(p));
-  return run_ffn(p, a, 3, b, s);
+  return run_ffn(p, a, 3, b, s, fork_ok);
 }
 
 }  // namespace
@@ -313,7 +378,7 @@ moe_status layer_forward_checks(const moe_problem* p, const moe_weights* w, cons
 }
 
 moe_status layer_forward_run(const moe_problem* p, const moe_weights* w, const void* x, void* out,
-                             int32_t* topk_ids, float* topk_w, void* ws, hipStream_t s) {
+                             int32_t* topk_ids, float* topk_w, void* ws, hipStream_t s, bool fork_ok) {
   moe_status st;
   LayerWs L = layer_layout(p, ws);
   int32_t* ids = topk_ids ? topk_ids : L.ids;
@@ -329,7 +394,8 @@ moe_status layer_forward_run(const moe_problem* p, const moe_weights* w, const v
                                                       L.pos, static_cast<int32_t*>(L.stage), s,
                                                       /*distinct=*/true))) != MOE_OK)
     return st;
-  if ((st = do_ffn(p, w, x, L.offsets, L.sorted, L.y, sh ? L.y_sh : nullptr, L.stage, s)) != MOE_OK) return st;
+  if ((st = do_ffn(p, w, x, L.offsets, L.sorted, L.y, sh ? L.y_sh : nullptr, L.stage, s, fork_ok)) != MOE_OK)
+    return st;
   return hip_status(moe::launch_combine(L.y, L.pos, tw, sh ? L.y_sh : nullptr, sh ? L.sl : nullptr, out, (int)p->T,
                                         (int)p->H, (int)p->k, p->act_dtype == MOE_F32 ? 1 : 0, s));
 }
@@ -410,7 +476,7 @@ moe_status moe_expert_gate_up(const moe_problem* p, const moe_weights* w, const 
   FfnArgs a = ffn_args(p, w, x, expert_offsets, sorted_assign, h_shared != nullptr);
   a.h = h;
   a.h_sh = a.Is ? h_shared : nullptr;
-  return run_ffn(p, a, 1, ws, (hipStream_t)stream);
+  return run_ffn(p, a, 1, ws, (hipStream_t)stream, true);
 }
 
 moe_status moe_expert_down(const moe_problem* p, const moe_weights* w, const int32_t* expert_offsets,
@@ -429,7 +495,7 @@ moe_status moe_expert_down(const moe_problem* p, const moe_weights* w, const int
   a.h_sh = a.Is ? const_cast<void*>(h_shared) : nullptr;
   a.y = y;
   a.y_sh = a.Is ? y_shared : nullptr;
-  return run_ffn(p, a, 2, ws, (hipStream_t)stream);
+  return run_ffn(p, a, 2, ws, (hipStream_t)stream, true);
 }
 
 moe_status moe_combine(const moe_problem* p, const void* y, const int32_t* assign_pos, const float* topk_w,

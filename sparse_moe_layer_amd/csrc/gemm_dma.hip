@@ -512,7 +512,8 @@ __device__ __forceinline__ void run_tile(const FfnArgs& f, int mt, int nt, bf16*
 // launch.
 template <class C, int MODE>
 __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void ffn_tiles_kernel(FfnArgs f, int n_tiles_n, int super,
-                                                                           int tb, int te, int32_t* counters) {
+                                                                           int tb, int te, int32_t* counters,
+                                                                           int reserve) {
   __shared__ __attribute__((aligned(1024))) bf16 s0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) bf16 s1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) bf16 s2[C::S > 2 ? C::STAGE : 8];
@@ -532,7 +533,11 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_EU) void ffn_tiles_kernel(FfnAr
   const int mt_first = tb == kPlanStart ? 0 : f.plan[tb];
   const int MT = f.plan[te] - mt_first;
   const int total = MT * n_tiles_n;
-  const int G = gridDim.x;
+  // With streaming work in the plan and a streaming launch running beside
+  // this one, the last `reserve` workgroups (a multiple of 8, so every XCD
+  // gives up the same number) leave at once and free their CUs for it.
+  const int G = reserve > 0 && f.plan[kPlanBlocks] > 0 ? (int)gridDim.x - reserve : (int)gridDim.x;
+  if ((int)blockIdx.x >= G) return;
   const int chunk = G >> 3;
   auto xcd_tiles = [&](int x) {
     return (total / G) * chunk + min(max(total % G - x * chunk, 0), chunk);
@@ -586,7 +591,7 @@ int cu_count() {
 // One launch of a phase over the m-tiles [plan[tb], plan[te]), with the given
 // block of eight claim counters.
 template <class C>
-hipError_t launch(const FfnArgs& a, int phase, hipStream_t s, int tb, int te, int ctr_block) {
+hipError_t launch(const FfnArgs& a, int phase, hipStream_t s, int tb, int te, int ctr_block, int reserve) {
   const int wide = a.I > a.Is ? a.I : a.Is;
   const int ntn = phase == 1 ? (wide + C::BN / 2 - 1) / (C::BN / 2) : (a.H + C::BN - 1) / C::BN;
   const int grid = (cu_count() * C::WG_PER_CU + 7) / 8 * 8;  // resident workgroups, a multiple of 8 XCDs
@@ -596,8 +601,9 @@ hipError_t launch(const FfnArgs& a, int phase, hipStream_t s, int tb, int te, in
   // measured slower on the 8192-token skewed layer.)
   const int super = 8;
   int32_t* ctr = const_cast<int32_t*>(a.plan) + kPlanCounters + (ctr_block * 2 + phase - 1) * 8;
-  if (phase == 1) ffn_tiles_kernel<C, 1><<<grid, C::NT, 0, s>>>(a, ntn, super, tb, te, ctr);
-  else ffn_tiles_kernel<C, 2><<<grid, C::NT, 0, s>>>(a, ntn, super, tb, te, ctr);
+  reserve = reserve < grid - 8 ? reserve / 8 * 8 : 0;
+  if (phase == 1) ffn_tiles_kernel<C, 1><<<grid, C::NT, 0, s>>>(a, ntn, super, tb, te, ctr, reserve);
+  else ffn_tiles_kernel<C, 2><<<grid, C::NT, 0, s>>>(a, ntn, super, tb, te, ctr, reserve);
   return hipGetLastError();
 }
 
@@ -611,12 +617,12 @@ bool ffn_dma_supported(const FfnArgs& a) {
   return a.H % k == 0 && a.I % k == 0;
 }
 
-hipError_t launch_ffn_gemm_big(const FfnArgs& a, int phase, hipStream_t s) {
-  if (!a.fp8) return launch<BigCfg>(a, phase, s, kPlanStart, kPlanTiles, 0);
+hipError_t launch_ffn_gemm_big(const FfnArgs& a, int phase, hipStream_t s, int reserve) {
+  if (!a.fp8) return launch<BigCfg>(a, phase, s, kPlanStart, kPlanTiles, 0, reserve);
   // fp8 layers: the routed groups' tiles decode codes; the shared expert's
   // [plan[2], plan[0]) tiles are bf16
-  hipError_t e = launch<BigCfg8>(a, phase, s, kPlanStart, kPlanRoutedTiles, 0);
-  if (e == hipSuccess && a.Is > 0) e = launch<BigCfg>(a, phase, s, kPlanRoutedTiles, kPlanTiles, 1);
+  hipError_t e = launch<BigCfg8>(a, phase, s, kPlanStart, kPlanRoutedTiles, 0, reserve);
+  if (e == hipSuccess && a.Is > 0) e = launch<BigCfg>(a, phase, s, kPlanRoutedTiles, kPlanTiles, 1, reserve);
   return e;
 }
 

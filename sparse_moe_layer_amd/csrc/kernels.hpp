@@ -108,7 +108,10 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int phase, hipStream_t s);
 // hundreds of rows per expert (ragged last m-tiles included; bf16 weights
 // need H, I and I_shared multiples of 32).
 bool ffn_dma_supported(const FfnArgs& a);
-hipError_t launch_ffn_gemm_big(const FfnArgs& a, int phase, hipStream_t s);
+// reserve: workgroups of the persistent grid that leave at once when the
+// plan has streaming blocks, so that a streaming launch on another stream
+// gets their CUs (0: the whole grid takes tiles).
+hipError_t launch_ffn_gemm_big(const FfnArgs& a, int phase, hipStream_t s, int reserve = 0);
 // phase 1 gate/up, 2 down.  self_plan: T <= kStreamMaxRows and no plan kernel
 // ran; the kernels list the touched groups from the offsets themselves.
 hipError_t launch_ffn_stream(const FfnArgs& a, int phase, hipStream_t s, bool self_plan = false);
@@ -124,10 +127,12 @@ hipError_t launch_combine_gr_write(const void* y, const int32_t* pos, const floa
 
 // The whole layer behind moe_layer_forward: argument checks (MOE_OK also
 // for an empty batch, which needs no run), then the launches on workspace
-// ws of moe_workspace_bytes(p) bytes (no workspace check).
+// ws of moe_workspace_bytes(p) bytes (no workspace check).  fork_ok: the
+// FFN's streaming launches may run on the device's second stream (created
+// on first use); false keeps every launch on s.
 moe_status layer_forward_checks(const moe_problem* p, const moe_weights* w, const void* x, const void* out);
 moe_status layer_forward_run(const moe_problem* p, const moe_weights* w, const void* x, void* out,
-                             int32_t* topk_ids, float* topk_w, void* ws, hipStream_t s);
+                             int32_t* topk_ids, float* topk_w, void* ws, hipStream_t s, bool fork_ok = true);
 
 // Gated residual read / write (bf16).
 // Expert-weight audit (bf16): histograms of the bit patterns per slice and

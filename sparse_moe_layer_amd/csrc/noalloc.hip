@@ -49,5 +49,6 @@ extern "C" moe_status moe_layer_forward_noalloc(const moe_problem* p, const moe_
   if (moe_workspace_bytes(p) > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
   void* ws = nullptr;
   if (moe::device_scratch(&ws) != hipSuccess) return MOE_ERR_HIP;
-  return moe::layer_forward_run(p, w, x, out, topk_ids, topk_w, ws, (hipStream_t)stream);
+  // every launch on the caller's stream: no second stream is created here
+  return moe::layer_forward_run(p, w, x, out, topk_ids, topk_w, ws, (hipStream_t)stream, /*fork_ok=*/false);
 }
