@@ -17,11 +17,22 @@
  * Conventions for every entry point
  * ---------------------------------
  *  - Pointers are device pointers (hipMalloc'd or equivalent) owned by the
- *    caller; the library never allocates, frees or synchronises.  Tensors are
- *    row-major and contiguous, except routed expert matrices, which may sit
- *    at any element stride from one expert to the next (moe_weights).
+ *    caller; the library never allocates or frees device memory for them and
+ *    never synchronises.  Tensors are row-major and contiguous, except routed
+ *    expert matrices, which may sit at any element stride from one expert to
+ *    the next (moe_weights).
  *  - `stream` is a hipStream_t (NULL = the default stream).  All work is
- *    enqueued on it asynchronously; no host<->device copy happens inside a call.
+ *    enqueued asynchronously and ordered after earlier work on it; no
+ *    host<->device copy happens inside a call.  When an expert FFN call has
+ *    both 256-row GEMM tiles and streamed groups, the streamed groups run on
+ *    a second stream of the library's (one per device, default priority,
+ *    created with two events on the first such call): forked from `stream`
+ *    after the call's first kernel and joined back into it before the call's
+ *    later work, so to the caller every call is ordered on `stream` alone
+ *    (also under graph capture, where the fork and join become graph edges).
+ *    Host threads that share a device serialise on that second stream's
+ *    enqueue; a thread must not capture a graph while another uses the
+ *    library on the same device.  moe_layer_forward_noalloc never forks.
  *  - `ws`/`ws_bytes` is caller-owned scratch device memory of at least
  *    moe_workspace_bytes(p) bytes, 256-byte aligned.  Its contents on entry
  *    do not matter; it must not be used by anything else until the stream has
