@@ -245,8 +245,9 @@ def test_gemm_tile_kernels(tile):
 
 
 def test_256_row_tiles_with_128_row_remainders():
-    # skewed load in 256-row tiling: each group's last m-tile of at most 128
-    # rows runs in the 128-row kernel, every other m-tile in the 256-row one
+    # skewed load in 256-row tiling: every m-tile of a group, its ragged last
+    # one included, runs in the persistent 256-row kernel; the streamed
+    # groups run beside it on the library's second stream
     cfg = CONFIGS["max_prefill"].with_(name="two_lists", T=1536, H=256, E=16, k=2, I=128, I_shared=64,
                                        zipf_s=1.1)
     p = gpu_problem(cfg, 13)
