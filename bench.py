@@ -9,7 +9,7 @@ GEMM, weighted combine with the gated shared expert, as one moe_layer_forward
 call on the current stream.  The headline workload (default: the 2.4T-shape
 prefill layer, 8192 tokens) is timed as K steps back to back between two
 device synchronisations; `value` is its tokens/s.  K more steps are timed one
-by one with HIP events after a 512 MiB device fill that evicts the caches
+by one with HIP events after a 1 GiB read pass that evicts the caches
 (`cold_ms`: median, p10, p90), and K more stage by stage through the five
 entry points with HIP events between them (`stages_ms`).
 
@@ -413,9 +413,10 @@ def pct(vals, q):
 def measure(lib, acc, cfg, args, dev, stream, flags, full):
     """One workload: the contract's timed region (K moe_layer_forward calls
     back to back between two device synchronisations), then K steps each
-    timed alone with HIP events on the launch stream after a 512 MiB device
-    fill that evicts the L2s and the 256 MB memory-side cache (median, p10,
-    p90), then K steps stage by stage with events between the entry points.
+    timed alone with HIP events on the launch stream after a 1 GiB read pass
+    that evicts the L2s and the 256 MB memory-side cache with clean lines
+    (median, p10, p90), then K steps stage by stage with events between the
+    entry points.
     full: also the roofline object and the widened rows."""
     import torch
     from sparse_moe_layer_amd.tensors import structs
@@ -440,7 +441,11 @@ def measure(lib, acc, cfg, args, dev, stream, flags, full):
     y = torch.empty((R, H), dtype=adt, device=dev)
     y_sh = torch.empty((T, H), dtype=adt, device=dev) if sh else None
     out = torch.empty((T, H), dtype=adt, device=dev)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # cache eviction between cold steps: one read pass over 1 GiB (twice the
+    # 256 MB memory-side cache and every L2), by the library's read probe, so
+    # the evicting lines are clean and leave no write-back behind them
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    flush_sink = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def layer():
         lib.moe_layer_forward(P, W, prob.x, out, None, None, ws, stream)
@@ -472,7 +477,7 @@ def measure(lib, acc, cfg, args, dev, stream, flags, full):
     # each step alone after evicting the caches, HIP events around the call
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.steps):
-        flush.fill_(i & 255)
+        lib.moe_hbm_read_probe(flush, flush_sink, stream)
         evs[i][0].record(stream)
         layer()
         evs[i][1].record(stream)
