@@ -86,8 +86,11 @@ typedef enum {
  *       section "What FP8 actually quantizes"); scale_block must be 128 and
  *       H, I multiples of 128.
  * Limits: 1 <= E <= 1024, 1 <= k <= min(E, 64), H and I multiples of 8 (bf16)
- * or of 4 (f32), I_shared 0 or a multiple of 8; every tensor below 2^31
- * elements (T*H, T*k*H, T*k*I, T*I_shared, I*H, I_shared*H).                 */
+ * or of 4 (f32), I_shared 0 or a multiple of 8; T*k < 2^31; the tensors the
+ * kernels address with 32-bit element offsets below 2^31 elements (T*H,
+ * T*k*I, T*I_shared, I*H, I_shared*H).  The per-assignment outputs y [T*k, H]
+ * are addressed with 64-bit offsets and may exceed 2^31 elements (e.g. a
+ * 32768-token chunk of the 2.4T shape).                                       */
 typedef struct {
   int64_t T;          /* tokens                                               */
   int64_t H;          /* hidden width                                          */

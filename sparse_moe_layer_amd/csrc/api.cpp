@@ -109,10 +109,11 @@ moe_status check_problem(const moe_problem* p) {
     return MOE_ERR_SHAPE;
   if (p->T > (int64_t)INT32_MAX / p->k || p->H > (1 << 24) || p->I > (1 << 24) || p->I_shared > (1 << 24))
     return MOE_ERR_SHAPE;
-  // kernels address rows with 32-bit element offsets inside one tensor
+  // kernels address x, h, h_sh and one expert's matrices with 32-bit element
+  // offsets; y [R, H] rows go through 64-bit offsets
   const int64_t lim = (int64_t)1 << 31;
   const int64_t R = p->T * p->k;
-  if (p->T * p->H >= lim || R * p->I >= lim || R * p->H >= lim || p->T * p->I_shared >= lim || p->I * p->H >= lim ||
+  if (p->T * p->H >= lim || R * p->I >= lim || p->T * p->I_shared >= lim || p->I * p->H >= lim ||
       p->I_shared * p->H >= lim)
     return MOE_ERR_UNSUPPORTED;
   const bool f32 = p->act_dtype == MOE_F32 && p->w_dtype == MOE_F32;

@@ -79,7 +79,9 @@ OK = _lib.MOE_OK
     (dict(flags=21), OK),
     (dict(flags=32), _lib.MOE_ERR_UNSUPPORTED),
     (dict(T=2 ** 31 // 4), _lib.MOE_ERR_SHAPE),
-    (dict(T=2 ** 24, H=256), _lib.MOE_ERR_UNSUPPORTED),  # T*k*H elements >= 2^31
+    (dict(T=2 ** 24, H=256), _lib.MOE_ERR_UNSUPPORTED),  # T*H elements >= 2^31 (x)
+    (dict(T=2 ** 20, k=16, I=256), _lib.MOE_ERR_UNSUPPORTED),  # T*k*I elements >= 2^31 (h)
+    (dict(T=2 ** 21, H=512), OK),  # T*k*H = 2^32: y takes 64-bit offsets
 ])
 def test_validate(kw, status):
     base = dict(T=64, H=256, E=16, k=4, I=128, I_shared=0, act="bf16", wdt="bf16", scale_block=128, flags=0)

@@ -337,6 +337,57 @@ def test_small_batch_fused_route_and_dispatch(T, E, k, H, Is):
     check(p, g)
 
 
+@pytest.mark.timeout(400)
+def test_per_assignment_outputs_beyond_2_31_elements():
+    # R*H > 2^31: the rows of y past element 2^31 (64-bit offsets in the
+    # GEMM epilogues and the combine) checked against the oracle
+    cfg = CONFIGS["max_prefill"].with_(name="big_y", T=32800, H=8192, E=16, k=8, I=128, I_shared=128, zipf_s=0.0)
+    T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
+    R = T * k
+    assert R * H > 2 ** 31
+    p = gpu_problem(cfg, 51)
+    P, W = structs(p)
+    ws = lib.workspace(P)
+    dev = p.x.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    sl = torch.empty(T, dtype=torch.float32, device=dev)
+    lib.moe_route(P, p.x, p.w_router, p.sh_gate_w, ids, w, sl, ws)
+    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sa = torch.empty(R, dtype=torch.int32, device=dev)
+    pos = torch.empty(R, dtype=torch.int32, device=dev)
+    lib.moe_dispatch(P, ids, offs, sa, pos, ws)
+    y = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    ysh = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    lib.moe_expert_ffn(P, W, p.x, offs, sa, y, ysh, ws)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    lib.moe_combine(P, y, pos, w, ysh, sl, out)
+    out2 = torch.empty_like(out)
+    lib.moe_layer_forward(P, W, p.x, out2, None, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    # tokens with an assignment in y rows at or past element 2^31, and the ends
+    first_far = 2 ** 31 // H
+    far_tok = torch.unique(sa[first_far:].long() // k).cpu().numpy()
+    rng = np.random.default_rng(5)
+    toks = np.union1d(rng.choice(far_tok, min(8, len(far_tok)), replace=False), [0, T - 1])
+    print(f"[parity] big_y: {len(far_tok)} tokens with rows past 2^31 elements; checking {len(toks)}", flush=True)
+    r = adapter.forward(p, toks)
+    assert np.array_equal(ids.cpu().numpy(), r["ids"])
+    assert np.array_equal(offs.cpu().numpy(), r["offsets"])
+    assert np.array_equal(sa.cpu().numpy(), r["sorted_assign"])
+    assert np.array_equal(pos.cpu().numpy(), r["assign_pos"])
+    rows = pos.cpu().numpy()[(toks[:, None] * k + np.arange(k)[None, :]).reshape(-1)]
+    assert (rows >= first_far).any()
+    y_s = y[torch.from_numpy(rows).long().to(dev)].float().cpu().numpy().reshape(len(toks), k, H)
+    e_y = rel_err(y_s, r["y"])
+    e_out = rel_err(out[torch.from_numpy(toks).long().to(dev)].float().cpu().numpy(), r["out"])
+    print(f"[parity] big_y: y {e_y:.2e} out {e_out:.2e}", flush=True)
+    assert e_y <= tol(cfg) and e_out <= tol(cfg)
+    del y, ysh, out, out2, ws, p
+    torch.cuda.empty_cache()
+
+
 def test_decode_batch_forced_gemm():
     # T <= 16 with the GEMM path forced: the plan kernel runs, no group streams
     cfg = CONFIGS["flash_decode"].with_(name="decode_gemm", T=16, H=256, E=32, k=4, I=128, I_shared=64)
