@@ -64,6 +64,9 @@ def parse():
                     help="skip the gated-residual and weight-audit rows (kernel traces of the layer alone)")
     ap.add_argument("--stream-ceiling", action="store_true",
                     help="only time moe_hbm_read_probe (one pass over 4 GiB, 16 B per lane) and print its rate")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only time moe_mfma_pipe_probe's variants, and the 256x256 tile kernel and hipBLASLt on "
+                         "one dense 8192x4096x8192 gate/up product (zero and random operands), and print them")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scale factor for HBM byte counters)")
     return ap.parse_args()
@@ -104,6 +107,81 @@ def stream_ceiling(lib, stream, nbytes=4 << 30, launches=20):
     return {"kernel": "hbm_read_probe_kernel", "bytes": nbytes, "launches": launches,
             "ms_median": round(pct(ms, 0.5), 4), "gbs_median": round(pct(gbs, 0.5), 1),
             "gbs_best": round(max(gbs), 1), "frac_of_8tbs": round(pct(gbs, 0.5) / 8000.0, 4)}
+
+
+def mfma_ceiling(lib, stream):
+    """What the tile kernel's pipeline costs the MFMA rate, and where it stands
+    against the vendor GEMM on one dense product.
+
+    - probe: moe_mfma_pipe_probe's variants (the tile kernel's per-step work
+      taken apart, zero operands), each timed over 5 launches of 20000 steps
+      with HIP events on the stream it is launched on;
+    - dense: the gate/up product of one expert holding all 8192 rows (H 8192,
+      I 2048: an 8192 x 4096 x 8192 GEMM) through moe_expert_gate_up with
+      256-row tiles, and torch.matmul (hipBLASLt) on the same shape, each
+      launched back to back for about a second so that the clock settles, with
+      the shader clock sampled meanwhile; once on zero operands (the clock stays
+      near its maximum) and once on random ones (the chip's power limit lowers
+      it)."""
+    import torch
+    res = {"probe": {}, "dense": {}}
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    src = torch.zeros(4 << 20, dtype=torch.uint8, device="cuda")  # 128 slots of 32 KB: stays in L2
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    steps = 20000
+    names = ["mfma only", "+ fragment reads", "+ barrier per step", "+ direct loads", "direct loads, no barrier"]
+    for v, name in enumerate(names):
+        with torch.cuda.stream(stream):
+            lib.moe_mfma_pipe_probe(v, steps // 10, src, sink, stream)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(5):
+                lib.moe_mfma_pipe_probe(v, steps, src, sink, stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / 5
+        tf = cus * 8 * steps * 16 * 32768 / (ms * 1e-3) / 1e12
+        res["probe"][name] = {"variant": v, "ms": round(ms, 4), "tflops": round(tf, 1),
+                              "frac_of_2500": round(tf / 2500.0, 4)}
+    T, H, I = 8192, 8192, 2048
+    flops = 4.0 * T * H * I
+    for data in ("zeros", "random"):
+        g = torch.Generator(device="cuda").manual_seed(0)
+        x = torch.randn(T, H, device="cuda", generator=g).to(torch.bfloat16)
+        wg = (torch.randn(1, I, H, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        wu = (torch.randn(1, I, H, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        wd = (torch.randn(1, H, I, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        if data == "zeros":
+            for t in (x, wg, wu, wd):
+                t.zero_()
+        P = lib.problem(T, H, 1, 1, I, 0, "bf16", "bf16", 128, lib.MOE_FLAG_FORCE_GEMM | lib.MOE_FLAG_GEMM_TILE_256)
+        W = lib.weights(None, wg, wu, wd, None, None, None)
+        ws = lib.workspace(P)
+        offs = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+        sa = torch.arange(T, dtype=torch.int32, device="cuda")
+        h = torch.empty(T, I, dtype=torch.bfloat16, device="cuda")
+        wgu = torch.cat([wg[0], wu[0]], 0).contiguous()
+        runs = {"tile_kernel_gate_up": lambda: lib.moe_expert_gate_up(P, W, x, offs, sa, h, None, ws, stream),
+                "hipblaslt_matmul": lambda: torch.matmul(x, wgu.T)}
+        for name, fn in runs.items():
+            with torch.cuda.stream(stream):
+                for _ in range(5):
+                    fn()
+                torch.cuda.synchronize()
+                n = 2000
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                with ClockSampler(0.01) as clk:
+                    a.record(stream)
+                    for _ in range(n):
+                        fn()
+                    b.record(stream)
+                    torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / n
+            res["dense"][f"{name}_{data}"] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                                             "sclk": clk.summary()}
+        del x, wg, wu, wd, h, wgu, ws
+        torch.cuda.empty_cache()
+    return res
 
 
 def kernel_source_sha():
@@ -574,6 +652,9 @@ def main():
     print(f"[bench] {torch.cuda.get_device_name(dev)}", file=sys.stderr, flush=True)
     if args.stream_ceiling:
         print(json.dumps({"stream_ceiling": stream_ceiling(lib, torch.cuda.current_stream())}), flush=True)
+        return
+    if args.mfma_ceiling:
+        print(json.dumps({"mfma_ceiling": mfma_ceiling(lib, torch.cuda.current_stream())}), flush=True)
         return
     flags = {"auto": 0, "128": lib.MOE_FLAG_GEMM_TILE_128, "256": lib.MOE_FLAG_GEMM_TILE_256}[args.gemm_tile]
     flags |= {"auto": 0, "gemm": lib.MOE_FLAG_FORCE_GEMM, "stream": lib.MOE_FLAG_FORCE_STREAM}[args.path]

@@ -117,6 +117,12 @@ def moe_hbm_read_probe(src, sink, stream=None):
            "moe_hbm_read_probe")
 
 
+def moe_mfma_pipe_probe(variant: int, steps: int, src, sink, stream=None):
+    nbytes = 0 if src is None else src.numel() * src.element_size()
+    _check(LIB.moe_mfma_pipe_probe(variant, steps, _ptr(src), nbytes, _ptr(sink), _stream(stream)),
+           "moe_mfma_pipe_probe")
+
+
 def moe_layer_forward_noalloc(p, w: moe_weights, x, out, topk_ids, topk_w, stream=None):
     _check(LIB.moe_layer_forward_noalloc(ctypes.byref(p), ctypes.byref(w), _ptr(x), _ptr(out), _ptr(topk_ids),
                                          _ptr(topk_w), _stream(stream)), "moe_layer_forward_noalloc")

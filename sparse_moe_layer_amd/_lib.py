@@ -28,7 +28,7 @@ EXPORTS = ["moe_abi_version", "moe_status_str", "moe_validate", "moe_workspace_b
            "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down", "moe_combine",
            "moe_layer_forward", "moe_gr_workspace_bytes", "moe_gr_read", "moe_gr_write", "moe_combine_gr_write",
            "moe_audit_workspace_bytes", "moe_weight_audit", "moe_layer_forward_noalloc",
-           "moe_hbm_read_probe"]
+           "moe_hbm_read_probe", "moe_mfma_pipe_probe"]
 
 
 class moe_problem(ctypes.Structure):
@@ -77,6 +77,7 @@ def _load():
         "moe_layer_forward": (i32, [P, W, vp, vp, vp, vp, vp, sz, vp]),
         "moe_layer_forward_noalloc": (i32, [P, W, vp, vp, vp, vp, vp]),
         "moe_hbm_read_probe": (i32, [vp, sz, vp, vp]),
+        "moe_mfma_pipe_probe": (i32, [ctypes.c_int32, ctypes.c_int32, vp, sz, vp, vp]),
         "moe_gr_workspace_bytes": (sz, [P, ctypes.c_int64]),
         "moe_gr_read": (i32, [P, G, vp, vp, vp, vp, sz, vp]),
         "moe_gr_write": (i32, [P, vp, vp, vp, vp, vp]),

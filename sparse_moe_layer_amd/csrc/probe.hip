@@ -1,7 +1,22 @@
+// Measurement helpers (not steps of the layer).
+//
 // moe_hbm_read_probe: reads a buffer once with the access the streaming
 // kernels use at their best (16 bytes per lane, whole waves on contiguous
 // runs, several loads in flight per lane) and nothing else, so its rate is
 // the practical HBM read ceiling the streaming rooflines are read against.
+//
+// moe_mfma_pipe_probe: the 256 x 256 tile kernel's per-step work taken apart,
+// to show what each part costs the MFMA rate.  One workgroup of 8 waves per
+// CU (two per SIMD, as in the tile kernel); per step each wave issues 16
+// v_mfma_f32_32x32x16_bf16 on zero operands (no power limit on the clock)
+// into 8 accumulators, and by variant also:
+//   0: nothing else;
+//   1: the tile kernel's fragment reads, 12 ds_read_b128 per step;
+//   2: 1 and one workgroup barrier per step;
+//   3: 2 and the tile kernel's direct loads, 4 global_load_lds of 1 KB per
+//      wave per step (32 KB per workgroup) from an L2-resident buffer, the
+//      barrier preceded by a wait for the loads two steps old;
+//   4: 3 without the barrier (the same loads and waits).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -32,8 +47,110 @@ __global__ __launch_bounds__(kProbeThreads) void hbm_read_probe_kernel(const u32
   if (r == 0x9E3779B9u) sink[0] = r;  // keeps the loads; practically never taken
 }
 
+constexpr int kPipeWaves = 8;
+constexpr int kPipeSlot = 32768;  // bytes one workgroup loads per step
+
+constexpr int pipe_vmcnt(int n) { return 0xF70 | (n & 15) | (((n >> 4) & 3) << 14); }
+
+template <int V>
+__global__ __launch_bounds__(kPipeWaves * 64, 1) void mfma_pipe_probe_kernel(const char* __restrict__ src,
+                                                                             int nslots, int steps, float* sink) {
+  constexpr bool READS = V >= 1, BAR = V == 2 || V == 3, DMA = V >= 3;
+  __shared__ __attribute__((aligned(1024))) char frag[kPipeSlot];
+  __shared__ __attribute__((aligned(1024))) char land[DMA ? 4 : 1][DMA ? kPipeSlot : 16];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kPipeSlot / 4; i += kPipeWaves * 64) reinterpret_cast<int*>(frag)[i] = 0;
+  __syncthreads();
+  f32x16 acc[4][2];
+  bf16x8 a[4], b[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = bf16x8{};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) b[j] = bf16x8{};
+  const int base = lane * 16;
+  for (int s = 0; s < steps; ++s) {
+    if constexpr (DMA) __builtin_amdgcn_s_waitcnt(pipe_vmcnt(8));  // this wave's loads of step s-2 landed
+    if constexpr (BAR) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    if constexpr (DMA) {
+      // slot ((workgroup * 7 + s) mod nslots): 1 KB per wave and load, the
+      // workgroup's four loads per wave covering the 32 KB slot
+      const char* g = src + (int64_t)((blockIdx.x * 7 + s) % nslots) * kPipeSlot + wave * 1024 + lane * 16;
+      char* d = land[s & 3] + wave * 1024;
+#pragma unroll
+      for (int l = 0; l < 4; ++l) __builtin_amdgcn_global_load_lds(g + l * 8192, d + l * 8192, 16, 0, 0);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if constexpr (READS) {
+        // 16 bytes per lane, a 1 KB row block per read; the step moves the
+        // window so the reads stay inside the loop
+        const int w = ((s & 7) << 11) + (ks << 12);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(frag + ((base + i * 1024 + w) & (kPipeSlot - 1)));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          b[j] = *reinterpret_cast<const bf16x8*>(frag + ((base + 16384 + j * 1024 + w) & (kPipeSlot - 1)));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(pipe_vmcnt(0));
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) t += acc[i][j][v];
+  if constexpr (DMA) t += (float)land[0][threadIdx.x & 15];
+  if (t == 1234.5f) sink[0] = t;  // keeps the work; never taken (every operand is zero)
+}
+
 }  // namespace
 }  // namespace moe
+
+extern "C" moe_status moe_mfma_pipe_probe(int32_t variant, int32_t steps, const void* src, size_t src_bytes,
+                                          float* sink, void* stream) {
+  if (!sink) return MOE_ERR_NULL;
+  if (variant < 0 || variant > 4 || steps < 1 || steps > (1 << 24)) return MOE_ERR_SHAPE;
+  int nslots = 1;
+  if (variant >= 3) {
+    if (!src) return MOE_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(src) & 15u) return MOE_ERR_ALIGN;
+    if (src_bytes < (size_t)moe::kPipeSlot || src_bytes % moe::kPipeSlot || src_bytes / moe::kPipeSlot > (1u << 20))
+      return MOE_ERR_SHAPE;
+    nslots = (int)(src_bytes / moe::kPipeSlot);
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return MOE_ERR_HIP;
+  const char* s = static_cast<const char*>(src);
+  hipStream_t st = (hipStream_t)stream;
+  constexpr int nt = moe::kPipeWaves * 64;
+  switch (variant) {
+    case 0: moe::mfma_pipe_probe_kernel<0><<<cus, nt, 0, st>>>(s, nslots, steps, sink); break;
+    case 1: moe::mfma_pipe_probe_kernel<1><<<cus, nt, 0, st>>>(s, nslots, steps, sink); break;
+    case 2: moe::mfma_pipe_probe_kernel<2><<<cus, nt, 0, st>>>(s, nslots, steps, sink); break;
+    case 3: moe::mfma_pipe_probe_kernel<3><<<cus, nt, 0, st>>>(s, nslots, steps, sink); break;
+    default: moe::mfma_pipe_probe_kernel<4><<<cus, nt, 0, st>>>(s, nslots, steps, sink); break;
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
 
 extern "C" moe_status moe_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
   if (!src || !sink) return MOE_ERR_NULL;

@@ -209,3 +209,18 @@ def test_audit_entry_points_validate_before_any_launch():
     assert A(fake, bf, 4, 100, 100, fake + 4, fake, wsz, None) == _lib.MOE_ERR_ALIGN
     assert A(fake, bf, 4, 100, 100, fake, fake + 16, wsz, None) == _lib.MOE_ERR_ALIGN
     assert A(fake, bf, 4, 100, 100, fake, fake, wsz - 1, None) == _lib.MOE_ERR_WORKSPACE
+
+
+def test_measurement_probes_validate_before_launch():
+    L = _lib.LIB
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails its checks first
+    assert L.moe_hbm_read_probe(None, 16, fake, None) == _lib.MOE_ERR_NULL
+    assert L.moe_hbm_read_probe(ctypes.c_void_p(0x10008), 16, fake, None) == _lib.MOE_ERR_ALIGN
+    assert L.moe_hbm_read_probe(fake, 24, fake, None) == _lib.MOE_ERR_ALIGN
+    assert L.moe_mfma_pipe_probe(0, 10, None, 0, None, None) == _lib.MOE_ERR_NULL
+    for variant, steps in ((-1, 10), (5, 10), (0, 0), (2, (1 << 24) + 1)):
+        assert L.moe_mfma_pipe_probe(variant, steps, None, 0, fake, None) == _lib.MOE_ERR_SHAPE
+    assert L.moe_mfma_pipe_probe(3, 10, None, 32768, fake, None) == _lib.MOE_ERR_NULL
+    assert L.moe_mfma_pipe_probe(4, 10, ctypes.c_void_p(0x10008), 32768, fake, None) == _lib.MOE_ERR_ALIGN
+    for nbytes in (0, 16384, 32768 + 16, (1 << 20) * 32768 + 32768):
+        assert L.moe_mfma_pipe_probe(3, 10, fake, nbytes, fake, None) == _lib.MOE_ERR_SHAPE
