@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only time moe_mfma_pipe_probe's variants, and the 256x256 tile kernel and hipBLASLt on "
                          "one dense 8192x4096x8192 gate/up product (zero and random operands), and print them")
+    ap.add_argument("--mfma-launches", type=int, default=2000,
+                    help="--mfma-ceiling: back-to-back launches of each dense run (fewer under a counter profiler)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scale factor for HBM byte counters)")
     return ap.parse_args()
@@ -109,7 +111,7 @@ def stream_ceiling(lib, stream, nbytes=4 << 30, launches=20):
             "gbs_best": round(max(gbs), 1), "frac_of_8tbs": round(pct(gbs, 0.5) / 8000.0, 4)}
 
 
-def mfma_ceiling(lib, stream):
+def mfma_ceiling(lib, stream, launches=2000):
     """What the tile kernel's pipeline costs the MFMA rate, and where it stands
     against the vendor GEMM on one dense product.
 
@@ -120,7 +122,7 @@ def mfma_ceiling(lib, stream):
       I 2048: an 8192 x 4096 x 8192 GEMM) through moe_expert_gate_up with
       256-row tiles, and torch.matmul (hipBLASLt) on the same shape, each
       launched back to back for about a second so that the clock settles, with
-      the shader clock sampled meanwhile; once on zero operands (the clock stays
+      the shader clock sampled meanwhile (`launches` times each); once on zero operands (the clock stays
       near its maximum) and once on random ones (the chip's power limit lowers
       it)."""
     import torch
@@ -168,7 +170,7 @@ def mfma_ceiling(lib, stream):
                 for _ in range(5):
                     fn()
                 torch.cuda.synchronize()
-                n = 2000
+                n = launches
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 with ClockSampler(0.01) as clk:
                     a.record(stream)
@@ -654,7 +656,8 @@ def main():
         print(json.dumps({"stream_ceiling": stream_ceiling(lib, torch.cuda.current_stream())}), flush=True)
         return
     if args.mfma_ceiling:
-        print(json.dumps({"mfma_ceiling": mfma_ceiling(lib, torch.cuda.current_stream())}), flush=True)
+        print(json.dumps({"mfma_ceiling": mfma_ceiling(lib, torch.cuda.current_stream(), args.mfma_launches)}),
+              flush=True)
         return
     flags = {"auto": 0, "128": lib.MOE_FLAG_GEMM_TILE_128, "256": lib.MOE_FLAG_GEMM_TILE_256}[args.gemm_tile]
     flags |= {"auto": 0, "gemm": lib.MOE_FLAG_FORCE_GEMM, "stream": lib.MOE_FLAG_FORCE_STREAM}[args.path]
