@@ -31,13 +31,16 @@ __device__ __forceinline__ void accumulate(float* acc, float wgt, u32x4 v) {
 }
 
 // Workgroup (t, blockIdx.y) covers 16-byte chunks blockIdx.y*256 + tid of
-// token t.  The token's k row positions and weights are staged in LDS once;
-// a thread then issues the y loads of up to 8 assignments before adding them
-// (j ascending), so the k+1 row reads overlap instead of forming a chain.
+// token t.  The token's k row positions and weights are the same for the
+// whole workgroup (scalar loads); a thread issues the y rows of the token's
+// assignments and the shared expert's row at once, then adds them (j
+// ascending, the shared expert last), so the k+1 row reads overlap instead
+// of forming a chain.  KB > 0: k <= KB, one batch, every load unconditional
+// (indices clamped into the token's k); KB == 0: any k, batches of 16.
 // GRW (bf16 only): the gated-residual stream write in the epilogue;
 // resid / s / resid_out as gr_write (resid_out may alias resid: each element
 // is read and then written by one thread), out may be null.
-template <bool F32, bool GRW = false>
+template <bool F32, bool GRW, int KB>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y, const int32_t* __restrict__ pos,
                                                       const float* __restrict__ w, const void* __restrict__ y_sh,
                                                       const float* __restrict__ sl, void* __restrict__ out, int H,
@@ -46,21 +49,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   static_assert(!(F32 && GRW), "the gated residual is bf16");
   constexpr int VEC = F32 ? 4 : 8;
   constexpr int ESZ = F32 ? 4 : 2;
-  constexpr int BATCH = 8;
-  __shared__ int64_t s_row[64];
-  __shared__ float s_w[64];
   const int t = blockIdx.x;
-  if ((int)threadIdx.x < k) {
-    const int64_t a = (int64_t)t * k + threadIdx.x;
-    s_row[threadIdx.x] = (int64_t)pos[a] * H;
-    s_w[threadIdx.x] = w[a];
-  }
-  __syncthreads();
   const int c = blockIdx.y * blockDim.x + threadIdx.x;
   if (c >= H / VEC) return;
   const int64_t col = (int64_t)c * VEC;
   const char* yb = reinterpret_cast<const char*>(y);
-  // the streams' loads go first, so they are in flight with the y rows
+  const int32_t* pt = pos + (int64_t)t * k;
+  const float* wt = w + (int64_t)t * k;
   constexpr int STREAMS = 4;
   u32x4 r[GRW ? STREAMS : 1];
   if constexpr (GRW) {
@@ -70,18 +65,38 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   float acc[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-  for (int j0 = 0; j0 < k; j0 += BATCH) {
-    u32x4 v[BATCH];
+  if constexpr (KB > 0) {
+    // without a shared expert its load reads row 0 of y instead (unused)
+    const char* shp = y_sh ? reinterpret_cast<const char*>(y_sh) + (int64_t)t * H * ESZ : yb;
+    const u32x4 vsh = ld16(shp + col * ESZ);
+    int64_t row[KB];
+    float wj[KB];
 #pragma unroll
-    for (int b = 0; b < BATCH; ++b)
-      if (j0 + b < k) v[b] = ld16(yb + (s_row[j0 + b] + col) * ESZ);
+    for (int b = 0; b < KB; ++b) {
+      const int j = b < k ? b : k - 1;
+      row[b] = (int64_t)pt[j] * H;
+      wj[b] = wt[j];
+    }
+    u32x4 v[KB];
 #pragma unroll
-    for (int b = 0; b < BATCH; ++b)
-      if (j0 + b < k) accumulate<F32>(acc, s_w[j0 + b], v[b]);
-  }
-  if (y_sh) {
-    const u32x4 v = ld16(reinterpret_cast<const char*>(y_sh) + ((int64_t)t * H + col) * ESZ);
-    accumulate<F32>(acc, sigmoid(sl[t]), v);
+    for (int b = 0; b < KB; ++b) v[b] = ld16(yb + (row[b] + col) * ESZ);
+#pragma unroll
+    for (int b = 0; b < KB; ++b)
+      if (b < k) accumulate<F32>(acc, wj[b], v[b]);
+    if (y_sh) accumulate<F32>(acc, sigmoid(sl[t]), vsh);
+  } else {
+    u32x4 vsh = {0, 0, 0, 0};
+    if (y_sh) vsh = ld16(reinterpret_cast<const char*>(y_sh) + ((int64_t)t * H + col) * ESZ);
+    for (int j0 = 0; j0 < k; j0 += 16) {
+      u32x4 v[16];
+#pragma unroll
+      for (int b = 0; b < 16; ++b)
+        if (j0 + b < k) v[b] = ld16(yb + ((int64_t)pt[j0 + b] * H + col) * ESZ);
+#pragma unroll
+      for (int b = 0; b < 16; ++b)
+        if (j0 + b < k) accumulate<F32>(acc, wt[j0 + b], v[b]);
+    }
+    if (y_sh) accumulate<F32>(acc, sigmoid(sl[t]), vsh);
   }
   char* dst = out ? reinterpret_cast<char*>(out) + ((int64_t)t * H + col) * ESZ : nullptr;
   if constexpr (F32) {
@@ -108,14 +123,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 
 }  // namespace
 
+// One batch of KB row loads: the smallest of 1, 2, 4, 8, 10, 12, 16 that
+// covers k (the common k load no row twice); k > 16: batches of 16.
+#define MOE_COMBINE_KB(F32, GRW, ...)                                                             \
+  do {                                                                                           \
+    if (k <= 1) combine_kernel<F32, GRW, 1><<<grid, 256, 0, s>>>(__VA_ARGS__);                   \
+    else if (k <= 2) combine_kernel<F32, GRW, 2><<<grid, 256, 0, s>>>(__VA_ARGS__);              \
+    else if (k <= 4) combine_kernel<F32, GRW, 4><<<grid, 256, 0, s>>>(__VA_ARGS__);              \
+    else if (k <= 8) combine_kernel<F32, GRW, 8><<<grid, 256, 0, s>>>(__VA_ARGS__);              \
+    else if (k <= 10) combine_kernel<F32, GRW, 10><<<grid, 256, 0, s>>>(__VA_ARGS__);            \
+    else if (k <= 12) combine_kernel<F32, GRW, 12><<<grid, 256, 0, s>>>(__VA_ARGS__);            \
+    else if (k <= 16) combine_kernel<F32, GRW, 16><<<grid, 256, 0, s>>>(__VA_ARGS__);            \
+    else combine_kernel<F32, GRW, 0><<<grid, 256, 0, s>>>(__VA_ARGS__);                          \
+  } while (0)
+
 hipError_t launch_combine(const void* y, const int32_t* pos, const float* w, const void* y_sh,
                           const float* shared_logit, void* out, int T, int H, int k, int f32, hipStream_t s) {
   const int vec = f32 ? 4 : 8;
   const dim3 grid(T, (H / vec + 255) / 256);
-  if (f32)
-    combine_kernel<true><<<grid, 256, 0, s>>>(y, pos, w, y_sh, shared_logit, out, H, k, nullptr, nullptr, nullptr);
-  else
-    combine_kernel<false><<<grid, 256, 0, s>>>(y, pos, w, y_sh, shared_logit, out, H, k, nullptr, nullptr, nullptr);
+  if (f32) MOE_COMBINE_KB(true, false, y, pos, w, y_sh, shared_logit, out, H, k, nullptr, nullptr, nullptr);
+  else MOE_COMBINE_KB(false, false, y, pos, w, y_sh, shared_logit, out, H, k, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -123,10 +150,10 @@ hipError_t launch_combine_gr_write(const void* y, const int32_t* pos, const floa
                                    const float* shared_logit, void* out, const void* resid, const float* gate,
                                    void* resid_out, int T, int H, int k, hipStream_t s) {
   const dim3 grid(T, (H / 8 + 255) / 256);
-  combine_kernel<false, true><<<grid, 256, 0, s>>>(y, pos, w, y_sh, shared_logit, out, H, k,
-                                                   reinterpret_cast<const bf16*>(resid), gate,
-                                                   reinterpret_cast<bf16*>(resid_out));
+  MOE_COMBINE_KB(false, true, y, pos, w, y_sh, shared_logit, out, H, k, reinterpret_cast<const bf16*>(resid), gate,
+                 reinterpret_cast<bf16*>(resid_out));
   return hipGetLastError();
 }
+#undef MOE_COMBINE_KB
 
 }  // namespace moe
