@@ -170,8 +170,10 @@ inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : M
 // stage bodies (arguments already validated)
 // ---------------------------------------------------------------------------
 // Where the layer call's small batches (T <= kSmallBatch) take the dispatch
-// from the top-k kernel itself.  Such a batch always routes with the
-// streaming (or fp32) router, whose launch zeroes the top-k counter.
+// from the top-k kernel itself (fp32 layers, fp8 weights, or the GEMM path
+// forced; bf16 layers take it in the gate/up streaming launch instead).  Such
+// a batch always routes with the streaming (or fp32) router, whose launch
+// zeroes the top-k counter.
 static_assert(moe::kSmallBatch <= moe::kStreamMaxRows, "small batches take the streaming router");
 struct DispatchOut {
   int32_t* offsets;
@@ -297,7 +299,10 @@ constexpr int kStreamReserve = 32;
 
 // phases: bit 0 gate/up, bit 1 down.  The plan kernel runs first (bf16/fp8).
 // fork_ok: the streaming launches may run on the device's second stream.
-moe_status run_ffn(const moe_problem* p, FfnArgs& a, int phases, void* plan_ws, hipStream_t s, bool fork_ok) {
+// route (may be null): the gate/up streaming launch takes the small batch's
+// dispatch from the ids (see moe::SmallRoute).
+moe_status run_ffn(const moe_problem* p, FfnArgs& a, int phases, void* plan_ws, hipStream_t s, bool fork_ok,
+                   const moe::SmallRoute* route = nullptr) {
   if (p->act_dtype == MOE_F32) return hip_status(moe::launch_ffn_f32(a, phases, s));
   int32_t* plan = static_cast<int32_t*>(plan_ws);
   const bool big = use_big_tiles(p, a);
@@ -330,7 +335,9 @@ moe_status run_ffn(const moe_problem* p, FfnArgs& a, int phases, void* plan_ws, 
         const hipError_t e = big ? moe::launch_ffn_gemm_big(a, phase, s) : moe::launch_ffn_gemm(a, phase, s);
         if (e != hipSuccess) return MOE_ERR_HIP;
       }
-      if (any_stream && moe::launch_ffn_stream(a, phase, s, self_plan) != hipSuccess) return MOE_ERR_HIP;
+      if (any_stream &&
+          moe::launch_ffn_stream(a, phase, s, self_plan, phase == 1 ? route : nullptr) != hipSuccess)
+        return MOE_ERR_HIP;
     }
     return MOE_OK;
   }
@@ -352,7 +359,8 @@ moe_status run_ffn(const moe_problem* p, FfnArgs& a, int phases, void* plan_ws, 
 }
 
 moe_status do_ffn(const moe_problem* p, const moe_weights* w, const void* x, const int32_t* offsets,
-                  const int32_t* sorted, void* y, void* y_sh, void* stage, hipStream_t s, bool fork_ok = true) {
+                  const int32_t* sorted, void* y, void* y_sh, void* stage, hipStream_t s, bool fork_ok = true,
+                  const moe::SmallRoute* route = nullptr) {
   FfnArgs a = ffn_args(p, w, x, offsets, sorted, y_sh != nullptr);
   a.y = y;
   a.y_sh = a.Is ? y_sh : nullptr;
@@ -361,7 +369,7 @@ moe_status do_ffn(const moe_problem* p, const moe_weights* w, const void* x, con
   const size_t plan_bytes = up(moe::ffn_plan_ints(p->T, p->E, p->k, a.Is > 0) * 4);
   a.h = b + plan_bytes;
   a.h_sh = b + plan_bytes + up((size_t)p->T * p->k * p->I * act_bytes(p));
-  return run_ffn(p, a, 3, b, s, fork_ok);
+  return run_ffn(p, a, 3, b, s, fork_ok, route);
 }
 
 }  // namespace
@@ -385,17 +393,23 @@ moe_status layer_forward_run(const moe_problem* p, const moe_weights* w, const v
   int32_t* ids = topk_ids ? topk_ids : L.ids;
   float* tw = topk_w ? topk_w : L.w;
   const bool sh = p->I_shared > 0;
-  // a small batch's dispatch comes out of the top-k workgroup
+  // A small batch's dispatch comes out of the gate/up streaming launch (bf16
+  // weights, every group streaming) or else out of the top-k workgroups; a
+  // larger batch's from the dispatch kernels.
   const bool small = p->T <= moe::kSmallBatch;
+  const bool route_in_ffn = small && p->act_dtype == MOE_BF16 && p->w_dtype == MOE_BF16 &&
+                            !(p->flags & MOE_FLAG_FORCE_GEMM);
   const DispatchOut d{L.offsets, L.sorted, L.pos};
+  const moe::SmallRoute route{ids, L.offsets, L.sorted, L.pos};
   if ((st = do_route(p, x, w->w_router, sh ? w->sh_gate_w : nullptr, ids, tw, sh ? L.sl : nullptr, L.stage, s,
-                     small ? &d : nullptr)) != MOE_OK)
+                     small && !route_in_ffn ? &d : nullptr)) != MOE_OK)
     return st;
   if (!small && (st = hip_status(moe::launch_dispatch(ids, (int)p->T, (int)p->E, (int)p->k, L.offsets, L.sorted,
                                                       L.pos, static_cast<int32_t*>(L.stage), s,
                                                       /*distinct=*/true))) != MOE_OK)
     return st;
-  if ((st = do_ffn(p, w, x, L.offsets, L.sorted, L.y, sh ? L.y_sh : nullptr, L.stage, s, fork_ok)) != MOE_OK)
+  if ((st = do_ffn(p, w, x, L.offsets, L.sorted, L.y, sh ? L.y_sh : nullptr, L.stage, s, fork_ok,
+                   route_in_ffn ? &route : nullptr)) != MOE_OK)
     return st;
   return hip_status(moe::launch_combine(L.y, L.pos, tw, sh ? L.y_sh : nullptr, sh ? L.sl : nullptr, out, (int)p->T,
                                         (int)p->H, (int)p->k, p->act_dtype == MOE_F32 ? 1 : 0, s));

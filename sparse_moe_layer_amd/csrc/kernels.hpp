@@ -112,9 +112,23 @@ bool ffn_dma_supported(const FfnArgs& a);
 // plan has streaming blocks, so that a streaming launch on another stream
 // gets their CUs (0: the whole grid takes tiles).
 hipError_t launch_ffn_gemm_big(const FfnArgs& a, int phase, hipStream_t s, int reserve = 0);
+// A small batch's dispatch done by the gate/up streaming launch itself (bf16
+// weights, T <= kSmallBatch): from the router's picks ids [T, k] (distinct
+// within a token), every workgroup builds each expert's token mask and the
+// list of touched experts in LDS, and workgroup 0 writes offsets [E+1],
+// sorted [R] and pos [R] (the outputs of launch_dispatch) for the launches
+// after it.
+struct SmallRoute {
+  const int32_t* ids;
+  int32_t* offsets;
+  int32_t* sorted;
+  int32_t* pos;
+};
 // phase 1 gate/up, 2 down.  self_plan: T <= kStreamMaxRows and no plan kernel
-// ran; the kernels list the touched groups from the offsets themselves.
-hipError_t launch_ffn_stream(const FfnArgs& a, int phase, hipStream_t s, bool self_plan = false);
+// ran; the kernels list the touched groups from the offsets themselves, or
+// (route, phase 1 with bf16 weights and T <= kSmallBatch) from the ids.
+hipError_t launch_ffn_stream(const FfnArgs& a, int phase, hipStream_t s, bool self_plan = false,
+                             const SmallRoute* route = nullptr);
 hipError_t launch_ffn_f32(const FfnArgs& a, int phases, hipStream_t s);  // bit 0 gate/up, bit 1 down
 hipError_t launch_combine(const void* y, const int32_t* pos, const float* w, const void* y_sh,
                           const float* shared_logit, void* out, int T, int H, int k, int f32,

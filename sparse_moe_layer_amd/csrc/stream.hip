@@ -75,11 +75,22 @@ __device__ __forceinline__ void stream_dot(const bf16* a_row, const bf16* const*
 // workgroup lists the touched groups itself, in ascending order with the
 // shared expert last, from the expert offsets (the plan's stream list for
 // such a batch); the list bounds name plan positions as without it.
+// self_plan == 2 (route.ids non-null; bf16 gate/up split items, T <=
+// kSmallBatch): the dispatch is not in memory yet.  Each workgroup ORs every
+// assignment a = t*k + j into its expert's token mask in LDS (bit t; a
+// token's picks are distinct experts), lists the experts with a nonzero mask
+// as (expert | mask << 11), and takes an item's first dispatched row as the
+// number of rows of the experts listed before it: the stable order of the
+// dispatch kernels, in which an expert's rows are its tokens ascending.
+// Wave 0 of workgroup 0 also writes offsets, sorted and pos from the masks.
 template <int PHASE, bool FP8, bool SPLIT = false>
 __global__ __launch_bounds__(WAVES * 64, 2) void stream_kernel(FfnArgs f, int list_begin_idx, int list_end_idx,
-                                                               int self_plan) {
+                                                               int self_plan, SmallRoute route) {
   static_assert(!SPLIT || (PHASE == 1 && !FP8), "split items are bf16 gate/up");
   constexpr int STAGE_BYTES = item_lds_bytes<FP8, SPLIT>();  // per wave
+  constexpr bool ROUTES = PHASE == 1 && !FP8 && SPLIT;       // may take the dispatch (self_plan == 2)
+  // the masks and (workgroup 0) the experts' first rows fit wave 0's own stage buffer
+  static_assert(!ROUTES || 2 * kMaxExperts * 4 <= STAGE_BYTES, "route scratch in the stage");
   __shared__ __attribute__((aligned(16))) char stage[WAVES * STAGE_BYTES];
   __shared__ int glist[kMaxExperts + 1];  // SELF_PLAN: touched groups
   __shared__ int wtot[WAVES];
@@ -88,25 +99,83 @@ __global__ __launch_bounds__(WAVES * 64, 2) void stream_kernel(FfnArgs f, int li
   const int gw = blockIdx.x * WAVES + (threadIdx.x >> 6);
   const int nw = gridDim.x * WAVES;
   int sb_begin, sb_end;
+  // route: token masks per expert in the stage buffers until the items start
+  uint32_t* tmask = reinterpret_cast<uint32_t*>(stage);
+  const bool routed = ROUTES && self_plan == 2;
+  if (routed) {
+    for (int e = threadIdx.x; e < f.E; e += WAVES * 64) tmask[e] = 0u;
+    __syncthreads();
+    for (int a = threadIdx.x; a < f.T * f.k; a += WAVES * 64) {
+      int e = route.ids[a];
+      e = (unsigned)e < (unsigned)f.E ? e : f.E - 1;  // (the router's ids are in range)
+      atomicOr(&tmask[e], 1u << (a / f.k));
+    }
+    __syncthreads();
+  }
   if (self_plan) {
     // ordered compaction of the routed groups with rows, 64*WAVES at a time:
     // a wave's ballot gives each lane its rank, the waves' totals its offset
     int n_routed = 0;
     for (int g0 = 0; g0 < f.E; g0 += WAVES * 64) {
       const int g = g0 + threadIdx.x;
-      const bool t = g < f.E && f.offsets[g + 1] > f.offsets[g];
+      uint32_t mk = 0u;
+      bool t;
+      if (routed) {
+        mk = g < f.E ? tmask[g] : 0u;
+        t = mk != 0u;
+      } else {
+        t = g < f.E && f.offsets[g + 1] > f.offsets[g];
+      }
       const uint64_t bal = __ballot(t);
       const int rank = __popcll(bal & ((1ull << lane) - 1ull));
       if (lane == 0) wtot[wave] = __popcll(bal);
       __syncthreads();
       int off = n_routed;
       for (int w = 0; w < wave; ++w) off += wtot[w];
-      if (t) glist[off + rank] = g;
+      if (t) glist[off + rank] = routed ? (int)((uint32_t)g | (mk << 11)) : g;
       for (int w = 0; w < WAVES; ++w) n_routed += wtot[w];
       __syncthreads();
     }
     if (threadIdx.x == 0) glist[n_routed] = f.E;  // the shared expert (read only when present)
     __syncthreads();
+    if (routed && blockIdx.x == 0 && wave == 0) {
+      // the dispatch's outputs: offsets from an exclusive scan of the mask
+      // populations (lane i owns experts [i*per, (i+1)*per)), then each
+      // assignment at its expert's first row plus its token's rank in the
+      // expert's mask.  The start of each expert goes to the second half of
+      // the scratch (this wave's own stage buffer, before its items).
+      int* start = reinterpret_cast<int*>(tmask + kMaxExperts);
+      const int per = (f.E + 63) / 64;
+      const int e0 = lane * per;
+      int local = 0;
+      for (int i = 0; i < per; ++i) local += e0 + i < f.E ? __popc(tmask[e0 + i]) : 0;
+      int incl = local;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+      }
+      int run = incl - local;
+      for (int i = 0; i < per; ++i) {
+        const int e = e0 + i;
+        if (e < f.E) {
+          route.offsets[e] = run;
+          start[e] = run;
+          run += __popc(tmask[e]);
+        }
+      }
+      if (lane == 63) route.offsets[f.E] = incl;
+      __builtin_amdgcn_wave_barrier();
+      for (int a = lane; a < f.T * f.k; a += 64) {
+        int e = route.ids[a];
+        e = (unsigned)e < (unsigned)f.E ? e : f.E - 1;
+        const int t = a / f.k;
+        const int p = start[e] + __popc(tmask[e] & ((1u << t) - 1u));
+        route.sorted[p] = a;
+        route.pos[a] = p;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
     const int n_all = n_routed + (f.Is > 0 ? 1 : 0);
     sb_begin = list_begin_idx == kPlanStart ? 0 : (list_begin_idx == kPlanRoutedBlocks ? n_routed : n_all);
     sb_end = list_end_idx == kPlanRoutedBlocks ? n_routed : n_all;
@@ -123,7 +192,25 @@ __global__ __launch_bounds__(WAVES * 64, 2) void stream_kernel(FfnArgs f, int li
     const int sb = sb_begin + item / n_slabs;
     const int slab = item % n_slabs;
     int g, r0, base, nrows;
-    if (self_plan) {
+    uint32_t mk = 0u;
+    if (routed) {
+      const int entry = glist[sb];
+      g = entry & 2047;
+      r0 = 0;
+      if (g < f.E) {
+        mk = (uint32_t)entry >> 11;
+        nrows = __popc(mk);
+        // first dispatched row: the rows of the experts listed before it
+        int cnt = 0;
+        for (int j = lane; j < sb; j += 64) cnt += __popc((uint32_t)glist[j] >> 11);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+        base = cnt;
+      } else {
+        base = 0;
+        nrows = f.T;
+      }
+    } else if (self_plan) {
       g = glist[sb];
       r0 = 0;
       base = g < f.E ? f.offsets[g] : 0;
@@ -135,7 +222,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void stream_kernel(FfnArgs f, int li
       nrows = f.sb_nrows[sb];
     }
     stream_item<PHASE, FP8, SPLIT>(f, g, r0, base, nrows, self_plan ? nullptr : f.sb_tok + sb * kStreamBM, slab,
-                                   lane, stage + wave * STAGE_BYTES);
+                                   lane, stage + wave * STAGE_BYTES, mk);
   }
 }
 
@@ -219,24 +306,34 @@ hipError_t launch_router_stream(const void* x, const void* w_router, const void*
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_stream(const FfnArgs& a, int phase, hipStream_t s, bool self_plan) {
+hipError_t launch_ffn_stream(const FfnArgs& a, int phase, hipStream_t s, bool self_plan, const SmallRoute* route) {
   const int grid = stream_grid();
   const int blk = WAVES * 64;
-  const int sp = self_plan ? 1 : 0;
+  int sp = self_plan ? 1 : 0;
   // a batch of at most kStreamMaxRows tokens streams every group: split items
   const bool split = a.T <= kStreamMaxRows;
+  SmallRoute r{nullptr, nullptr, nullptr, nullptr};
+  if (route) {
+    // the dispatch from the ids: bf16 gate/up of a small batch listing its own groups
+    if (phase != 1 || a.fp8 || !self_plan || a.T > kSmallBatch || a.E > kMaxExperts || !route->ids ||
+        !route->offsets || !route->sorted || !route->pos)
+      return hipErrorInvalidValue;
+    r = *route;
+    sp = 2;
+  }
   if (a.fp8) {
-    if (phase == 1) stream_kernel<1, true><<<grid, blk, 0, s>>>(a, kPlanStart, kPlanRoutedBlocks, sp);
-    else stream_kernel<2, true><<<grid, blk, 0, s>>>(a, kPlanStart, kPlanRoutedBlocks, sp);
+    if (phase == 1) stream_kernel<1, true><<<grid, blk, 0, s>>>(a, kPlanStart, kPlanRoutedBlocks, sp, r);
+    else stream_kernel<2, true><<<grid, blk, 0, s>>>(a, kPlanStart, kPlanRoutedBlocks, sp, r);
     if (a.Is > 0) {
-      if (phase == 1 && split) stream_kernel<1, false, true><<<grid, blk, 0, s>>>(a, kPlanRoutedBlocks, kPlanBlocks, sp);
-      else if (phase == 1) stream_kernel<1, false><<<grid, blk, 0, s>>>(a, kPlanRoutedBlocks, kPlanBlocks, sp);
-      else stream_kernel<2, false><<<grid, blk, 0, s>>>(a, kPlanRoutedBlocks, kPlanBlocks, sp);
+      if (phase == 1 && split)
+        stream_kernel<1, false, true><<<grid, blk, 0, s>>>(a, kPlanRoutedBlocks, kPlanBlocks, sp, r);
+      else if (phase == 1) stream_kernel<1, false><<<grid, blk, 0, s>>>(a, kPlanRoutedBlocks, kPlanBlocks, sp, r);
+      else stream_kernel<2, false><<<grid, blk, 0, s>>>(a, kPlanRoutedBlocks, kPlanBlocks, sp, r);
     }
   } else {
-    if (phase == 1 && split) stream_kernel<1, false, true><<<grid, blk, 0, s>>>(a, kPlanStart, kPlanBlocks, sp);
-    else if (phase == 1) stream_kernel<1, false><<<grid, blk, 0, s>>>(a, kPlanStart, kPlanBlocks, sp);
-    else stream_kernel<2, false><<<grid, blk, 0, s>>>(a, kPlanStart, kPlanBlocks, sp);
+    if (phase == 1 && split) stream_kernel<1, false, true><<<grid, blk, 0, s>>>(a, kPlanStart, kPlanBlocks, sp, r);
+    else if (phase == 1) stream_kernel<1, false><<<grid, blk, 0, s>>>(a, kPlanStart, kPlanBlocks, sp, r);
+    else stream_kernel<2, false><<<grid, blk, 0, s>>>(a, kPlanStart, kPlanBlocks, sp, r);
   }
   return hipGetLastError();
 }

@@ -269,13 +269,16 @@ constexpr int item_lds_bytes() {
 
 // One item: slab `slab` of group g (routed expert g < E, or the shared
 // expert g == E) for rows r0 .. r0+nrows-1 of the group (nrows <= 16), whose
-// dispatched rows start at `base`.  tok_row: the gathered token of each row
-// (the plan's list), or null to read them from f.sorted.  lds: this wave's
-// item_lds_bytes<FP8, SPLIT>() bytes.  Returns at once if the slab lies past
-// the group's columns.
+// dispatched rows start at `base`.  The gathered token of each row: tok_row
+// (the plan's list); else, when tok_mask is nonzero, the group's tokens as a
+// bit mask (row m is the token of its m-th set bit: a batch of at most 32
+// tokens whose dispatch is not in memory yet); else f.sorted.  lds: this
+// wave's item_lds_bytes<FP8, SPLIT>() bytes.  Returns at once if the slab
+// lies past the group's columns.
 template <int PHASE, bool FP8, bool SPLIT>
 __device__ __forceinline__ void stream_item(const FfnArgs& f, int g, int r0, int base, int nrows,
-                                            const int32_t* tok_row, int slab, int lane, char* lds) {
+                                            const int32_t* tok_row, int slab, int lane, char* lds,
+                                            uint32_t tok_mask = 0u) {
   static_assert(!SPLIT || (PHASE == 1 && !FP8), "split items are bf16 gate/up");
   constexpr int NB = SPLIT ? 1 : 2;
   const int cols_per_item = PHASE == 1 ? (SPLIT ? 8 : 16) : 32;
@@ -292,8 +295,15 @@ __device__ __forceinline__ void stream_item(const FfnArgs& f, int g, int r0, int
     const int gr = base + r0 + m;
     if (PHASE == 1) {
       int tok;
-      if (tok_row) tok = tok_row[m];
-      else tok = g < f.E ? f.sorted[gr] / f.k : m;
+      if (tok_row) {
+        tok = tok_row[m];
+      } else if (tok_mask) {
+        uint32_t mm = tok_mask;
+        for (int i = 0; i < m; ++i) mm &= mm - 1u;  // drop the m lowest set bits
+        tok = __builtin_ctz(mm);
+      } else {
+        tok = g < f.E ? f.sorted[gr] / f.k : m;
+      }
       tok = (unsigned)tok < (unsigned)f.T ? tok : f.T - 1;  // also clamps a negative index
       a_row = reinterpret_cast<const bf16*>(f.x) + (int64_t)tok * f.H;
     } else {

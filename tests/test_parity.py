@@ -328,13 +328,28 @@ def test_decode_batch_max_experts():
 @pytest.mark.parametrize("T,E,k,H,Is", [(1, 40, 3, 256, 0), (7, 100, 10, 512, 64), (16, 64, 64, 128, 128),
                                          (16, 512, 10, 136, 64), (12, 1000, 8, 2560, 640)])
 def test_small_batch_fused_route_and_dispatch(T, E, k, H, Is):
-    # T <= 16: the layer call's top-k and dispatch run as one kernel (k = 64
-    # gives R = 1024 assignments, the most it takes); same bits as the
-    # separate top-k and dispatch kernels of the stage calls
+    # T <= 16, bf16: the layer call's dispatch is built by the gate/up
+    # streaming launch from the top-k ids (k = 64 gives R = 1024 assignments,
+    # the most it takes); same bits as the dispatch kernels of the stage calls
+    # (offsets, sorted and pos feed the down launch and the combine)
     cfg = CONFIGS["flash_decode"].with_(name=f"small_T{T}_E{E}_k{k}", T=T, H=H, E=E, k=k, I=64, I_shared=Is)
     p = gpu_problem(cfg, 21 + T)
     g = run_stages(p)
     check(p, g)
+
+
+@pytest.mark.parametrize("case", ["f32", "fp8", "gemm"])
+def test_small_batch_dispatch_from_topk(case):
+    # T <= 16 with fp32 activations, fp8 weights or the GEMM path forced: the
+    # layer call's top-k workgroups also dispatch (the last one to finish)
+    if case == "fp8":
+        cfg = CONFIGS["max_fp8"].with_(name="small_fp8", T=16, H=256, E=96, k=6, I=128, I_shared=128, zipf_s=0.0)
+    else:
+        cfg = CONFIGS["flash_decode"].with_(name=f"small_{case}", T=13, H=192, E=80, k=7, I=96, I_shared=64,
+                                            act="f32" if case == "f32" else "bf16",
+                                            wdt="f32" if case == "f32" else "bf16")
+    p = gpu_problem(cfg, 31)
+    check(p, run_stages(p, lib.MOE_FLAG_FORCE_GEMM if case == "gemm" else 0))
 
 
 @pytest.mark.timeout(400)
