@@ -110,7 +110,8 @@ moe_status check_problem(const moe_problem* p) {
   if (p->T > (int64_t)INT32_MAX / p->k || p->H > (1 << 24) || p->I > (1 << 24) || p->I_shared > (1 << 24))
     return MOE_ERR_SHAPE;
   // kernels address x, h, h_sh and one expert's matrices with 32-bit element
-  // offsets; y [R, H] rows go through 64-bit offsets
+  // offsets (the tile kernel's buffer loads with 32-bit byte offsets of bf16
+  // elements); y [R, H] rows go through 64-bit offsets
   const int64_t lim = (int64_t)1 << 31;
   const int64_t R = p->T * p->k;
   if (p->T * p->H >= lim || R * p->I >= lim || p->T * p->I_shared >= lim || p->I * p->H >= lim ||

@@ -69,7 +69,18 @@ using BigCfg8 = Cfg<256, 256, 2, 4, 4, 1, 32, true>;
 
 constexpr int vmcnt_imm(int n) { return 0xF70 | (n & 15) | (((n >> 4) & 3) << 14); }
 
-__device__ __forceinline__ void dma16(const void* g, bf16* l) { __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0); }
+// A 16-byte direct load (global memory to LDS, no registers) through a
+// buffer resource over base, at byte offset off < 2^32 (the layer checks keep
+// every element offset below 2^31).  The compiler counts buffer loads to LDS
+// apart from LDS reads, so fragment reads keep partial LDS waits; with the
+// global_load_lds form in flight it waits for every outstanding LDS operation
+// before each MFMA that consumes a fragment.
+constexpr int kBufferFlags = 0x00020000;  // raw (untyped) 32-bit buffer access
+__device__ __forceinline__ void dma16b(const void* base, uint32_t off, bf16* l) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0xFFFFFFFF,
+                                                                      kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 16, off, 0, 0, 0);
+}
 
 // Compiler-level fence around the raw s_barrier (the barrier builtin itself
 // does not order memory operations for the compiler).
@@ -92,14 +103,14 @@ template <class C>
 __device__ __forceinline__ void issue_stage(bf16* st, const bf16* abase, const uint32_t* aoff,
                                             const bf16* const* bbase, const uint32_t* boff, uint32_t k0, int wave) {
 #pragma unroll
-  for (int i = 0; i < C::LA; ++i) dma16(abase + (aoff[i] + k0), st + (C::NW * i + wave) * 512);
+  for (int i = 0; i < C::LA; ++i) dma16b(abase, (aoff[i] + k0) * 2u, st + (C::NW * i + wave) * 512);
 #pragma unroll
   for (int i = 0; i < C::LB; ++i) {
     // fp8: bbase holds byte pointers, boff byte offsets (k0 counts codes)
     if constexpr (C::F8)
-      dma16(reinterpret_cast<const uint8_t*>(bbase[i]) + (boff[i] + k0), st + C::BM * C::BK + (C::NW * i + wave) * 512);
+      dma16b(bbase[i], boff[i] + k0, st + C::BM * C::BK + (C::NW * i + wave) * 512);
     else
-      dma16(bbase[i] + (boff[i] + k0), st + C::BM * C::BK + (C::NW * i + wave) * 512);
+      dma16b(bbase[i], (boff[i] + k0) * 2u, st + C::BM * C::BK + (C::NW * i + wave) * 512);
   }
 }
 
