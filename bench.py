@@ -131,7 +131,8 @@ def mfma_ceiling(lib, stream, launches=2000):
     src = torch.zeros(4 << 20, dtype=torch.uint8, device="cuda")  # 128 slots of 32 KB: stays in L2
     sink = torch.zeros(1, dtype=torch.float32, device="cuda")
     steps = 20000
-    names = ["mfma only", "+ fragment reads", "+ barrier per step", "+ direct loads", "direct loads, no barrier"]
+    names = ["mfma only", "+ fragment reads", "+ barrier per step", "+ direct loads", "direct loads, no barrier",
+             "direct loads as global_load_lds"]
     for v, name in enumerate(names):
         with torch.cuda.stream(stream):
             lib.moe_mfma_pipe_probe(v, steps // 10, src, sink, stream)

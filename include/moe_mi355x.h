@@ -359,13 +359,15 @@ moe_status moe_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, voi
  *   0  nothing (the MFMA rate alone);
  *   1  the tile kernel's 12 16-byte LDS fragment reads per wave and step;
  *   2  one workgroup barrier per step;
- *   3  its direct loads (global_load_lds, 4 x 1 KB per wave and step, 32 KB
- *      per workgroup) from src, with a wait for the loads two steps old;
- *   4  variant 3 without the barrier.
- * src (variants 3, 4): device, 16-byte aligned, src_bytes a nonzero multiple
+ *   3  its direct loads (buffer_load ... lds, 4 x 1 KB per wave and step,
+ *      32 KB per workgroup) from src, with a wait for the loads two steps old;
+ *   4  variant 3 without the barrier;
+ *   5  variant 3 with the loads as global_load_lds (with these in flight the
+ *      compiler waits for every LDS operation before each MFMA).
+ * src (variants 3-5): device, 16-byte aligned, src_bytes a nonzero multiple
  * of 32768 (at most 2^20 slots), read in 32 KB slots; ignored by variants
  * 0-2 (may be NULL).  sink: a device float, written only in a case that does
- * not arise.  MOE_ERR_SHAPE for a variant outside 0-4 or steps outside
+ * not arise.  MOE_ERR_SHAPE for a variant outside 0-5 or steps outside
  * [1, 2^24]; errors are reported before any launch.
  * --------------------------------------------------------------------------- */
 moe_status moe_mfma_pipe_probe(int32_t variant, int32_t steps, const void* src, size_t src_bytes, float* sink,

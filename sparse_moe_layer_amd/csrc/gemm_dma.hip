@@ -12,10 +12,14 @@
 // and the second half the up rows of the same hidden columns, so SiLU(g) * u
 // is formed in registers.
 //
-// Operands move HBM/L2 -> LDS with gfx950's direct loads (global_load_lds,
-// 16 bytes per lane, no VGPR staging) into statically separate stage buffers
-// (A rows, then B rows), four stages, loads three K steps ahead; waits are
-// explicit s_waitcnt vmcnt + s_barrier.  A stage holds a 32-wide K slice,
+// Operands move HBM/L2 -> LDS with gfx950's direct loads (buffer_load ... lds
+// through a buffer resource per operand, 16 bytes per lane, no VGPR staging)
+// into statically separate stage buffers (A rows, then B rows), four stages,
+// loads three K steps ahead and issued first in each step; waits are
+// explicit s_waitcnt vmcnt + s_barrier.  With bf16 weights the second K
+// sub-step of a stage is carried: its fragments are read during the first
+// sub-step's MFMAs and its MFMAs run after the next barrier, while the next
+// stage's first fragments are read, so no stage starts on an LDS wait.  A stage holds a 32-wide K slice,
 // [row][4 chunks of 16 B], chunk c of row r at position c ^ ((r >> 2) & 3):
 // a half-wave's 16-byte fragment reads cover 16 rows and 64 banks span four
 // 64-byte rows, so the XOR spreads them over all banks.  (The template also
@@ -68,18 +72,21 @@ using BigCfg = Cfg<256, 256, 2, 4, 4, 1>;
 using BigCfg8 = Cfg<256, 256, 2, 4, 4, 1, 32, true>;
 
 constexpr int vmcnt_imm(int n) { return 0xF70 | (n & 15) | (((n >> 4) & 3) << 14); }
+// the same wait, and for every LDS operation of this wave
+constexpr int vmcnt_lgkm0_imm(int n) { return vmcnt_imm(n) & ~0xF00; }
 
 // A 16-byte direct load (global memory to LDS, no registers) through a
-// buffer resource over base, at byte offset off < 2^32 (the layer checks keep
-// every element offset below 2^31).  The compiler counts buffer loads to LDS
+// buffer resource over base, at byte offset voff + soff < 2^32 (the layer
+// checks keep every element offset below 2^31); soff is wave-uniform (the K
+// step), voff the lane's row and chunk.  The compiler counts buffer loads to LDS
 // apart from LDS reads, so fragment reads keep partial LDS waits; with the
 // global_load_lds form in flight it waits for every outstanding LDS operation
 // before each MFMA that consumes a fragment.
 constexpr int kBufferFlags = 0x00020000;  // raw (untyped) 32-bit buffer access
-__device__ __forceinline__ void dma16b(const void* base, uint32_t off, bf16* l) {
+__device__ __forceinline__ void dma16b(const void* base, uint32_t voff, uint32_t soff, bf16* l) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0xFFFFFFFF,
                                                                       kBufferFlags);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 16, off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 16, voff, soff, 0, 0);
 }
 
 // Compiler-level fence around the raw s_barrier (the barrier builtin itself
@@ -103,14 +110,14 @@ template <class C>
 __device__ __forceinline__ void issue_stage(bf16* st, const bf16* abase, const uint32_t* aoff,
                                             const bf16* const* bbase, const uint32_t* boff, uint32_t k0, int wave) {
 #pragma unroll
-  for (int i = 0; i < C::LA; ++i) dma16b(abase, (aoff[i] + k0) * 2u, st + (C::NW * i + wave) * 512);
+  for (int i = 0; i < C::LA; ++i) dma16b(abase, aoff[i] * 2u, k0 * 2u, st + (C::NW * i + wave) * 512);
 #pragma unroll
   for (int i = 0; i < C::LB; ++i) {
     // fp8: bbase holds byte pointers, boff byte offsets (k0 counts codes)
     if constexpr (C::F8)
-      dma16b(bbase[i], boff[i] + k0, st + C::BM * C::BK + (C::NW * i + wave) * 512);
+      dma16b(bbase[i], boff[i], k0, st + C::BM * C::BK + (C::NW * i + wave) * 512);
     else
-      dma16b(bbase[i], (boff[i] + k0) * 2u, st + C::BM * C::BK + (C::NW * i + wave) * 512);
+      dma16b(bbase[i], boff[i] * 2u, k0 * 2u, st + C::BM * C::BK + (C::NW * i + wave) * 512);
   }
 }
 
@@ -144,6 +151,56 @@ __device__ __forceinline__ void load_frags(const bf16* st, int ks, const FragOff
 #pragma unroll
   for (int jj = 0; jj < C::NJ; ++jj)
     bfr[jj] = *reinterpret_cast<const bf16x8*>(st + o.b[ks] + jj * 32 * C::BK);
+}
+
+// bf16 fragments of one K sub-step held across a barrier: the stage's second
+// sub-step, whose MFMAs run at the start of the next stage (zero at a tile's
+// first stage, so there they add nothing).
+template <class C>
+constexpr bool kCarry = !C::F8 && C::BK == 32 && C::MI * C::NJ <= 8;
+
+template <class C, int NB>
+struct Carry {
+  bf16x8 a[NB], b[C::NJ];
+};
+
+template <class C, int NB>
+__device__ __forceinline__ void mfma_sub(f32x16 (&acc)[C::MI][C::NJ], const bf16x8* af, const bf16x8* bfr) {
+#pragma unroll
+  for (int ii = 0; ii < NB; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < C::NJ; ++jj)
+      acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ii], bfr[jj], acc[ii][jj], 0, 0, 0);
+}
+
+// bf16 stage with the second sub-step carried: the first sub-step's fragment
+// reads run under the previous stage's carried MFMAs, the second sub-step's
+// reads under the first sub-step's MFMAs, so no stage starts on an LDS wait.
+template <class C, int NB>
+__device__ __forceinline__ void compute_stage_carry(f32x16 (&acc)[C::MI][C::NJ], const bf16* st, const FragOff& o,
+                                                    Carry<C, NB>& cy) {
+  static_assert(C::BK == 32 && !C::F8, "two bf16 K sub-steps per stage");
+  bf16x8 af[NB], bfr[C::NJ];
+  load_frags<C, NB>(st, 0, o, af, bfr);
+  mfma_sub<C, NB>(acc, cy.a, cy.b);
+  mfma_sub<C, NB>(acc, af, bfr);
+  load_frags<C, NB>(st, 1, o, cy.a, cy.b);
+  constexpr int NR = NB + C::NJ;  // fragment reads per sub-step
+  constexpr int NM = NB * C::NJ;  // MFMAs per sub-step
+  constexpr int NP = NR < NM ? NR : NM;
+  // the stage's direct loads (issued just before) go out first, for the
+  // longest lead
+  __builtin_amdgcn_sched_group_barrier(0x010, C::L, 0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    if constexpr (NR > NP) __builtin_amdgcn_sched_group_barrier(0x100, NR - NP, 0);
+    if constexpr (NM > NP) __builtin_amdgcn_sched_group_barrier(0x008, NM - NP, 0);
+  }
 }
 
 // MFMAs of one stage: 2 K sub-steps of 16, fragments of both loaded first.
@@ -250,16 +307,27 @@ template <class C, int NB, int B>
 __device__ __forceinline__ void step(f32x16 (&acc)[C::MI][C::NJ], bf16* const* stg, const bf16* abase,
                                      const uint32_t* aoff, const bf16* const* bbase, const uint32_t* boff, int s,
                                      uint32_t klast, int wave, const FragOff& o, const float* sc0,
-                                     const float* sc1, float& scl0, float& scl1) {
+                                     const float* sc1, float& scl0, float& scl1, Carry<C, NB>& cy) {
   if constexpr (C::F8 && B == 0) {
     scl0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sc0[s >> 2])));
     scl1 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sc1[s >> 2])));
   }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm((C::S - 2) * C::L));
-  block_sync();
+  // carried reads of buffer b-1 must be done before any wave refills it
+  if constexpr (kCarry<C>) {
+    // nothing of the previous stage (its last MFMAs cover its last reads)
+    // moves past the wait and barrier
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((C::S - 2) * C::L));
+    block_sync();
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((C::S - 2) * C::L));
+    block_sync();
+  }
   const uint32_t kn = (uint32_t)(s + C::S - 1) * C::BK;
   issue_stage<C>(stg[(B + C::S - 1) % C::S], abase, aoff, bbase, boff, kn < klast ? kn : klast, wave);
-  compute_stage<C, NB>(acc, stg[B], o, scl0, scl1);
+  if constexpr (kCarry<C>) compute_stage_carry<C, NB>(acc, stg[B], o, cy);
+  else compute_stage<C, NB>(acc, stg[B], o, scl0, scl1);
 }
 
 // The K loop of one tile over nk steps, nk % S == R: step s uses buffer s % S.
@@ -269,6 +337,11 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::MI][C::NJ], bf16* cons
                                          int nk, int wave, const FragOff& o, const float* sc0, const float* sc1) {
   const uint32_t klast = (uint32_t)(nk - 1) * C::BK;
   float scl0 = 0.f, scl1 = 0.f;  // fp8: the current K block's scales
+  Carry<C, NB> cy;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) cy.a[i] = bf16x8{};
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) cy.b[j] = bf16x8{};
   // every wave's loads (vmcnt(0) before the call) and LDS reads of the
   // previous tile are finished before its buffers are refilled
   block_sync();
@@ -279,18 +352,19 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::MI][C::NJ], bf16* cons
   }
   const int nfull = nk - R;
   for (int kt = 0; kt < nfull; kt += C::S) {
-    step<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, kt + 0, klast, wave, o, sc0, sc1, scl0, scl1);
-    step<C, NB, 1>(acc, stg, abase, aoff, bbase, boff, kt + 1, klast, wave, o, sc0, sc1, scl0, scl1);
-    if constexpr (C::S > 2) step<C, NB, 2>(acc, stg, abase, aoff, bbase, boff, kt + 2, klast, wave, o, sc0, sc1, scl0, scl1);
-    if constexpr (C::S > 3) step<C, NB, 3>(acc, stg, abase, aoff, bbase, boff, kt + 3, klast, wave, o, sc0, sc1, scl0, scl1);
-    if constexpr (C::S > 4) step<C, NB, 4>(acc, stg, abase, aoff, bbase, boff, kt + 4, klast, wave, o, sc0, sc1, scl0, scl1);
-    if constexpr (C::S > 5) step<C, NB, 5>(acc, stg, abase, aoff, bbase, boff, kt + 5, klast, wave, o, sc0, sc1, scl0, scl1);
+    step<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, kt + 0, klast, wave, o, sc0, sc1, scl0, scl1, cy);
+    step<C, NB, 1>(acc, stg, abase, aoff, bbase, boff, kt + 1, klast, wave, o, sc0, sc1, scl0, scl1, cy);
+    if constexpr (C::S > 2) step<C, NB, 2>(acc, stg, abase, aoff, bbase, boff, kt + 2, klast, wave, o, sc0, sc1, scl0, scl1, cy);
+    if constexpr (C::S > 3) step<C, NB, 3>(acc, stg, abase, aoff, bbase, boff, kt + 3, klast, wave, o, sc0, sc1, scl0, scl1, cy);
+    if constexpr (C::S > 4) step<C, NB, 4>(acc, stg, abase, aoff, bbase, boff, kt + 4, klast, wave, o, sc0, sc1, scl0, scl1, cy);
+    if constexpr (C::S > 5) step<C, NB, 5>(acc, stg, abase, aoff, bbase, boff, kt + 5, klast, wave, o, sc0, sc1, scl0, scl1, cy);
   }
-  if constexpr (R > 0) step<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, nfull + 0, klast, wave, o, sc0, sc1, scl0, scl1);
-  if constexpr (R > 1) step<C, NB, 1>(acc, stg, abase, aoff, bbase, boff, nfull + 1, klast, wave, o, sc0, sc1, scl0, scl1);
-  if constexpr (R > 2) step<C, NB, 2>(acc, stg, abase, aoff, bbase, boff, nfull + 2, klast, wave, o, sc0, sc1, scl0, scl1);
-  if constexpr (R > 3) step<C, NB, 3>(acc, stg, abase, aoff, bbase, boff, nfull + 3, klast, wave, o, sc0, sc1, scl0, scl1);
-  if constexpr (R > 4) step<C, NB, 4>(acc, stg, abase, aoff, bbase, boff, nfull + 4, klast, wave, o, sc0, sc1, scl0, scl1);
+  if constexpr (R > 0) step<C, NB, 0>(acc, stg, abase, aoff, bbase, boff, nfull + 0, klast, wave, o, sc0, sc1, scl0, scl1, cy);
+  if constexpr (R > 1) step<C, NB, 1>(acc, stg, abase, aoff, bbase, boff, nfull + 1, klast, wave, o, sc0, sc1, scl0, scl1, cy);
+  if constexpr (R > 2) step<C, NB, 2>(acc, stg, abase, aoff, bbase, boff, nfull + 2, klast, wave, o, sc0, sc1, scl0, scl1, cy);
+  if constexpr (R > 3) step<C, NB, 3>(acc, stg, abase, aoff, bbase, boff, nfull + 3, klast, wave, o, sc0, sc1, scl0, scl1, cy);
+  if constexpr (R > 4) step<C, NB, 4>(acc, stg, abase, aoff, bbase, boff, nfull + 4, klast, wave, o, sc0, sc1, scl0, scl1, cy);
+  if constexpr (kCarry<C>) mfma_sub<C, NB>(acc, cy.a, cy.b);
 }
 
 template <class C, int NB>

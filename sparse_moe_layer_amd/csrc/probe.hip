@@ -13,10 +13,13 @@
 //   0: nothing else;
 //   1: the tile kernel's fragment reads, 12 ds_read_b128 per step;
 //   2: 1 and one workgroup barrier per step;
-//   3: 2 and the tile kernel's direct loads, 4 global_load_lds of 1 KB per
-//      wave per step (32 KB per workgroup) from an L2-resident buffer, the
-//      barrier preceded by a wait for the loads two steps old;
-//   4: 3 without the barrier (the same loads and waits).
+//   3: 2 and the tile kernel's direct loads, 4 buffer_load ... lds of 1 KB
+//      per wave per step (32 KB per workgroup) from an L2-resident buffer,
+//      the barrier preceded by a wait for the loads two steps old;
+//   4: 3 without the barrier (the same loads and waits);
+//   5: 3 with the loads as global_load_lds, the form with which the compiler
+//      waits for every outstanding LDS operation before an MFMA that uses a
+//      fragment.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -55,7 +58,7 @@ constexpr int pipe_vmcnt(int n) { return 0xF70 | (n & 15) | (((n >> 4) & 3) << 1
 template <int V>
 __global__ __launch_bounds__(kPipeWaves * 64, 1) void mfma_pipe_probe_kernel(const char* __restrict__ src,
                                                                              int nslots, int steps, float* sink) {
-  constexpr bool READS = V >= 1, BAR = V == 2 || V == 3, DMA = V >= 3;
+  constexpr bool READS = V >= 1, BAR = V == 2 || V == 3 || V == 5, DMA = V >= 3, FLAT = V == 5;
   __shared__ __attribute__((aligned(1024))) char frag[kPipeSlot];
   __shared__ __attribute__((aligned(1024))) char land[DMA ? 4 : 1][DMA ? kPipeSlot : 16];
   const int lane = threadIdx.x & 63;
@@ -85,10 +88,21 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void mfma_pipe_probe_kernel(con
     if constexpr (DMA) {
       // slot ((workgroup * 7 + s) mod nslots): 1 KB per wave and load, the
       // workgroup's four loads per wave covering the 32 KB slot
-      const char* g = src + (int64_t)((blockIdx.x * 7 + s) % nslots) * kPipeSlot + wave * 1024 + lane * 16;
+      const char* slot = src + (int64_t)((blockIdx.x * 7 + s) % nslots) * kPipeSlot;
       char* d = land[s & 3] + wave * 1024;
+      if constexpr (FLAT) {
+        const char* g = slot + wave * 1024 + lane * 16;
 #pragma unroll
-      for (int l = 0; l < 4; ++l) __builtin_amdgcn_global_load_lds(g + l * 8192, d + l * 8192, 16, 0, 0);
+        for (int l = 0; l < 4; ++l) __builtin_amdgcn_global_load_lds(g + l * 8192, d + l * 8192, 16, 0, 0);
+      } else {
+        // raw (untyped) buffer over the slot
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(slot), 0, kPipeSlot, 0x00020000);
+#pragma unroll
+        for (int l = 0; l < 4; ++l)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(d + l * 8192), 16,
+                                                   (uint32_t)(wave * 1024 + lane * 16 + l * 8192), 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -126,7 +140,7 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void mfma_pipe_probe_kernel(con
 extern "C" moe_status moe_mfma_pipe_probe(int32_t variant, int32_t steps, const void* src, size_t src_bytes,
                                           float* sink, void* stream) {
   if (!sink) return MOE_ERR_NULL;
-  if (variant < 0 || variant > 4 || steps < 1 || steps > (1 << 24)) return MOE_ERR_SHAPE;
+  if (variant < 0 || variant > 5 || steps < 1 || steps > (1 << 24)) return MOE_ERR_SHAPE;
   int nslots = 1;
   if (variant >= 3) {
     if (!src) return MOE_ERR_NULL;
@@ -147,7 +161,8 @@ extern "C" moe_status moe_mfma_pipe_probe(int32_t variant, int32_t steps, const 
     case 1: moe::mfma_pipe_probe_kernel<1><<<cus, nt, 0, st>>>(s, nslots, steps, sink); break;
     case 2: moe::mfma_pipe_probe_kernel<2><<<cus, nt, 0, st>>>(s, nslots, steps, sink); break;
     case 3: moe::mfma_pipe_probe_kernel<3><<<cus, nt, 0, st>>>(s, nslots, steps, sink); break;
-    default: moe::mfma_pipe_probe_kernel<4><<<cus, nt, 0, st>>>(s, nslots, steps, sink); break;
+    case 4: moe::mfma_pipe_probe_kernel<4><<<cus, nt, 0, st>>>(s, nslots, steps, sink); break;
+    default: moe::mfma_pipe_probe_kernel<5><<<cus, nt, 0, st>>>(s, nslots, steps, sink); break;
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -218,7 +218,7 @@ def test_measurement_probes_validate_before_launch():
     assert L.moe_hbm_read_probe(ctypes.c_void_p(0x10008), 16, fake, None) == _lib.MOE_ERR_ALIGN
     assert L.moe_hbm_read_probe(fake, 24, fake, None) == _lib.MOE_ERR_ALIGN
     assert L.moe_mfma_pipe_probe(0, 10, None, 0, None, None) == _lib.MOE_ERR_NULL
-    for variant, steps in ((-1, 10), (5, 10), (0, 0), (2, (1 << 24) + 1)):
+    for variant, steps in ((-1, 10), (6, 10), (0, 0), (2, (1 << 24) + 1)):
         assert L.moe_mfma_pipe_probe(variant, steps, None, 0, fake, None) == _lib.MOE_ERR_SHAPE
     assert L.moe_mfma_pipe_probe(3, 10, None, 32768, fake, None) == _lib.MOE_ERR_NULL
     assert L.moe_mfma_pipe_probe(4, 10, ctypes.c_void_p(0x10008), 32768, fake, None) == _lib.MOE_ERR_ALIGN

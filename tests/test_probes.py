@@ -22,7 +22,7 @@ def test_mfma_pipe_probe_variants():
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     src = torch.zeros(4 << 20, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(1, dtype=torch.float32, device="cuda")
-    for v in range(5):
+    for v in range(6):
         lib.moe_mfma_pipe_probe(v, 100, src, sink)
     torch.cuda.synchronize()
     assert float(sink.item()) == 0.0
