@@ -16,8 +16,8 @@
 // through a buffer resource per operand, 16 bytes per lane, no VGPR staging)
 // into statically separate stage buffers (A rows, then B rows), four stages,
 // loads three K steps ahead and issued first in each step; waits are
-// explicit s_waitcnt vmcnt + s_barrier.  With bf16 weights the second K
-// sub-step of a stage is carried: its fragments are read during the first
+// explicit s_waitcnt vmcnt + s_barrier.  The second K sub-step of a stage
+// is carried (fp8: decoded first): its fragments are read during the first
 // sub-step's MFMAs and its MFMAs run after the next barrier, while the next
 // stage's first fragments are read, so no stage starts on an LDS wait.  A stage holds a 32-wide K slice,
 // [row][4 chunks of 16 B], chunk c of row r at position c ^ ((r >> 2) & 3):
@@ -157,7 +157,7 @@ __device__ __forceinline__ void load_frags(const bf16* st, int ks, const FragOff
 // sub-step, whose MFMAs run at the start of the next stage (zero at a tile's
 // first stage, so there they add nothing).
 template <class C>
-constexpr bool kCarry = !C::F8 && C::BK == 32 && C::MI * C::NJ <= 8;
+constexpr bool kCarry = C::BK == 32 && C::MI * C::NJ <= 8;
 
 template <class C, int NB>
 struct Carry {
@@ -200,6 +200,53 @@ __device__ __forceinline__ void compute_stage_carry(f32x16 (&acc)[C::MI][C::NJ],
     }
     if constexpr (NR > NP) __builtin_amdgcn_sched_group_barrier(0x100, NR - NP, 0);
     if constexpr (NM > NP) __builtin_amdgcn_sched_group_barrier(0x008, NM - NP, 0);
+  }
+}
+
+// fp8 stage with the second sub-step carried, as above: the carried
+// fragments are decoded (with this stage's block scales) before they are
+// carried.  B block jj: 8 codes of row (lane % 32) at K 16*ks + 8*(lane/32),
+// in chunk ks of its 32-row block; block 0 takes scale sc0, block 1 sc1.
+template <class C, int NB>
+__device__ __forceinline__ void compute_stage_carry8(f32x16 (&acc)[C::MI][C::NJ], const bf16* st, const FragOff& o,
+                                                     float sc0, float sc1, Carry<C, NB>& cy) {
+  static_assert(C::BK == 32 && C::F8, "two fp8 K sub-steps per stage");
+  const char* sb = reinterpret_cast<const char*>(st) + o.b8;
+  bf16x8 af[NB], bfr[C::NJ];
+  u32x2 c0[C::NJ], c1[C::NJ];
+#pragma unroll
+  for (int jj = 0; jj < C::NJ; ++jj) c0[jj] = *reinterpret_cast<const u32x2*>(sb + jj * 1024);
+#pragma unroll
+  for (int ii = 0; ii < NB; ++ii) af[ii] = *reinterpret_cast<const bf16x8*>(st + o.a[0] + ii * C::WM * 32 * C::BK);
+#pragma unroll
+  for (int jj = 0; jj < C::NJ; ++jj)
+    bfr[jj] = __builtin_bit_cast(bf16x8, fp8x8_to_bf16x8(c0[jj], jj == 0 ? sc0 : sc1));
+  mfma_sub<C, NB>(acc, cy.a, cy.b);
+  mfma_sub<C, NB>(acc, af, bfr);
+#pragma unroll
+  for (int jj = 0; jj < C::NJ; ++jj) c1[jj] = *reinterpret_cast<const u32x2*>(sb + jj * 1024 + 512);
+#pragma unroll
+  for (int ii = 0; ii < NB; ++ii) cy.a[ii] = *reinterpret_cast<const bf16x8*>(st + o.a[1] + ii * C::WM * 32 * C::BK);
+#pragma unroll
+  for (int jj = 0; jj < C::NJ; ++jj)
+    cy.b[jj] = __builtin_bit_cast(bf16x8, fp8x8_to_bf16x8(c1[jj], jj == 0 ? sc0 : sc1));
+  // Schedule: direct loads first; the carried MFMAs with the first
+  // sub-step's reads, then its decode over their second half; the first
+  // sub-step's MFMAs with the second sub-step's reads and decode likewise.
+  constexpr int NR = NB + C::NJ;  // fragment reads per sub-step
+  constexpr int NM = NB * C::NJ;  // MFMAs per sub-step
+  constexpr int NV = 16 * C::NJ;  // decode instructions per sub-step
+  constexpr int NH = NM - NM / 2; // MFMAs that the decode spreads over
+  __builtin_amdgcn_sched_group_barrier(0x010, C::L, 0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i >= NM / 2) __builtin_amdgcn_sched_group_barrier(0x002, NV / NH, 0);
+    }
+    if constexpr (NR > NM) __builtin_amdgcn_sched_group_barrier(0x100, NR - NM, 0);
   }
 }
 
@@ -326,7 +373,8 @@ __device__ __forceinline__ void step(f32x16 (&acc)[C::MI][C::NJ], bf16* const* s
   }
   const uint32_t kn = (uint32_t)(s + C::S - 1) * C::BK;
   issue_stage<C>(stg[(B + C::S - 1) % C::S], abase, aoff, bbase, boff, kn < klast ? kn : klast, wave);
-  if constexpr (kCarry<C>) compute_stage_carry<C, NB>(acc, stg[B], o, cy);
+  if constexpr (kCarry<C> && C::F8) compute_stage_carry8<C, NB>(acc, stg[B], o, scl0, scl1, cy);
+  else if constexpr (kCarry<C>) compute_stage_carry<C, NB>(acc, stg[B], o, cy);
   else compute_stage<C, NB>(acc, stg[B], o, scl0, scl1);
 }
 
