@@ -338,6 +338,19 @@ def test_small_batch_fused_route_and_dispatch(T, E, k, H, Is):
     check(p, g)
 
 
+@pytest.mark.parametrize("T,E,k,H,I,Is", [(16, 64, 8, 200, 8, 24), (3, 20, 2, 96, 16, 0), (9, 33, 33, 40, 24, 8),
+                                           (16, 400, 24, 128, 32, 16)])
+def test_small_batch_layer_edge_shapes(T, E, k, H, I, Is):
+    # T <= 16, bf16 (the dispatch from the gate/up streaming launch): one
+    # gate/up item per group (I = 8), a shared expert wider than the routed
+    # ones, no shared expert, every expert touched (k = E), output columns
+    # that end inside a down item (H % 32 != 0), 384 assignments over up to
+    # 400 groups.  The layer call must give the stage calls' bits.
+    cfg = CONFIGS["flash_decode"].with_(name=f"small_edge_T{T}_E{E}_k{k}", T=T, H=H, E=E, k=k, I=I, I_shared=Is)
+    p = gpu_problem(cfg, 41 + T)
+    check(p, run_stages(p))
+
+
 @pytest.mark.parametrize("case", ["f32", "fp8", "gemm"])
 def test_small_batch_dispatch_from_topk(case):
     # T <= 16 with fp32 activations, fp8 weights or the GEMM path forced: the
