@@ -9,9 +9,11 @@
  *   out_t       = sum_{j<k} w[t,j] expert_{ids[t,j]}(x_t)
  *                 + sigmoid(w_sg . x_t) * shared(x_t)
  *
- * computed in the stage order of that section's pipeline figure:
- *   Router [T,E] -> top-k + normalise -> dispatch R = k*T assignments ->
- *   grouped expert GEMMs -> weighted combine + gated shared expert.
+ * computed in the five stages of that section's pipeline figure: router
+ * logits over the E experts, the k best per token with their weights
+ * rescaled to sum to one, dispatch of the R = k*T (token, expert) pairs into
+ * per-expert groups, the grouped expert products, and the weighted combine
+ * with the gated shared expert.
  * One entry point per stage, plus the whole layer in one call.
  *
  * Conventions for every entry point
