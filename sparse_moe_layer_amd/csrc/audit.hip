@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kHistThreads) void audit_hist_kernel(const uint16_t
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t cu = c + (int64_t)u * kHistThreads;
-        v[u] = cu < nch ? q[cu] : u32x4{0x3F80u, 0x3F80u, 0x3F80u, 0x3F80u};  // placeholder, skipped below
+        v[u] = cu < nch ? __builtin_nontemporal_load(q + cu) : u32x4{0x3F80u, 0x3F80u, 0x3F80u, 0x3F80u};  // placeholder, skipped below
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {

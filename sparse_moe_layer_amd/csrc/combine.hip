@@ -3,7 +3,8 @@
 //   out[t] = sum_{j<k} w[t,j] * y[pos[t*k+j]] + sigmoid(s_t) * y_shared[t]
 // 16-byte loads of y rows (8 bf16 or 4 fp32 per thread), fp32 accumulation
 // with j ascending, one rounding to the output dtype.  HBM-bound: reads k+1
-// rows of H and writes one.
+// rows of H and writes one.  Every row is read once, so the loads are
+// non-temporal (2.4T-shape prefill combine 0.321 -> 0.273 ms).
 //
 // With the gated residual around the layer (same study, "Gated residual:
 // four streams, one sublayer input"), the stream write R'_i = R_i + s_i F(x)
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   u32x4 r[GRW ? STREAMS : 1];
   if constexpr (GRW) {
 #pragma unroll
-    for (int i = 0; i < STREAMS; ++i) r[i] = ld16(resid + ((int64_t)t * STREAMS + i) * H + col);
+    for (int i = 0; i < STREAMS; ++i) r[i] = ld16_nt(resid + ((int64_t)t * STREAMS + i) * H + col);
   }
   float acc[VEC];
 #pragma unroll
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   if constexpr (KB > 0) {
     // without a shared expert its load reads row 0 of y instead (unused)
     const char* shp = y_sh ? reinterpret_cast<const char*>(y_sh) + (int64_t)t * H * ESZ : yb;
-    const u32x4 vsh = ld16(shp + col * ESZ);
+    const u32x4 vsh = ld16_nt(shp + col * ESZ);
     int64_t row[KB];
     float wj[KB];
 #pragma unroll
@@ -79,19 +80,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     }
     u32x4 v[KB];
 #pragma unroll
-    for (int b = 0; b < KB; ++b) v[b] = ld16(yb + (row[b] + col) * ESZ);
+    for (int b = 0; b < KB; ++b) v[b] = ld16_nt(yb + (row[b] + col) * ESZ);
 #pragma unroll
     for (int b = 0; b < KB; ++b)
       if (b < k) accumulate<F32>(acc, wj[b], v[b]);
     if (y_sh) accumulate<F32>(acc, sigmoid(sl[t]), vsh);
   } else {
     u32x4 vsh = {0, 0, 0, 0};
-    if (y_sh) vsh = ld16(reinterpret_cast<const char*>(y_sh) + ((int64_t)t * H + col) * ESZ);
+    if (y_sh) vsh = ld16_nt(reinterpret_cast<const char*>(y_sh) + ((int64_t)t * H + col) * ESZ);
     for (int j0 = 0; j0 < k; j0 += 16) {
       u32x4 v[16];
 #pragma unroll
       for (int b = 0; b < 16; ++b)
-        if (j0 + b < k) v[b] = ld16(yb + ((int64_t)pt[j0 + b] * H + col) * ESZ);
+        if (j0 + b < k) v[b] = ld16_nt(yb + ((int64_t)pt[j0 + b] * H + col) * ESZ);
 #pragma unroll
       for (int b = 0; b < 16; ++b)
         if (j0 + b < k) accumulate<F32>(acc, wt[j0 + b], v[b]);

@@ -30,6 +30,11 @@ __device__ __forceinline__ float silu(float z) { return z * sigmoid(z); }
 // 16-byte global load / store helpers (addresses must be 16-byte aligned).
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// A 16-byte load marked non-temporal (data read once: streamed expert
+// weights), so it does not displace lines that are read again.
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 // Eight OCP e4m3fn codes (two dwords) times one fp32 scale -> eight bf16.
 // gfx950's v_cvt_pk_f32_fp8 decodes the OCP E4M3FN format.

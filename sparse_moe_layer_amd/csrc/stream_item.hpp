@@ -6,8 +6,10 @@
 // registers, re-laid into
 // v_mfma_f32_16x16x32_bf16 fragments through a wave-private LDS stage (no
 // barriers), and multiplied by the group's (at most 16) activation rows,
-// which come from L2.  fp8 codes are decoded with their 128 x 128 block scale
-// as fragments leave LDS.
+// which come from L2.  Each weight byte is read once, so the weight loads are
+// non-temporal, which measured faster (16-token decode: gate/up 154 -> 142.5
+// us, down 81 -> 73 us).  fp8 codes are decoded with their 128 x 128 block
+// scale as fragments leave LDS.
 //   gate/up item: 16 hidden columns (16 gate rows + 16 up rows), SiLU*mul in
 //                 registers; SPLIT: 8 columns (8 gate + 8 up rows in one block)
 //   down item   : 32 output columns (2 blocks of 16 W_down rows)
@@ -75,10 +77,10 @@ __device__ __forceinline__ void stream_dot_lds(const bf16* a_row, const bf16* a_
         if constexpr (SPLIT) {
           const int half = i >> 2, rh = (2 * i + h) & 7;  // rows 0-7: first half, 8-15: second
           const int r = rh < nvalid[half] ? rh : nvalid[half] - 1;
-          wb[x][i] = ld16(wrow0[half] + (live ? (uint32_t)(r * ldw + k) : 0u));
+          wb[x][i] = ld16_nt(wrow0[half] + (live ? (uint32_t)(r * ldw + k) : 0u));
         } else {
           const int r = 2 * i + h < nvalid[j] ? 2 * i + h : nvalid[j] - 1;
-          wb[x][j * 8 + i] = ld16(wrow0[j] + (live ? (uint32_t)(r * ldw + k) : 0u));
+          wb[x][j * 8 + i] = ld16_nt(wrow0[j] + (live ? (uint32_t)(r * ldw + k) : 0u));
         }
       }
   };
@@ -191,7 +193,7 @@ __device__ __forceinline__ void stream_dot_lds8(const bf16* a_row, const bf16* a
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * i + q4 < nvalid[j] ? 4 * i + q4 : nvalid[j] - 1;
-        wb[j * 4 + i] = ld16(wrow0[j] + (uint32_t)(r * ldw + k));
+        wb[j * 4 + i] = ld16_nt(wrow0[j] + (uint32_t)(r * ldw + k));
       }
   };
   auto load_a = [&](int x, int b) {
