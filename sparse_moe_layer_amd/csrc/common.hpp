@@ -30,8 +30,11 @@ __device__ __forceinline__ float silu(float z) { return z * sigmoid(z); }
 // 16-byte global load / store helpers (addresses must be 16-byte aligned).
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
-// A 16-byte load marked non-temporal (data read once: streamed expert
-// weights), so it does not displace lines that are read again.
+// 16-byte accesses marked non-temporal: data read once (streamed expert
+// weights) or written once and read back only by a later launch.
+__device__ __forceinline__ void st16_nt(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 __device__ __forceinline__ u32x4 ld16_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
