@@ -728,11 +728,14 @@ hipError_t launch(const FfnArgs& a, int phase, hipStream_t s, int tb, int te, in
   const int wide = a.I > a.Is ? a.I : a.Is;
   const int ntn = phase == 1 ? (wide + C::BN / 2 - 1) / (C::BN / 2) : (a.H + C::BN - 1) / C::BN;
   const int grid = (cu_count() * C::WG_PER_CU + 7) / 8 * 8;  // resident workgroups, a multiple of 8 XCDs
-  // Each XCD takes grid/8 consecutive tiles of a round: supertiles of 8
-  // m-tiles, so an expert's weight slice serves up to 8 of its m-tiles from
-  // L2.  (Two m-tiles x all n-tiles per XCD, which fetches each A slice once,
-  // measured slower on the 8192-token skewed layer.)
-  const int super = 8;
+  // Each XCD takes grid/8 consecutive tiles of a round: supertiles of 4
+  // m-tiles, so an XCD's 28 or 32 tiles at a time are about 4 m-tiles x 7-8
+  // n-tiles, each weight slice serving 4 m-tiles and each A slice 7-8 n-tiles
+  // from L2.  On the 8192-token skewed layer 4 measured 1.6% faster than 8
+  // (10.86-10.88 against 11.02-11.08 ms per step) and within noise of 2 and
+  // 3; 1 and 16 were slower.  (Two m-tiles x all n-tiles per XCD, which
+  // fetches each A slice once, measured slower too.)
+  const int super = 4;
   int32_t* ctr = const_cast<int32_t*>(a.plan) + kPlanCounters + (ctr_block * 2 + phase - 1) * 8;
   reserve = reserve < grid - 8 ? reserve / 8 * 8 : 0;
   if (phase == 1) ffn_tiles_kernel<C, 1><<<grid, C::NT, 0, s>>>(a, ntn, super, tb, te, ctr, reserve);
