@@ -55,6 +55,20 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 codes, float scale) {
   return out;
 }
 
+// Eight OCP e4m3fn codes -> eight bf16, exactly (every e4m3fn value is a
+// bf16 value): gfx950's scaled conversion at scale 1.0, two codes per
+// instruction.  (Its scale operand contributes only its power-of-two
+// exponent, so a block scale cannot be folded in here.)
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8_exact(u32x2 codes) {
+  u32x4 out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    out[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[h], 1.0f, false));
+    out[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[h], 1.0f, true));
+  }
+  return out;
+}
+
 // Wave-wide reductions (64 lanes).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -165,9 +165,10 @@ __device__ __forceinline__ void stream_dot_lds(const bf16* a_row, const bf16* a_
 // Same scheme for e4m3fn codes: a batch holds SB8 = 256 K values (256 B) of
 // NB*16 weight rows; rows 2i and 2i+1 sit in 512 B at i * 528 B, odd rows
 // store chunk c at c ^ 8.  Each 16-byte-per-lane load covers 4 rows x 256
-// contiguous bytes.  Fragments are decoded when read from LDS: 8 codes times
-// the row's 128 x 128 block scale (s_row[j]: this lane's fragment row's scale
-// row, indexed by k / 128) to eight bf16.
+// contiguous bytes.  Fragments are converted when read from LDS (8 codes to
+// eight bf16, exactly), and each 128-wide K block's products are scaled by
+// the rows' 128 x 128 block scale (s_row[j]: this lane's fragment row's scale
+// row, indexed by k / 128) before they join the sums.
 constexpr int SB8 = 256;
 constexpr int PAIR8 = 528;
 
@@ -220,22 +221,35 @@ __device__ __forceinline__ void stream_dot_lds8(const bf16* a_row, const bf16* a
             wb[j * 4 + i];
       }
   };
+  // A batch is two 128-wide K blocks.  The codes convert exactly to bf16
+  // (every e4m3fn value is a bf16 value), the MFMAs of one K block add into
+  // part[j], and part[j] times the block's scale goes into acc[j]: one
+  // multiply-add per accumulator per K block instead of one multiply per
+  // weight (the 16 rows of a block share one 128-row scale block).
   auto compute = [&](int x, int b) {
     const int n = lane & 15;
     const int hn = n & 1;
 #pragma unroll
-    for (int s = 0; s < NA; ++s) {
-      const int kk = kbeg + b * SB8 + s * KSTEP + kq;
-      const u32x4 am = (a_row && kk < kend) ? av[x][s] : u32x4{0, 0, 0, 0};
-      const int byte = s * KSTEP + kq;  // offset in the 256-byte row run
-      const int cc = byte >> 4;
+    for (int h = 0; h < 2; ++h) {
+      f32x4 part[NB];
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const u32x2 codes = *reinterpret_cast<const u32x2*>(lds + (j * 8 + (n >> 1)) * PAIR8 + hn * 256 +
-                                                            ((cc ^ (hn << 3)) << 4) + (byte & 15));
-        const u32x4 bv = fp8x8_to_bf16x8(codes, sc[x][j][s >= NA / 2 ? 1 : 0]);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(am), as_bf16x8(bv), acc[j], 0, 0, 0);
+      for (int j = 0; j < NB; ++j) part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = h * (NA / 2); s < (h + 1) * (NA / 2); ++s) {
+        const int kk = kbeg + b * SB8 + s * KSTEP + kq;
+        const u32x4 am = (a_row && kk < kend) ? av[x][s] : u32x4{0, 0, 0, 0};
+        const int byte = s * KSTEP + kq;  // offset in the 256-byte row run
+        const int cc = byte >> 4;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const u32x2 codes = *reinterpret_cast<const u32x2*>(lds + (j * 8 + (n >> 1)) * PAIR8 + hn * 256 +
+                                                              ((cc ^ (hn << 3)) << 4) + (byte & 15));
+          const u32x4 bv = fp8x8_to_bf16x8_exact(codes);
+          part[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(am), as_bf16x8(bv), part[j], 0, 0, 0);
+        }
       }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[j] += sc[x][j][h] * part[j];
     }
   };
   load_w(0);
