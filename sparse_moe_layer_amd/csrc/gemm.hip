@@ -586,12 +586,22 @@ hipError_t launch_ffn_plan(const int32_t* offsets, const int32_t* sorted, int T,
 int router_gemm_split(int T, int H, int E) {
   // as many (m, n, K-chunk) tiles as fit in one round of resident workgroups
   // (two per CU): a split that spills a few tiles into a second round
-  // doubles the kernel's time.  Chunks are whole 64-wide K steps.
+  // doubles the kernel's time.  Up to 4 chunks, a split whose rounds cost
+  // less in K steps may take more than one round: the 8192-token router's
+  // 320 tiles run as 960 thirds in two rounds of 512 (router and top-k
+  // stage 0.208 -> 0.170 ms).  Chunks are whole 64-wide K steps.
   int tiles = ((T + BM - 1) / BM) * ((E + 1 + BN - 1) / BN);
   tiles = tiles < 1 ? 1 : tiles;  // an empty batch still sizes one split
-  int ns = (2 * num_cus()) / tiles;
+  const int slots = 2 * num_cus();
+  int ns = slots / tiles;
   const int maxs = H / (4 * BK) > 0 ? H / (4 * BK) : 1;
   ns = ns < 1 ? 1 : (ns > maxs ? maxs : ns);
+  // rounds / ns is the time in units of one whole-K tile; keep the
+  // one-round split unless a larger one is strictly cheaper
+  auto cost = [&](int n) { return (double)((tiles * n + slots - 1) / slots) / n; };
+  const int n1 = ns;
+  for (int n = n1 + 1; n <= 4 && n <= maxs; ++n)
+    if (cost(n) < cost(ns)) ns = n;
   int kchunk = (H + ns - 1) / ns;
   kchunk = (kchunk + BK - 1) / BK * BK;
   return (H + kchunk - 1) / kchunk;
