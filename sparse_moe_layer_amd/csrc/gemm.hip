@@ -583,13 +583,13 @@ hipError_t launch_ffn_plan(const int32_t* offsets, const int32_t* sorted, int T,
   return hipGetLastError();
 }
 
-int router_gemm_split(int T, int H, int E) {
+int router_gemm_split(int T, int H, int E, int max_split) {
   // as many (m, n, K-chunk) tiles as fit in one round of resident workgroups
   // (two per CU): a split that spills a few tiles into a second round
-  // doubles the kernel's time.  Up to 4 chunks, a split whose rounds cost
-  // less in K steps may take more than one round: the 8192-token router's
-  // 320 tiles run as 960 thirds in two rounds of 512 (router and top-k
-  // stage 0.208 -> 0.170 ms).  Chunks are whole 64-wide K steps.
+  // doubles the kernel's time.  Up to max_split chunks, a split whose rounds
+  // cost less in K steps may take more than one round: the 8192-token
+  // router's 320 tiles run as 960 thirds in two rounds of 512 (router and
+  // top-k stage 0.208 -> 0.170 ms).  Chunks are whole 64-wide K steps.
   int tiles = ((T + BM - 1) / BM) * ((E + 1 + BN - 1) / BN);
   tiles = tiles < 1 ? 1 : tiles;  // an empty batch still sizes one split
   const int slots = 2 * num_cus();
@@ -600,7 +600,7 @@ int router_gemm_split(int T, int H, int E) {
   // one-round split unless a larger one is strictly cheaper
   auto cost = [&](int n) { return (double)((tiles * n + slots - 1) / slots) / n; };
   const int n1 = ns;
-  for (int n = n1 + 1; n <= 4 && n <= maxs; ++n)
+  for (int n = n1 + 1; n <= max_split && n <= maxs; ++n)
     if (cost(n) < cost(ns)) ns = n;
   int kchunk = (H + ns - 1) / ns;
   kchunk = (kchunk + BK - 1) / BK * BK;

@@ -291,8 +291,13 @@ __global__ void gr_write_kernel(const bf16* resid, const float* __restrict__ s, 
 
 }  // namespace
 
+// The read projection's K split may run in more rounds than the router's:
+// its K is 4H, and 8 chunks (two rounds plus) cut the 2.4T-shape read from
+// 0.97 to 0.94 ms; its partial sums are read once by the gate kernel.
+constexpr int kGrMaxSplit = 8;
+
 size_t gr_workspace_bytes(int64_t T, int64_t H, int64_t rank) {
-  const int nsplit = router_gemm_split((int)T, (int)(STREAMS * H), (int)(rank + STREAMS));
+  const int nsplit = router_gemm_split((int)T, (int)(STREAMS * H), (int)(rank + STREAMS), kGrMaxSplit);
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
   return up((size_t)T * STREAMS * H * 2) + up((size_t)nsplit * T * (rank + STREAMS) * 4) + up((size_t)T * rank * 2);
 }
@@ -304,7 +309,7 @@ hipError_t launch_gr_read(const void* resid, const void* norm_w, const void* w_r
   bf16* rhat = reinterpret_cast<bf16*>(w);
   w += up((size_t)T * STREAMS * H * 2);
   const int N = rank + STREAMS;
-  const int nsplit = router_gemm_split(T, STREAMS * H, N);
+  const int nsplit = router_gemm_split(T, STREAMS * H, N, kGrMaxSplit);
   float* partial = reinterpret_cast<float*>(w);
   w += up((size_t)nsplit * T * N * 4);
   bf16* z = reinterpret_cast<bf16*>(w);

@@ -66,7 +66,8 @@ size_t ffn_plan_ints(int64_t T, int64_t E, int64_t k, bool shared);
 // n < E router rows, n == E the shared gate (when w_sg != null).  The top-k
 // kernel adds the chunks in order c = 0..nsplit-1.  The small-batch
 // streaming router writes complete logits (nsplit = 1).
-int router_gemm_split(int T, int H, int E);
+// max_split: the largest split taken when it needs more than one round.
+int router_gemm_split(int T, int H, int E, int max_split = 4);
 // gated_residual: the same GEMM for the gated residual's read projection
 // (a separately named kernel instance, so traces tell the two apart).
 hipError_t launch_router_logits_bf16(const void* x, const void* w_router, const void* w_sg,
