@@ -334,10 +334,20 @@ __global__ __launch_bounds__(NT, BKT == 32 ? 3 : 2) void gemm_kernel(FfnArgs f, 
           const int kk = k0 + kcol * 8;
           ra_reg[0][i] = (kk < K && a_in[i]) ? ld16(a_ptr[i] + kk) : u32x4{0, 0, 0, 0};
         }
+        // expert weights are non-temporal: a 128-row m-tile covers a
+        // Flash-Next prefill group whole, so each weight line is read once
+        // (gate/up 0.770 -> 0.741 ms); the router's weights serve every
+        // m-tile and stay cached
 #pragma unroll
         for (int i = 0; i < NPASS; ++i) {
           const int kk = k0 + kcol * 8;
-          rb_reg[0][i] = kk < K ? ld16(reinterpret_cast<const bf16*>(b_ptr[i]) + kk) : u32x4{0, 0, 0, 0};
+          const bf16* bp = reinterpret_cast<const bf16*>(b_ptr[i]) + kk;
+          u32x4 v = u32x4{0, 0, 0, 0};
+          if (kk < K) {
+            if constexpr (MODE == M_ROUTER) v = ld16(bp);
+            else v = ld16_nt(bp);
+          }
+          rb_reg[0][i] = v;
         }
       };
       gload1(0);
